@@ -1,0 +1,195 @@
+"""Seeded synthetic inputs for the transformer linear layer Y = X·Wᵀ (+ b).
+
+This module only draws numbers and stores them in the element formats the
+kernels read. It holds none of the multiply's arithmetic, so both the HIP path
+and the CPU oracle can be fed from it without sharing any of the computation.
+
+Recipe (one source of truth for tests and the benchmark):
+
+* Generator: numpy ``PCG64`` seeded per tensor. The pages fix their weights with
+  a seeded generator but never say which one ("Optimizing a GPT-2-class
+  transformer on a GPU", Results), so the draws differ from theirs.
+* Seeds: ``1000 * workload + 10 * layer + tensor`` with tensor X = 1, W = 2,
+  b = 3.
+* Values are drawn in float64, rounded to float32 with round-to-nearest-even,
+  then (for half formats) rounded again to float16 / bfloat16 with
+  round-to-nearest-even. The stored values are exactly what the kernels read;
+  the oracle widens those same stored values.
+* "N(0, 0.02)" means standard deviation 0.02 (the GPT-2 initialisation).
+
+Storage arrays: float32 -> ``np.float32``, float16 -> ``np.float16``,
+bfloat16 -> ``np.uint16`` holding the raw bit patterns.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+DTYPES = ("f32", "f16", "bf16")
+TENSOR_X, TENSOR_W, TENSOR_B = 1, 2, 3
+
+
+def seed_for(workload: int, layer: int, tensor: int) -> int:
+    return 1000 * workload + 10 * layer + tensor
+
+
+def _rng(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (round to nearest, ties to even); raw bits.
+
+    NaN inputs map to a quiet NaN. This is the storage conversion of the
+    generator, applied once when inputs are made.
+    """
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    rounded = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    nan = np.isnan(a)
+    if nan.any():
+        rounded = rounded.copy()
+        rounded[nan] = ((u[nan] >> 16).astype(np.uint16) | np.uint16(0x0040))
+    return rounded
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen raw bfloat16 bits to float32 (exact)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def store(values_f64: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float64 draws into the storage format ``dtype``."""
+    f32 = np.asarray(values_f64, dtype=np.float64).astype(np.float32)
+    if dtype == "f32":
+        return f32
+    if dtype == "f16":
+        return f32.astype(np.float16)
+    if dtype == "bf16":
+        return f32_to_bf16_bits(f32)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def widen(stored: np.ndarray, dtype: str) -> np.ndarray:
+    """Stored values as float64 (exact widening; for checks and plots)."""
+    if dtype == "bf16":
+        return bf16_bits_to_f32(stored).astype(np.float64)
+    return np.asarray(stored).astype(np.float64)
+
+
+def normal(seed: int, shape, std: float, dtype: str) -> np.ndarray:
+    return store(_rng(seed).standard_normal(size=shape) * std, dtype)
+
+
+def uniform(seed: int, shape, lo: float, hi: float, dtype: str) -> np.ndarray:
+    return store(_rng(seed).uniform(lo, hi, size=shape), dtype)
+
+
+@dataclass
+class LinearCase:
+    """One linear layer's inputs in storage form.
+
+    ``W`` is out×in ``[N][K]`` for layout ``"NK"`` and ``[K][N]`` for ``"KN"``.
+    ``b`` is ``None`` when the layer has no bias.
+    """
+
+    name: str
+    M: int
+    N: int
+    K: int
+    in_dtype: str
+    out_dtype: str
+    layout: str
+    bias: bool
+    gelu: bool
+    X: np.ndarray
+    W: np.ndarray
+    b: np.ndarray | None
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+
+def _gpt2_linear(name, workload, layer, tensor_base, M, N, K, dt, out_dt, gelu):
+    X = normal(seed_for(workload, layer, tensor_base + TENSOR_X), (M, K), 1.0, dt)
+    W = normal(seed_for(workload, layer, tensor_base + TENSOR_W), (N, K), 0.02, dt)
+    b = normal(seed_for(workload, layer, tensor_base + TENSOR_B), (N,), 0.02, dt)
+    return LinearCase(name, M, N, K, dt, out_dt, "NK", True, gelu, X, W, b)
+
+
+# GPT-2-small linear shapes: (name, N, K, gelu) with d_model 768, d_ff 3072.
+GPT2_LINEARS = (
+    ("qkv", 2304, 768, False),
+    ("attn_out", 768, 768, False),
+    ("fc", 3072, 768, True),
+    ("proj", 768, 3072, False),
+)
+
+
+def workload_fp32_linear_128x768(workload: int = 1) -> LinearCase:
+    """fp32 linear, M=128, K=768, N=768, bias, no activation."""
+    M, N, K = 128, 768, 768
+    X = normal(seed_for(workload, 0, TENSOR_X), (M, K), 1.0, "f32")
+    W = normal(seed_for(workload, 0, TENSOR_W), (N, K), 0.02, "f32")
+    b = normal(seed_for(workload, 0, TENSOR_B), (N,), 0.02, "f32")
+    return LinearCase("linear_128x768x768_f32", M, N, K, "f32", "f32", "NK", True, False, X, W, b)
+
+
+def workload_fp16_narrow(workload: int = 2, copy: int = 0, M: int = 16, N: int = 4096,
+                         K: int = 4096, dtype: str = "f16") -> LinearCase:
+    """Narrow linear 16×4096×4096, X, W ~ U(-1,1)·0.05, fp16 in, fp16 out."""
+    X = uniform(seed_for(workload, 0, TENSOR_X), (M, K), -0.05, 0.05, dtype)
+    W = uniform(seed_for(workload, copy, TENSOR_W), (N, K), -0.05, 0.05, dtype)
+    return LinearCase(f"narrow_{M}x{N}x{K}_{dtype}", M, N, K, dtype, dtype, "NK", False, False,
+                      X, W, None)
+
+
+def workload_gpt2_layer(workload: int = 3, M: int = 128, dtype: str = "f32", layer: int = 0):
+    """The four GPT-2-small linears of one layer at M rows (bias on all, GELU on fc)."""
+    cases = []
+    for i, (name, N, K, gelu) in enumerate(GPT2_LINEARS):
+        cases.append(_gpt2_linear(f"{name}_{M}x{N}x{K}_{dtype}", workload, layer, 3 * i, M, N, K,
+                                  dtype, dtype, gelu))
+    return cases
+
+
+def workload_square(workload: int = 4, n: int = 4096, dtype: str = "f32") -> LinearCase:
+    """Square GEMM C = A·B, row-major A [M][K] and B [K][N], U(-1,1), no bias.
+
+    With bfloat16 inputs the output stays float32.
+    """
+    A = uniform(seed_for(workload, 0, TENSOR_X), (n, n), -1.0, 1.0, dtype)
+    B = uniform(seed_for(workload, 0, TENSOR_W), (n, n), -1.0, 1.0, dtype)
+    return LinearCase(f"square_{n}_{dtype}", n, n, n, dtype, "f32", "KN", False, False, A, B, None)
+
+
+def workload_gpt2_stack(workload: int = 5, batch: int = 64, seq: int = 128, layers: int = 12,
+                        dtype: str = "f32"):
+    """Batched GPT-2-small stack: ``layers`` × four linears at M = batch·seq.
+
+    Activations are drawn independently for every GEMM (the stack is not
+    chained: there is no attention or layernorm between the linears).
+    """
+    M = batch * seq
+    out = []
+    for layer in range(layers):
+        out.extend(workload_gpt2_layer(workload, M, dtype, layer))
+    return out
+
+
+def random_case(seed: int, M: int, N: int, K: int, in_dtype: str = "f32", out_dtype: str | None = None,
+                layout: str = "NK", bias: bool = False, gelu: bool = False,
+                x_scale: float = 1.0, w_scale: float = 0.05) -> LinearCase:
+    """A generic seeded case for parity tests of arbitrary shapes."""
+    out_dtype = out_dtype or in_dtype
+    X = normal(seed * 16 + TENSOR_X, (M, K), x_scale, in_dtype)
+    wshape = (N, K) if layout == "NK" else (K, N)
+    W = normal(seed * 16 + TENSOR_W, wshape, w_scale, in_dtype)
+    b = normal(seed * 16 + TENSOR_B, (N,), w_scale, in_dtype) if bias else None
+    return LinearCase(f"rand_{M}x{N}x{K}_{in_dtype}_{layout}", M, N, K, in_dtype, out_dtype,
+                      layout, bias, gelu, X, W, b)

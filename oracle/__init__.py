@@ -1,0 +1,164 @@
+"""CPU oracle for Y = X·Wᵀ (+ b, optional tanh-GELU).  TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product library never does, and
+this package imports nothing from it: the two share only the seeded inputs.
+
+The arithmetic lives in ``oracle.c`` (plain C, double accumulation in
+ascending k, OpenMP over output rows, every element computed independently),
+built with gcc into ``liboracle.so`` beside it.  This module is marshalling
+only: it hands numpy storage arrays to the C functions and returns float64.
+
+Pins (checked by ``tests/test_oracle.py`` without a GPU): exact rational brute
+force on tiny shapes, the hand-worked examples in ``tests/golden``, identity,
+permutation and all-ones closed forms, numpy float64 matmul, linearity,
+layout equivalence, and the GELU identities plus its distance to the erf form.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+_DT = {"f32": 0, "f16": 1, "bf16": 2}
+_LAYOUT = {"NK": 0, "KN": 1}
+_STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile ``oracle.c`` with gcc (no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+               "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        i64, vp, dp = ctypes.c_int64, ctypes.c_void_p, ctypes.POINTER(ctypes.c_double)
+        ci = ctypes.c_int
+        lib.oracle_linear_rows.argtypes = [i64, i64, i64, ci, ci, vp, vp, vp, ci, i64, i64, dp, ci]
+        lib.oracle_linear_rows.restype = ci
+        lib.oracle_linear_points.argtypes = [i64, i64, i64, ci, ci, vp, vp, vp, ci, i64,
+                                             ctypes.POINTER(i64), ctypes.POINTER(i64), dp, ci]
+        lib.oracle_linear_points.restype = ci
+        lib.oracle_gelu_tanh.argtypes = [ctypes.c_double]
+        lib.oracle_gelu_tanh.restype = ctypes.c_double
+        lib.oracle_decode.argtypes = [vp, i64, ci]
+        lib.oracle_decode.restype = ctypes.c_double
+        lib.oracle_max_threads.restype = ci
+        _lib = lib
+    return _lib
+
+
+def _prep(X, W, b, dtype, layout, M, N, K):
+    st = _STORAGE[dtype]
+    X = np.ascontiguousarray(X, dtype=st)
+    W = np.ascontiguousarray(W, dtype=st)
+    if X.shape != (M, K):
+        raise ValueError(f"X shape {X.shape} != {(M, K)}")
+    want = (N, K) if layout == "NK" else (K, N)
+    if W.shape != want:
+        raise ValueError(f"W shape {W.shape} != {want} for layout {layout}")
+    if b is not None:
+        b = np.ascontiguousarray(b, dtype=st)
+        if b.shape != (N,):
+            raise ValueError(f"bias shape {b.shape} != {(N,)}")
+    return X, W, b
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def linear_rows(X, W, b=None, *, dtype="f32", layout="NK", gelu=False, rows=None,
+                threads: int = 0) -> np.ndarray:
+    """Float64 reference for rows ``rows = (m0, m1)`` of the output (all by default)."""
+    M, K = np.shape(X)
+    N = np.shape(W)[0] if layout == "NK" else np.shape(W)[1]
+    X, W, b = _prep(X, W, b, dtype, layout, M, N, K)
+    m0, m1 = (0, M) if rows is None else rows
+    out = np.empty((m1 - m0, N), dtype=np.float64)
+    flags = (1 if b is not None else 0) | (2 if gelu else 0)
+    rc = _load().oracle_linear_rows(M, N, K, _DT[dtype], _LAYOUT[layout], _ptr(X), _ptr(W), _ptr(b),
+                                    flags, m0, m1,
+                                    out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), threads)
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return out
+
+
+def linear(X, W, b=None, *, dtype="f32", layout="NK", gelu=False, threads: int = 0) -> np.ndarray:
+    """Float64 reference of the whole output ``[M][N]``."""
+    return linear_rows(X, W, b, dtype=dtype, layout=layout, gelu=gelu, threads=threads)
+
+
+def linear_points(X, W, b=None, *, dtype="f32", layout="NK", gelu=False, mi, ni,
+                  threads: int = 0) -> np.ndarray:
+    """Float64 reference of the elements ``(mi[i], ni[i])``."""
+    M, K = np.shape(X)
+    N = np.shape(W)[0] if layout == "NK" else np.shape(W)[1]
+    X, W, b = _prep(X, W, b, dtype, layout, M, N, K)
+    mi = np.ascontiguousarray(mi, dtype=np.int64)
+    ni = np.ascontiguousarray(ni, dtype=np.int64)
+    out = np.empty(mi.shape[0], dtype=np.float64)
+    flags = (1 if b is not None else 0) | (2 if gelu else 0)
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    rc = _load().oracle_linear_points(M, N, K, _DT[dtype], _LAYOUT[layout], _ptr(X), _ptr(W),
+                                      _ptr(b), flags, mi.shape[0], mi.ctypes.data_as(i64p),
+                                      ni.ctypes.data_as(i64p),
+                                      out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), threads)
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return out
+
+
+def linear_case(case, threads: int = 0, rows=None) -> np.ndarray:
+    """Reference for an ``inputs.LinearCase``."""
+    return linear_rows(case.X, case.W, case.b, dtype=case.in_dtype, layout=case.layout,
+                       gelu=case.gelu, rows=rows, threads=threads)
+
+
+def gelu_tanh(y: float) -> float:
+    return _load().oracle_gelu_tanh(float(y))
+
+
+def decode(stored: np.ndarray, dtype: str) -> np.ndarray:
+    """The oracle's own widening of stored elements to float64."""
+    a = np.ascontiguousarray(stored, dtype=_STORAGE[dtype]).ravel()
+    lib = _load()
+    p = a.ctypes.data_as(ctypes.c_void_p)
+    return np.array([lib.oracle_decode(p, i, _DT[dtype]) for i in range(a.size)])
+
+
+def max_threads() -> int:
+    return _load().oracle_max_threads()
+
+
+def normalized_error(y, ref) -> float:
+    """max|y - ref| / max|ref|, the matmul error measure of "Writing a CUDA
+    matmul that catches cuBLAS", section "The measurement was nearly wrong".
+    """
+    y = np.asarray(y, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    denom = np.max(np.abs(ref)) if ref.size else 0.0
+    num = np.max(np.abs(y - ref)) if ref.size else 0.0
+    if denom == 0.0:
+        return 0.0 if num == 0.0 else float("inf")
+    return float(num / denom)
