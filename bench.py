@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""Benchmark of the transformer linear-layer GEMM on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+A step is one call of the library on the square fp32 GEMM C = A·B with
+M = N = K = 4096 and row-major A and B (warm operands).  Its throughput in
+TFLOP/s is ``value``.  The same run also times the narrow fp16 linear
+Y = X·Wᵀ with X 16×4096 and W 4096×4096 out×in, fp16 output, with cold
+weights: the launches rotate through 16 identical copies of W (512 MiB, more
+than the 256 MB Infinity Cache plus L2), as on "One multiply, one RTX 5090,
+eight kernels" ("Where the time goes").  That result is reported in µs and
+GB/s under ``narrow_fp16``.  Both results carry a parity verdict against
+the CPU oracle on sampled outputs, and both come with their roofline
+fraction: MFMA fp32 peak 157.3 TFLOP/s for the square GEMM, HBM 8 TB/s for
+the narrow one.
+
+The oracle (plain C, double accumulation) is timed on this host's cores on
+a bounded row sample of the square workload and reported as
+``cpu_baseline``; it is a reference point, not a target.
+
+Prints one JSON line.  ``--gpus`` above 1 exits with a message: this build
+runs on one GPU.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import subprocess
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "TFLOP/s (% MFMA peak) @4096³ fp32; µs + HBM GB/s @16×4096×4096 fp16"
+PEAK_F32_TFLOPS = 157.3      # MI355X dense fp32 matrix
+PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16/fp16 matrix
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+COLD_COPIES = 16
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def read_clocks():
+    """sclk/mclk as reported by rocm-smi (None if unavailable)."""
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        data = json.loads(out.stdout)
+        card = next(iter(data.values()))
+        return {k: v for k, v in card.items() if "sclk" in k.lower() or "mclk" in k.lower()}
+    except Exception:
+        return None
+
+
+def time_launches(fn, n: int, stream) -> float:
+    """Average ms per call of ``fn(i)`` over n back-to-back calls, HIP events on ``stream``."""
+    import torch
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(n):
+        fn(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / n
+
+
+def sampled_parity(case, y64, npts=2000, seed=0):
+    """max|err|/max|ref| over sampled outputs plus the first and last rows."""
+    import oracle
+
+    rng = np.random.default_rng(seed)
+    mi = np.concatenate([rng.integers(0, case.M, npts), np.repeat([0, case.M - 1], case.N)])
+    ni = np.concatenate([rng.integers(0, case.N, npts), np.tile(np.arange(case.N), 2)])
+    ref = oracle.linear_points(case.X, case.W, case.b, dtype=case.in_dtype, layout=case.layout, gelu=case.gelu,
+                               mi=mi, ni=ni)
+    return float(np.max(np.abs(y64[mi, ni] - ref)) / np.max(np.abs(ref)))
+
+
+def cpu_baseline(case, budget_s: float = 15.0):
+    """Time the oracle on a bounded row sample of ``case``; TFLOP/s-equivalent of the sample."""
+    import oracle
+
+    threads = oracle.max_threads()
+    t0 = time.perf_counter()
+    oracle.linear_case(case, rows=(0, 1))
+    one = max(time.perf_counter() - t0, 1e-3)
+    rows = int(max(1, min(case.M, budget_s / one)))
+    t0 = time.perf_counter()
+    oracle.linear_case(case, rows=(0, rows))
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * case.N * case.K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows} of {case.M} output rows of the {case.M}x{case.N}x{case.K} fp32 GEMM "
+                      f"({dt:.1f} s, fp64 accumulation, OpenMP over rows)",
+            "affinity_cpus": len(os.sched_getaffinity(0)),
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50, help="timed square-GEMM steps")
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--narrow-launches", type=int, default=2000, help="timed cold narrow launches")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parity", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU layout is described "
+              "in DESIGN.md and not built.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from dense_gemm_transformer_amd import inputs, tlgemm
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    clocks_before = read_clocks()
+
+    def to_dev(a, dt):
+        if dt == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def to_f64(t):
+        t = t.cpu()
+        if t.dtype == torch.bfloat16:
+            return inputs.widen(t.view(torch.int16).numpy().view(np.uint16), "bf16")
+        return t.numpy().astype(np.float64)
+
+    # ---- square fp32 GEMM 4096³ (the step) ----------------------------------------------
+    log("square fp32 4096^3: generating inputs")
+    sq = inputs.workload_square(dtype="f32")
+    A, B = to_dev(sq.X, "f32"), to_dev(sq.W, "f32")
+    C = torch.empty((sq.M, sq.N), dtype=torch.float32, device=dev)
+    plan = tlgemm.Plan.create(sq.M, sq.N, sq.K, "f32", "f32", "KN")
+    run_sq = lambda i: plan.run_ptrs(A.data_ptr(), B.data_ptr(), 0, C.data_ptr(), 0, 0, stream.cuda_stream)
+    run_sq(0)
+    torch.cuda.synchronize()
+    sq_err = None if args.no_parity else sampled_parity(sq, to_f64(C))
+    log(f"square fp32: {plan.describe()} parity {sq_err}")
+    for i in range(args.warmup):
+        run_sq(i)
+    ms = time_launches(run_sq, args.steps, stream)
+    sq_tflops = sq.flops / (ms * 1e-3) / 1e12
+    log(f"square fp32: {ms * 1e3:.1f} us/step, {sq_tflops:.1f} TFLOP/s")
+
+    # bf16 inputs, fp32 output (same shape), reported beside
+    sqb = inputs.workload_square(dtype="bf16")
+    Ab, Bb = to_dev(sqb.X, "bf16"), to_dev(sqb.W, "bf16")
+    planb = tlgemm.Plan.create(sqb.M, sqb.N, sqb.K, "bf16", "f32", "KN")
+    run_sqb = lambda i: planb.run_ptrs(Ab.data_ptr(), Bb.data_ptr(), 0, C.data_ptr(), 0, 0, stream.cuda_stream)
+    run_sqb(0)
+    torch.cuda.synchronize()
+    sqb_err = None if args.no_parity else sampled_parity(sqb, to_f64(C))
+    for i in range(args.warmup):
+        run_sqb(i)
+    msb = time_launches(run_sqb, args.steps, stream)
+    log(f"square bf16: {msb * 1e3:.1f} us, {sqb.flops / (msb * 1e-3) / 1e12:.1f} TFLOP/s, parity {sqb_err}")
+    del Ab, Bb
+
+    # ---- narrow fp16 linear 16×4096×4096, cold weights -----------------------------------
+    log("narrow fp16 16x4096x4096: generating inputs")
+    nc = inputs.workload_fp16_narrow()
+    X = to_dev(nc.X, "f16")
+    W0 = to_dev(nc.W, "f16")
+    Ws = [W0] + [W0.clone() for _ in range(COLD_COPIES - 1)]
+    Y = torch.empty((nc.M, nc.N), dtype=torch.float16, device=dev)
+    nplan = tlgemm.Plan.create(nc.M, nc.N, nc.K, "f16", "f16", "NK")
+    run_n = lambda i: nplan.run_ptrs(X.data_ptr(), Ws[i % COLD_COPIES].data_ptr(), 0, Y.data_ptr(), 0, 0,
+                                     stream.cuda_stream)
+    run_n(0)
+    torch.cuda.synchronize()
+    n_err = None if args.no_parity else sampled_parity(nc, to_f64(Y))
+    for i in range(COLD_COPIES * 4):
+        run_n(i)
+    n_ms = time_launches(run_n, args.narrow_launches, stream)
+    warm_ms = time_launches(lambda i: run_n(0), args.narrow_launches, stream)
+    n_bytes = nc.M * nc.K * 2 + nc.N * nc.K * 2 + nc.M * nc.N * 2
+    n_gbs = n_bytes / (n_ms * 1e-3) / 1e9
+    log(f"narrow fp16: {nplan.describe()} cold {n_ms * 1e3:.2f} us ({n_gbs:.0f} GB/s), warm {warm_ms * 1e3:.2f} us, "
+        f"parity {n_err}")
+    clocks_after = read_clocks()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline: timing the oracle on a row sample")
+        cpu = cpu_baseline(sq)
+
+    tol32, tol16 = 1e-5, 1e-2
+    out = {
+        "metric": METRIC,
+        "value": round(sq_tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "fp32 GEMM C=A.B, M=N=K=4096, row-major A[M][K] and B[K][N], U(-1,1), warm",
+                   "M": sq.M, "N": sq.N, "K": sq.K, "layout": "KN", "plan": plan.describe()},
+        "roofline": {"bound": "mfma", "achieved": round(sq_tflops, 3), "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(sq_tflops / PEAK_F32_TFLOPS, 4), "traffic": None,
+                     "kernel": "tiled_kernel (fp32, 128x128x16)",
+                     "algorithmic_flops_per_launch": sq.flops},
+        "cpu_baseline": cpu,
+        "parity": {"square_f32_err": sq_err, "square_f32_pass": None if sq_err is None else sq_err <= tol32,
+                   "square_bf16_err": sqb_err, "narrow_f16_err": n_err,
+                   "narrow_f16_pass": None if n_err is None else n_err <= tol16,
+                   "measure": "max|err|/max|ref| on sampled outputs vs the CPU oracle"},
+        "square_bf16": {"us": round(msb * 1e3, 2), "TFLOP/s": round(sqb.flops / (msb * 1e-3) / 1e12, 2),
+                        "frac_mfma_peak": round(sqb.flops / (msb * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                        "plan": planb.describe()},
+        "narrow_fp16": {"workload": "fp16 linear Y=X.W^T, M=16, K=4096, N=4096, W out x in, fp16 out, cold W "
+                                    f"({COLD_COPIES} rotated copies)",
+                        "us": round(n_ms * 1e3, 3), "warm_us": round(warm_ms * 1e3, 3),
+                        "GB/s": round(n_gbs, 1),
+                        "roofline": {"bound": "hbm", "achieved": round(n_gbs, 1), "peak": PEAK_HBM_GBS,
+                                     "unit": "GB/s", "frac": round(n_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                                     "kernel": "stream_kernel (fp16, 8 waves x 16 loads)",
+                                     "algorithmic_bytes_per_launch": n_bytes},
+                        "timing": "HIP events over back-to-back launches (includes launch gaps)",
+                        "plan": nplan.describe()},
+        "clocks": {"before": clocks_before, "after": clocks_after},
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,135 @@
+// Device helpers shared by the gfx950 kernels: element formats, 16-byte
+// vectors, MFMA operand types and the fused epilogue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "../tlgemm_internal.h"
+
+namespace tlg {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---- element formats ------------------------------------------------------------
+// Storage: fp32 as float, fp16 and bf16 as their 16-bit patterns.
+template <int DT> struct Elem;
+template <> struct Elem<TLG_F32> {
+    using storage = float;
+    static constexpr int per16 = 4;  // elements per 16-byte vector
+    __device__ static float to_f32(float v) { return v; }
+};
+template <> struct Elem<TLG_F16> {
+    using storage = uint16_t;
+    static constexpr int per16 = 8;
+    __device__ static float to_f32(uint16_t v) { return (float)__builtin_bit_cast(_Float16, v); }
+};
+template <> struct Elem<TLG_BF16> {
+    using storage = uint16_t;
+    static constexpr int per16 = 8;
+    __device__ static float to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+};
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ inline uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+template <int DT> __device__ inline void store_out(void* Y, int64_t idx, float v) {
+    if constexpr (DT == TLG_F32) {
+        static_cast<float*>(Y)[idx] = v;
+    } else if constexpr (DT == TLG_F16) {
+        static_cast<_Float16*>(Y)[idx] = (_Float16)v;  // v_cvt_f16_f32: round to nearest even
+    } else {
+        static_cast<uint16_t*>(Y)[idx] = f32_to_bf16_rne(v);
+    }
+}
+
+template <int DT> __device__ inline float load_elem(const void* p, int64_t idx) {
+    return Elem<DT>::to_f32(static_cast<const typename Elem<DT>::storage*>(p)[idx]);
+}
+
+// ---- fused epilogue ----------------------------------------------------------------
+// Bias first, then the tanh form of GELU, evaluated in fp32.
+__device__ inline float gelu_tanh(float y) {
+    const float c = 0.7978845608028654f;  // sqrt(2/pi)
+    const float u = c * (y + 0.044715f * y * y * y);
+    return 0.5f * y * (1.0f + tanhf(u));
+}
+
+template <uint32_t EPI> __device__ inline float epilogue(float acc, float b) {
+    float y = acc;
+    if constexpr ((EPI & TLG_EPI_BIAS) != 0) y += b;
+    if constexpr ((EPI & TLG_EPI_GELU_TANH) != 0) y = gelu_tanh(y);
+    return y;
+}
+
+// ---- 16-byte global loads --------------------------------------------------------
+__device__ inline u32x4 ldg16(const void* p) { return *static_cast<const u32x4*>(p); }
+
+// ---- MFMA wrappers -----------------------------------------------------------------
+// 16x16 output block, fp32 accumulate.
+__device__ inline f32x4 mfma16_f32(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+template <int DT> __device__ inline f32x4 mfma16_16bit(u32x4 a, u32x4 b, f32x4 c) {
+    if constexpr (DT == TLG_F16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+// 32x32 output block.
+__device__ inline f32x16 mfma32_f32(float a, float b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+template <int DT> __device__ inline f32x16 mfma32_16bit(u32x4 a, u32x4 b, f32x16 c) {
+    if constexpr (DT == TLG_F16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// ---- host-side dispatch helpers ----------------------------------------------------
+template <int V> using ic = std::integral_constant<int, V>;
+
+template <class F> inline int with_epi(uint32_t epi, F&& f) {
+    switch (epi) {
+    case 0: return f(ic<0>{});
+    case TLG_EPI_BIAS: return f(ic<TLG_EPI_BIAS>{});
+    case TLG_EPI_GELU_TANH: return f(ic<TLG_EPI_GELU_TANH>{});
+    default: return f(ic<TLG_EPI_BIAS | TLG_EPI_GELU_TANH>{});
+    }
+}
+
+// The five supported (in, out) pairs.
+template <class F> inline int with_types(int in_dt, int out_dt, F&& f) {
+    if (in_dt == TLG_F32) return f(ic<TLG_F32>{}, ic<TLG_F32>{});
+    if (in_dt == TLG_F16) {
+        if (out_dt == TLG_F16) return f(ic<TLG_F16>{}, ic<TLG_F16>{});
+        return f(ic<TLG_F16>{}, ic<TLG_F32>{});
+    }
+    if (out_dt == TLG_BF16) return f(ic<TLG_BF16>{}, ic<TLG_BF16>{});
+    return f(ic<TLG_BF16>{}, ic<TLG_F32>{});
+}
+
+template <class F> inline int with_layout(int layout, F&& f) {
+    if (layout == TLG_NK) return f(ic<TLG_NK>{});
+    return f(ic<TLG_KN>{});
+}
+
+int check_launch(const char* what);
+
+}  // namespace tlg

@@ -1,0 +1,8 @@
+// Stream kernel instantiations for f16 inputs (one translation unit per
+// input type so the kernel variants compile in parallel).
+#include "stream.h"
+
+namespace tlg {
+template int launch_stream_in<TLG_F16>(const tlg_plan&, const void*, const void*, const void*, void*,
+                                        hipStream_t);
+}  // namespace tlg

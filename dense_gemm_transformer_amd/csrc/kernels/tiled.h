@@ -1,0 +1,310 @@
+// LDS-tiled MFMA kernel for the compute-bound shapes (square GEMM, the
+// batched GPT-2 stack) and, with split-K, the 128-row GPT-2 layers.
+//
+// The ladder of "Writing a CUDA matmul that catches cuBLAS" (block tiling,
+// register/warp tiling, double buffering in "Kernel 8: the loop was shaped
+// wrong", matrix-core fragments in "Kernel 9"/"Kernel 10") rebuilt for gfx950:
+//
+//  * A workgroup computes a BM×BN tile with WM×WN waves; each wave owns a
+//    (BM/WM)×(BN/WN) block of 32×32 MFMA accumulators (fp32:
+//    v_mfma_f32_32x32x2_f32; fp16/bf16: v_mfma_f32_32x32x16_*).
+//  * K advances in slices of BK (64 bytes of each operand row).  The next
+//    slice is loaded with 16-byte global loads into registers while the
+//    current slice is multiplied from LDS; two LDS buffers, one barrier per
+//    slice.
+//  * LDS rows are k-contiguous with a 16-byte pad (stride 80 B), so the
+//    16-byte operand reads of 16 consecutive rows hit 64 distinct banks.
+//    A row-major [K][N] fp32 operand stays n-contiguous (stride BN+8 floats,
+//    so the two half-waves read disjoint bank halves); a [K][N] 16-bit
+//    operand is transposed while it is written to LDS.
+//  * For fp32 one 16-byte read feeds four MFMAs; the k order inside a slice
+//    is permuted identically for both operands, which leaves each dot
+//    product unchanged.
+//  * Workgroup ids are remapped so that tiles sharing operand panels run on
+//    one XCD (ids are dealt to the 8 XCDs round-robin, each with its own L2),
+//    then grouped 8 tile-rows at a time.
+//  * Split-K ("Optimizing a GPT-2-class transformer on a GPU", Act I): grid
+//    dimension y splits K; each split writes fp32 partials to the workspace
+//    and a second kernel sums them in split order (fixed order, so results
+//    are reproducible) and applies the epilogue.
+
+#pragma once
+#include "common.h"
+
+namespace tlg {
+
+template <int IN, int OUT, int LAYOUT, uint32_t EPI, int BM, int BN, int BK, int WM, int WN, bool EVEN,
+          bool SPLIT>
+__global__ __launch_bounds__(64 * WM * WN) void tiled_kernel(const void* __restrict__ Xv,
+                                                            const void* __restrict__ Wv,
+                                                            const void* __restrict__ bias,
+                                                            void* __restrict__ Y, float* __restrict__ ws,
+                                                            int M, int N, int K, int kper) {
+    using S = typename Elem<IN>::storage;
+    constexpr bool F32 = IN == TLG_F32;
+    constexpr int THREADS = 64 * WM * WN;
+    constexpr int EPV = Elem<IN>::per16;  // elements per 16 bytes
+    constexpr int VPR = BK / EPV;         // 16-byte vectors per tile row
+    static_assert(BK * (int)sizeof(S) == 64, "one slice is 64 bytes of each operand row");
+    constexpr int LDA = BK + EPV;         // padded LDS row (elements)
+    constexpr bool B_NMAJOR = (LAYOUT == TLG_KN) && F32;  // fp32 [K][N] stays n-contiguous
+    constexpr int LDBN = BN + 8;                         // its padded row (floats)
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int TM = WTM / 32, TN = WTN / 32;
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile is a multiple of 32×32");
+    constexpr int AV = BM * VPR / THREADS;
+    constexpr int BV = (LAYOUT == TLG_NK) ? BN * VPR / THREADS : BK * (BN / EPV) / THREADS;
+    static_assert(AV * THREADS == BM * VPR && BV >= 1, "tile loads divide evenly over the threads");
+    constexpr int A_ELEMS = BM * LDA;
+    constexpr int B_ELEMS = B_NMAJOR ? BK * LDBN : BN * LDA;
+
+    __shared__ __attribute__((aligned(16))) S lds[2][A_ELEMS + B_ELEMS];
+
+    const S* __restrict__ X = static_cast<const S*>(Xv);
+    const S* __restrict__ W = static_cast<const S*>(Wv);
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int r = lane & 31, g = lane >> 5;
+    const int wm0 = (wave / WN) * WTM, wn0 = (wave % WN) * WTN;
+
+    // ---- tile coordinates: XCD-aware remap, then groups of 8 tile-rows ----
+    const int gx = (N + BN - 1) / BN, gy = (M + BM - 1) / BM;
+    const int total = gx * gy;
+    int lin = blockIdx.x;
+    if ((total & 7) == 0) lin = (lin & 7) * (total >> 3) + (lin >> 3);
+    constexpr int GROUP = 8;
+    const int group_tiles = GROUP * gx;
+    const int first = (lin / group_tiles) * GROUP;
+    const int rows_in_group = min(gy - first, GROUP);
+    const int within = lin % group_tiles;
+    const int m0 = (first + within % rows_in_group) * BM;
+    const int n0 = (within / rows_in_group) * BN;
+
+    const int z = blockIdx.y;
+    const int kbeg = z * kper;
+    const int kend = min(kbeg + kper, K);
+    const int nslices = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+
+    u32x4 ra[AV], rbv[BV];
+    auto gload = [&](int s) {
+        const int k0 = kbeg + s * BK;
+#pragma unroll
+        for (int i = 0; i < AV; ++i) {
+            const int v = t + THREADS * i;
+            const int row = v / VPR, k = k0 + (v % VPR) * EPV;
+            const int m = EVEN ? m0 + row : min(m0 + row, M - 1);
+            if (EVEN || k < kend)
+                ra[i] = ldg16(X + (int64_t)m * K + k);
+            else
+                ra[i] = u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int i = 0; i < BV; ++i) {
+            const int v = t + THREADS * i;
+            if constexpr (LAYOUT == TLG_NK) {
+                const int row = v / VPR, k = k0 + (v % VPR) * EPV;
+                const int n = EVEN ? n0 + row : min(n0 + row, N - 1);
+                if (EVEN || k < kend)
+                    rbv[i] = ldg16(W + (int64_t)n * K + k);
+                else
+                    rbv[i] = u32x4{0u, 0u, 0u, 0u};
+            } else {
+                constexpr int NV = BN / EPV;
+                const int kr = v / NV, nv = v % NV;
+                const int k = k0 + kr;
+                const int n = EVEN ? n0 + nv * EPV : min(n0 + nv * EPV, N - EPV);
+                if (EVEN || k < kend)
+                    rbv[i] = ldg16(W + (int64_t)k * N + n);
+                else
+                    rbv[i] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    };
+    auto lstore = [&](int buf) {
+        S* As = lds[buf];
+        S* Bs = lds[buf] + A_ELEMS;
+#pragma unroll
+        for (int i = 0; i < AV; ++i) {
+            const int v = t + THREADS * i;
+            *reinterpret_cast<u32x4*>(As + (v / VPR) * LDA + (v % VPR) * EPV) = ra[i];
+        }
+#pragma unroll
+        for (int i = 0; i < BV; ++i) {
+            const int v = t + THREADS * i;
+            if constexpr (LAYOUT == TLG_NK) {
+                *reinterpret_cast<u32x4*>(Bs + (v / VPR) * LDA + (v % VPR) * EPV) = rbv[i];
+            } else if constexpr (B_NMAJOR) {
+                constexpr int NV = BN / EPV;
+                *reinterpret_cast<u32x4*>(Bs + (v / NV) * LDBN + (v % NV) * EPV) = rbv[i];
+            } else {
+                constexpr int NV = BN / EPV;
+                const int kr = v / NV, nb = (v % NV) * EPV;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    Bs[(nb + e) * LDA + kr] = (S)((rbv[i][e >> 1] >> (16 * (e & 1))) & 0xffffu);
+            }
+        }
+    };
+
+    using Acc = f32x16;
+    Acc acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    auto compute = [&](int buf) {
+        const S* As = lds[buf];
+        const S* Bs = lds[buf] + A_ELEMS;
+        if constexpr (F32) {
+#pragma unroll
+            for (int kq = 0; kq < BK / 8; ++kq) {
+                f32x4 a[TM], b[TN];
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+                    a[i] = *reinterpret_cast<const f32x4*>(As + (wm0 + i * 32 + r) * LDA + kq * 8 + 4 * g);
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    if constexpr (B_NMAJOR) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            b[j][e] = Bs[(kq * 8 + 4 * g + e) * LDBN + wn0 + j * 32 + r];
+                    } else {
+                        b[j] = *reinterpret_cast<const f32x4*>(Bs + (wn0 + j * 32 + r) * LDA + kq * 8 + 4 * g);
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int i = 0; i < TM; ++i)
+#pragma unroll
+                        for (int j = 0; j < TN; ++j) acc[i][j] = mfma32_f32(a[i][e], b[j][e], acc[i][j]);
+            }
+        } else {
+#pragma unroll
+            for (int kq = 0; kq < BK / 16; ++kq) {
+                u32x4 a[TM], b[TN];
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+                    a[i] = *reinterpret_cast<const u32x4*>(As + (wm0 + i * 32 + r) * LDA + kq * 16 + 8 * g);
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    b[j] = *reinterpret_cast<const u32x4*>(Bs + (wn0 + j * 32 + r) * LDA + kq * 16 + 8 * g);
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j) acc[i][j] = mfma32_16bit<IN>(a[i], b[j], acc[i][j]);
+            }
+        }
+    };
+
+    if (nslices > 0) {
+        gload(0);
+        lstore(0);
+        __syncthreads();
+        for (int s = 0; s < nslices; ++s) {
+            const int cur = s & 1;
+            if (s + 1 < nslices) gload(s + 1);
+            compute(cur);
+            if (s + 1 < nslices) lstore(cur ^ 1);
+            __syncthreads();
+        }
+    }
+
+    // ---- epilogue: a 32×32 accumulator holds column (lane % 32) and rows
+    // 8*(e/4) + 4*(lane/32) + e%4 for register e.
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int n = n0 + wn0 + j * 32 + r;
+            float b = 0.0f;
+            if constexpr (!SPLIT && (EPI & TLG_EPI_BIAS) != 0)
+                if (EVEN || n < N) b = load_elem<IN>(bias, n);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int m = m0 + wm0 + i * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
+                if (!EVEN && (m >= M || n >= N)) continue;
+                if constexpr (SPLIT)
+                    ws[((int64_t)z * M + m) * N + n] = acc[i][j][e];
+                else
+                    store_out<OUT>(Y, (int64_t)m * N + n, epilogue<EPI>(acc[i][j][e], b));
+            }
+        }
+    }
+}
+
+// Sum the split partials in split order, then the epilogue.  Four outputs per thread.
+template <int IN, int OUT, uint32_t EPI>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws, int splits,
+                                                           const void* __restrict__ bias,
+                                                           void* __restrict__ Y, int64_t MN, int N) {
+    const int64_t base = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int64_t idx = base + e;
+        if (idx >= MN) return;
+        float s = 0.0f;
+        for (int z = 0; z < splits; ++z) s += ws[(int64_t)z * MN + idx];
+        float b = 0.0f;
+        if constexpr ((EPI & TLG_EPI_BIAS) != 0) b = load_elem<IN>(bias, idx % N);
+        store_out<OUT>(Y, idx, epilogue<EPI>(s, b));
+    }
+}
+
+template <int I, int O, int L, uint32_t E, int BM, int BN, int BK, int WM, int WN>
+static int launch_tiled_cfg(const tlg_plan& p, const void* X, const void* W, const void* bias, void* Y,
+                            float* ws, hipStream_t stream) {
+    const int S = p.split;
+    const int kper = (int)(ceil_div(ceil_div(p.K, S), BK) * BK);
+    const bool even = p.M % BM == 0 && p.N % BN == 0 && (int64_t)kper * S == p.K;
+    const dim3 grid((unsigned)(p.grid_x * p.grid_y), (unsigned)S), block(64 * WM * WN);
+    auto go = [&](auto ev, auto sp) {
+        hipLaunchKernelGGL((tiled_kernel<I, O, L, E, BM, BN, BK, WM, WN, decltype(ev)::value, decltype(sp)::value>),
+                           grid, block, 0, stream, X, W, bias, Y, ws, (int)p.M, (int)p.N, (int)p.K, kper);
+        return check_launch("tiled_kernel");
+    };
+    int rc;
+    if (S > 1)
+        rc = even ? go(std::true_type{}, std::true_type{}) : go(std::false_type{}, std::true_type{});
+    else
+        rc = even ? go(std::true_type{}, std::false_type{}) : go(std::false_type{}, std::false_type{});
+    if (rc != TLG_OK || S == 1) return rc;
+    const int64_t MN = p.M * p.N;
+    hipLaunchKernelGGL((splitk_reduce_kernel<I, O, E>), dim3((unsigned)ceil_div(MN, 1024)), dim3(256), 0, stream,
+                       (const float*)ws, S, bias, Y, MN, (int)p.N);
+    return check_launch("splitk_reduce_kernel");
+}
+
+
+// All launches for one input dtype; explicitly instantiated once per dtype
+// in its own translation unit (tiled_f32.hip, tiled_f16.hip, tiled_bf16.hip).
+template <int I>
+int launch_tiled_in(const tlg_plan& p, const void* X, const void* W, const void* bias, void* Y, void* ws,
+                    hipStream_t stream) {
+    float* wsf = static_cast<float*>(ws);
+    auto with_out = [&](auto f) {
+        if constexpr (I == TLG_F32) return f(ic<TLG_F32>{});
+        else if (p.out_dt == TLG_F32) return f(ic<TLG_F32>{});
+        else return f(ic<I>{});
+    };
+    return with_out([&](auto out) {
+        return with_layout(p.layout, [&](auto lay) {
+            return with_epi(p.epi, [&](auto epi) {
+                constexpr int O = decltype(out)::value, L = decltype(lay)::value;
+                constexpr uint32_t E = (uint32_t)decltype(epi)::value;
+                constexpr const TileCfg* T = I == TLG_F32 ? kTiledF32 : kTiled16;
+                static_assert(kNumTiledF32 == 3 && kNumTiled16 == 3, "tile lists changed");
+                constexpr TileCfg c0 = T[0], c1 = T[1], c2 = T[2];
+                switch (p.tile) {
+                case 0: return launch_tiled_cfg<I, O, L, E, c0.bm, c0.bn, c0.bk, c0.wm, c0.wn>(p, X, W, bias, Y, wsf, stream);
+                case 1: return launch_tiled_cfg<I, O, L, E, c1.bm, c1.bn, c1.bk, c1.wm, c1.wn>(p, X, W, bias, Y, wsf, stream);
+                default: return launch_tiled_cfg<I, O, L, E, c2.bm, c2.bn, c2.bk, c2.wm, c2.wn>(p, X, W, bias, Y, wsf, stream);
+                }
+            });
+        });
+    });
+}
+
+}  // namespace tlg

@@ -1,0 +1,8 @@
+// Tiled MFMA kernel instantiations for bf16 inputs (one translation unit per
+// input type so the kernel variants compile in parallel).
+#include "tiled.h"
+
+namespace tlg {
+template int launch_tiled_in<TLG_BF16>(const tlg_plan&, const void*, const void*, const void*, void*, void*,
+                                       hipStream_t);
+}  // namespace tlg

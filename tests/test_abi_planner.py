@@ -1,0 +1,141 @@
+"""C-ABI and planner checks that need no GPU (the planner is host-only)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from dense_gemm_transformer_amd import tlgemm as t
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "tlgemm.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemm_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert set(names) == set(t.EXPORTS)
+    lib = ctypes.CDLL(t.LIB_PATH)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def _plan(*a, **k):
+    return t.Plan.create(*a, **k)
+
+
+def test_narrow_fp16_goes_to_stream():
+    p = _plan(16, 4096, 4096, "f16", "f16")
+    i = p.info
+    assert i.variant == t.VARIANT_STREAM and i.workgroups == 256 and i.threads == 512
+    assert i.split_k == 8 and i.workspace_bytes == 0 and i.launches == 1
+
+
+def test_square_fp32_goes_to_tiled():
+    p = _plan(4096, 4096, 4096, "f32", "f32", "KN")
+    i = p.info
+    assert i.variant == t.VARIANT_TILED and (i.tile_m, i.tile_n) == (128, 128)
+    assert i.workgroups == 1024 and i.split_k == 1 and i.workspace_bytes == 0
+
+
+@pytest.mark.parametrize("N,K", [(2304, 768), (768, 768), (3072, 768), (768, 3072)])
+def test_gpt2_layer_shapes_fill_the_chip(N, K):
+    i = _plan(128, N, K, "f32", bias=True).info
+    assert i.variant == t.VARIANT_TILED
+    tiles = -(-128 // i.tile_m) * -(-N // i.tile_n)
+    assert tiles * i.split_k >= 256 or K // (i.tile_k * i.split_k) < 8
+    assert i.workspace_bytes == (i.split_k * 128 * N * 4 if i.split_k > 1 else 0)
+
+
+def test_misaligned_rows_go_to_generic():
+    assert _plan(8, 10, 7, "f32").info.variant == t.VARIANT_GENERIC          # K*4 not a multiple of 16
+    assert _plan(8, 10, 12, "f16").info.variant == t.VARIANT_GENERIC         # K*2 = 24
+    assert _plan(200, 10, 16, "f32", layout="KN").info.variant == t.VARIANT_GENERIC  # N*4 = 40
+
+
+def test_forced_variants_and_errors():
+    p = _plan(100, 64, 64, "bf16", variant=t.VARIANT_GENERIC)
+    assert p.info.variant == t.VARIANT_GENERIC
+    with pytest.raises(t.TlgError) as e:
+        _plan(100, 64, 64, "bf16", variant=t.VARIANT_STREAM)
+    assert e.value.status == t.ERR_UNSUPPORTED
+    with pytest.raises(t.TlgError) as e:
+        _plan(10, 64, 64, "f32", layout="KN", variant=t.VARIANT_STREAM)
+    assert e.value.status == t.ERR_UNSUPPORTED
+    p = _plan(100, 64, 64, "f32", variant=t.VARIANT_TILED, split_k=3, tile=2)
+    i = p.info
+    assert (i.split_k, i.tile_m, i.launches, i.workspace_bytes) == (3, 64, 2, 3 * 100 * 64 * 4)
+    with pytest.raises(t.TlgError) as e:
+        _plan(100, 64, 64, "f32", variant=t.VARIANT_TILED, split_k=5)  # 4 slices of 16
+    assert e.value.status == t.ERR_UNSUPPORTED
+    with pytest.raises(t.TlgError) as e:
+        _plan(100, 64, 64, "f32", split_k=2)  # override without a variant
+    assert e.value.status == t.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 1, 1, "f32"), t.ERR_INVALID_ARG),
+    ((1, -3, 1, "f32"), t.ERR_INVALID_ARG),
+    ((1, 1, 0, "f32"), t.ERR_INVALID_ARG),
+    ((1, 1, 1, 7), t.ERR_INVALID_ARG),
+])
+def test_bad_shapes_and_dtypes(args, status):
+    with pytest.raises(t.TlgError) as e:
+        t.gemm_plan(*args)
+    assert e.value.status == status
+
+
+def test_unsupported_pairs_and_flags():
+    with pytest.raises(t.TlgError) as e:
+        t.gemm_plan(4, 4, 4, "f32", "f16")
+    assert e.value.status == t.ERR_UNSUPPORTED
+    with pytest.raises(t.TlgError) as e:
+        t.gemm_plan(4, 4, 4, "f16", "bf16")
+    assert e.value.status == t.ERR_UNSUPPORTED
+    with pytest.raises(t.TlgError) as e:
+        t.gemm_plan(4, 4, 4, "f32", "f32", "NK", 4)
+    assert e.value.status == t.ERR_INVALID_ARG
+    with pytest.raises(t.TlgError) as e:
+        t.gemm_plan(4, 4, 4, "f32", "f32", 2, 0)
+    assert e.value.status == t.ERR_INVALID_ARG
+
+
+def test_null_handling_and_describe():
+    lib = t.lib()
+    assert lib.gemm_plan(None, 1, 1, 1, 0, 0, 0, 0) == t.ERR_INVALID_ARG
+    h = ctypes.c_void_p(1234)
+    assert lib.gemm_plan(ctypes.byref(h), 0, 1, 1, 0, 0, 0, 0) == t.ERR_INVALID_ARG
+    assert h.value is None  # *out is cleared on error
+    assert lib.gemm_destroy(None) == t.OK
+    assert lib.gemm_workspace_size(None) == 0
+    assert lib.gemm_plan_info(None, None) == t.ERR_INVALID_ARG
+    p = _plan(16, 4096, 4096, "f16")
+    full = p.describe()
+    assert "variant=stream" in full and "M=16" in full
+    buf = ctypes.create_string_buffer(10)
+    n = lib.gemm_plan_describe(p.handle, buf, 10)
+    assert n == len(full) and buf.value.decode() == full[:9]
+    assert t.gemm_status_string(t.ERR_MISALIGNED) == "misaligned pointer"
+    assert t.gemm_status_string(42) == "unknown status"
+
+
+def test_run_argument_errors_without_launch():
+    """gemm_run rejects bad arguments before touching the device."""
+    p = _plan(16, 64, 64, "f32", bias=True)
+    lib = t.lib()
+    good = 1 << 20
+    assert lib.gemm_run(None, good, good, good, good, None, 0, None) == t.ERR_INVALID_ARG
+    assert lib.gemm_run(p.handle, None, good, good, good * 4, None, 0, None) == t.ERR_INVALID_ARG
+    assert lib.gemm_run(p.handle, good, 2 * good, None, 3 * good, None, 0, None) == t.ERR_INVALID_ARG  # bias missing
+    assert lib.gemm_run(p.handle, good + 4, 2 * good, 4 * good, 3 * good, None, 0, None) == t.ERR_MISALIGNED
+    assert lib.gemm_run(p.handle, good, 2 * good, 4 * good, good + 64, None, 0, None) == t.ERR_INVALID_ARG  # Y aliases X
+    q = _plan(128, 768, 768, "f32", variant=t.VARIANT_TILED, split_k=4, tile=2)
+    big = 1 << 24
+    assert lib.gemm_run(q.handle, big, 2 * big, None, 3 * big, None, 0, None) == t.ERR_WORKSPACE
+    assert lib.gemm_run(q.handle, big, 2 * big, None, 3 * big, 8 * big, 16, None) == t.ERR_WORKSPACE
+    assert "workspace" in t.gemm_last_error()

@@ -1,0 +1,192 @@
+"""Parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: max|Y - ref| / max|ref| <= 1e-5 for fp32 inputs and <= 1e-2 for
+fp16/bf16 inputs (fp32 accumulation), the matmul error measure of "Writing a
+CUDA matmul that catches cuBLAS" ("The measurement was nearly wrong").
+Exact cases (identity and permutation weights, replicated rows, repeat
+runs) must match bitwise.
+"""
+
+import numpy as np
+import pytest
+
+from dense_gemm_transformer_amd import inputs, tlgemm
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from gpu_helpers import TOL, device_case, normalized_error, run_case, to_device, to_f64  # noqa: E402
+
+PAIRS = [("f32", "f32"), ("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"), ("bf16", "f32")]
+EPIS = [(False, False), (True, False), (False, True), (True, True)]
+
+
+def _check(case, **force):
+    Y, desc = run_case(case, **force)
+    ref = oracle.linear_case(case)
+    err = normalized_error(to_f64(Y), ref)
+    assert err <= TOL[case.in_dtype], f"{desc}: err {err:.3e}"
+    return Y, desc
+
+
+def _case(seed, M, N, K, pair, layout="NK", epi=(False, False)):
+    return inputs.random_case(seed, M, N, K, pair[0], pair[1], layout, bias=epi[0], gelu=epi[1])
+
+
+# --- every variant, dtype pair, layout and epilogue at ragged sizes ---------------------
+
+@pytest.mark.parametrize("pair", PAIRS, ids=lambda p: f"{p[0]}->{p[1]}")
+@pytest.mark.parametrize("layout", ["NK", "KN"])
+@pytest.mark.parametrize("epi", EPIS, ids=["none", "bias", "gelu", "bias+gelu"])
+def test_generic(pair, layout, epi):
+    for shape in [(1, 1, 1), (37, 70, 29), (130, 65, 100)]:
+        c = _case(1, *shape, pair, layout, epi)
+        _, desc = _check(c, variant=tlgemm.VARIANT_GENERIC)
+        assert "variant=generic" in desc
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=lambda p: f"{p[0]}->{p[1]}")
+@pytest.mark.parametrize("epi", EPIS, ids=["none", "bias", "gelu", "bias+gelu"])
+@pytest.mark.parametrize("tile", [1, 2, 3])
+def test_stream(pair, epi, tile):
+    for M, N, K in [(1, 16, 8), (16, 48, 512), (5, 50, 520), (17, 33, 1032), (40, 100, 264), (64, 16, 4096)]:
+        c = _case(2, M, N, K, pair, "NK", epi)
+        _, desc = _check(c, variant=tlgemm.VARIANT_STREAM, tile=tile)
+        assert "variant=stream" in desc
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=lambda p: f"{p[0]}->{p[1]}")
+@pytest.mark.parametrize("layout", ["NK", "KN"])
+@pytest.mark.parametrize("epi", EPIS, ids=["none", "bias", "gelu", "bias+gelu"])
+def test_tiled(pair, layout, epi):
+    for tile in (1, 2, 3):
+        for (M, N, K), split in [((130, 136, 72), 1), ((256, 256, 256), 1), ((64, 64, 32), 1),
+                                 ((200, 264, 400), 3), ((33, 520, 1024), 4)]:
+            c = _case(3, M, N, K, pair, layout, epi)
+            _, desc = _check(c, variant=tlgemm.VARIANT_TILED, tile=tile, split_k=split)
+            assert "variant=tiled" in desc
+
+
+# --- the workloads at their full sizes ---------------------------------------------------
+
+def test_fp32_linear_128x768():
+    c = inputs.workload_fp32_linear_128x768()
+    _check(c)
+
+
+def test_fp16_narrow_16x4096x4096():
+    c = inputs.workload_fp16_narrow()
+    _, desc = _check(c)
+    assert "variant=stream" in desc
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gpt2_layer_m128(dtype):
+    for c in inputs.workload_gpt2_layer(M=128, dtype=dtype):
+        _check(c)
+
+
+def _sampled(case, npts=3000, rows=8, seed=0):
+    Y, desc = run_case(case)
+    y = to_f64(Y)
+    rng = np.random.default_rng(seed)
+    mi = rng.integers(0, case.M, npts)
+    ni = rng.integers(0, case.N, npts)
+    # whole first and last rows as well
+    mi = np.concatenate([mi, np.repeat([0, case.M - 1], case.N)])
+    ni = np.concatenate([ni, np.tile(np.arange(case.N), 2)])
+    ref = oracle.linear_points(case.X, case.W, case.b, dtype=case.in_dtype, layout=case.layout, gelu=case.gelu,
+                               mi=mi, ni=ni)
+    err = np.max(np.abs(y[mi, ni] - ref)) / np.max(np.abs(ref))
+    assert err <= TOL[case.in_dtype], f"{desc}: err {err:.3e}"
+    assert np.all(np.isfinite(y))
+    return y, desc
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_square_4096(dtype):
+    c = inputs.workload_square(dtype=dtype)
+    _, desc = _sampled(c)
+    assert "variant=tiled" in desc
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gpt2_stack_m8192_first_layer(dtype):
+    for c in inputs.workload_gpt2_stack(layers=1, dtype=dtype):
+        _sampled(c, npts=2000)
+
+
+# --- exact properties ------------------------------------------------------------------
+
+@pytest.mark.parametrize("variant,tile,split", [(tlgemm.VARIANT_GENERIC, 0, 0), (tlgemm.VARIANT_STREAM, 1, 0),
+                                                 (tlgemm.VARIANT_TILED, 1, 1), (tlgemm.VARIANT_TILED, 2, 4)])
+def test_identity_and_permutation_bitwise(variant, tile, split):
+    M, K = 48, 256
+    X = inputs.normal(5, (M, K), 1.0, "f32")
+    perm = np.random.default_rng(1).permutation(K)
+    for Wnp, want in [(np.eye(K, dtype=np.float32), X), (np.eye(K, dtype=np.float32)[perm], X[:, perm])]:
+        c = inputs.LinearCase("perm", M, K, K, "f32", "f32", "NK", False, False, X, Wnp, None)
+        Y, _ = run_case(c, variant=variant, tile=tile, split_k=split)
+        assert np.array_equal(Y.cpu().numpy(), want)
+
+
+def test_repeat_runs_bitwise():
+    for c, kw in [(inputs.workload_fp16_narrow(), {}),
+                  (inputs.random_case(9, 128, 768, 3072, "f32", bias=True), {}),
+                  (inputs.random_case(9, 100, 264, 512, "bf16", bias=True, gelu=True),
+                   dict(variant=tlgemm.VARIANT_TILED, split_k=5, tile=2))]:
+        dev = device_case(c)
+        first, _ = run_case(c, dev=dev, **kw)
+        for _ in range(5):
+            again, _ = run_case(c, dev=dev, **kw)
+            assert torch.equal(first, again)
+
+
+def test_replicated_rows_bitwise():
+    K = 4096
+    row = inputs.uniform(3, (1, K), -0.05, 0.05, "f16")
+    c = inputs.workload_fp16_narrow()
+    c.X = np.repeat(row, 16, axis=0)
+    Y, _ = run_case(c)
+    assert all(torch.equal(Y[0], Y[i]) for i in range(16))
+
+
+def test_misaligned_pointer_rejected():
+    c = inputs.random_case(4, 16, 64, 64, "f32")
+    X, W, _ = device_case(c)
+    Y = torch.empty((16, 65), device="cuda:0", dtype=torch.float32)
+    p = tlgemm.Plan.create(16, 64, 64, "f32")
+    with pytest.raises(tlgemm.TlgError) as e:
+        p.run_ptrs(X.data_ptr() + 4, W.data_ptr(), 0, Y.data_ptr())
+    assert e.value.status == tlgemm.ERR_MISALIGNED
+
+
+def test_stream_argument_and_workspace_reuse():
+    """Two plans sharing one workspace on a side stream give the oracle's results."""
+    s = torch.cuda.Stream()
+    cases = [inputs.random_case(11 + i, 128, 768, 768, "f32", bias=True) for i in range(2)]
+    plans = [tlgemm.Plan.create(128, 768, 768, "f32", bias=True, variant=tlgemm.VARIANT_TILED, split_k=4, tile=2)
+             for _ in cases]
+    ws = torch.empty(max(p.workspace_size for p in plans), dtype=torch.uint8, device="cuda:0")
+    outs = []
+    with torch.cuda.stream(s):
+        for c, p in zip(cases, plans):
+            X, W, b = device_case(c)
+            outs.append(tlgemm.run(p, X, W, b, workspace=ws, stream=s))
+    s.synchronize()
+    for c, y in zip(cases, outs):
+        assert normalized_error(to_f64(y), oracle.linear_case(c)) <= 1e-5
+
+
+def test_subnormal_fp16_inputs_not_flushed():
+    """Subnormal fp16 weights (|w| < 2^-14) must contribute, not flush to zero."""
+    M, N, K = 16, 32, 4096
+    X = inputs.store(np.ones((M, K)), "f16")
+    W = inputs.store(np.full((N, K), 2.0 ** -20), "f16")  # subnormal in fp16
+    c = inputs.LinearCase("sub", M, N, K, "f16", "f32", "NK", False, False, X, W, None)
+    Y, _ = run_case(c)
+    assert np.allclose(Y.cpu().numpy(), K * 2.0 ** -20, rtol=1e-6)
