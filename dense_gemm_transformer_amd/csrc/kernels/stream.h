@@ -1,127 +1,227 @@
 // Stream kernel for narrow M (M <= 64, weight out×in).
 //
-// "One multiply, one RTX 5090, eight kernels" ("The multiply", "Filling the
-// chip", "Where the time goes"): with 16 input rows each weight value takes
-// part in only 16 products, so the multiply is a stream of W from memory and
-// its time is the time to read W.  The design for gfx950:
+// "One multiply, one RTX 5090, eight kernels" ("The multiply", "Tiles, blocks
+// and SMs", "Filling the chip", "Where the time goes"): with 16 input rows
+// each weight value takes part in only 16 products, so the multiply is a
+// stream of W from memory.  The design for gfx950:
 //
-//  * One workgroup owns 16 rows of W (16 output columns) over all of K.  Its
-//    waves split K into contiguous ranges (the split-K of "Filling the
-//    chip"), so a 4096-row weight gives 256 workgroups, one per CU, and every
-//    CU streams its own 128 KiB slab of W.
-//  * W never touches LDS: each lane issues 16-byte loads straight into
-//    registers, all of a chunk's loads before any use, so one wave keeps
-//    LOADS×1 KiB of W in flight.  The 4 lanes of a W row read 64
-//    consecutive bytes per load and consecutive loads continue the row.
-//  * Products run on MFMA: 16×16×32 for fp16/bf16 (one 16-row block of X is
+//  * A workgroup has NB × KW waves.  It owns BN = 16·NB rows of W (each wave
+//    16 rows: one MFMA column block) and one K range of the grid's split.
+//    Inside the workgroup the KW waves of a column block split the K range
+//    again, so a 16-row tile over all of K is 8 waves that never talk to
+//    another workgroup (NB = 1, KW = 8: 256 workgroups for 4096 rows).
+//  * W never passes through LDS: each lane issues 16-byte loads straight into
+//    registers, all of a chunk's loads before the first product, so a wave
+//    keeps LOADS KiB of W in flight.
+//  * The X slice of the workgroup's K range is read with fully coalesced
+//    loads (consecutive threads, consecutive 16 bytes of one row) into LDS
+//    and every wave takes its MFMA operands from there.
+//  * Products run on MFMA: 16×16×32 for fp16/bf16 (a 16-row block of X is
 //    one MFMA row block) and 16×16×4 for fp32.  For fp32 one 16-byte load
 //    feeds four MFMAs: the k order inside a chunk is permuted identically
-//    for X and W, which leaves the dot products unchanged.
-//  * The wave partials are summed through LDS in a fixed order (wave 0, 1,
-//    ...), so results are bitwise reproducible run to run, then the fused
-//    epilogue (bias, GELU, rounding) writes Y.  No workspace, one launch.
+//    for X and W, which leaves every dot product unchanged.
+//  * The KW wave partials of a column block are summed through LDS in wave
+//    order.  With a grid split (S > 1, the split-K of "Filling the chip")
+//    each workgroup then publishes its partial tile, takes a ticket for the
+//    tile, and the last to arrive sums the S partials in split order.  Both
+//    sums run in a fixed order, so results are bitwise reproducible (the
+//    rule of "Optimizing a GPT-2-class transformer on a GPU", Act I).  One
+//    launch, no atomics on data.
 //
 // Rows of X past M and rows of W past N are clamped to valid rows (their
-// outputs are never stored); K past each wave's range loads as zero.
-
+// outputs are never stored); K past the split's range loads as zero.
 #pragma once
 #include "common.h"
 
 namespace tlg {
 
-template <int IN, int OUT, uint32_t EPI, int WAVES, int LOADS, int ROWB, bool EVENK>
-__global__ __launch_bounds__(64 * WAVES) void stream_kernel(const void* __restrict__ Xv,
-                                                           const void* __restrict__ Wv,
-                                                           const void* __restrict__ bias,
-                                                           void* __restrict__ Y, int M, int N, int K,
-                                                           int kper) {
+template <int IN, int NB, int KW, int LOADS, int ROWB>
+struct StreamGeom {
+    static constexpr int EPV = Elem<IN>::per16;  // elements per 16-byte load
+    static constexpr int KSTEP = 4 * EPV;        // k covered by one load across the 4 lane groups
+    static constexpr int CK = LOADS * KSTEP;     // k per wave per chunk
+    static constexpr int WCK = KW * CK;          // k per workgroup per chunk
+    static constexpr int XROWS = 16 * ROWB;
+    static constexpr int LDX = WCK + EPV;        // padded LDS row of the X chunk (elements)
+    static constexpr int X_BYTES = XROWS * LDX * (int)sizeof(typename Elem<IN>::storage);
+    static constexpr int RED_BYTES = KW > 1 ? NB * KW * ROWB * 4 * 64 * 4 : 0;
+    static constexpr int LDS_BYTES = X_BYTES + RED_BYTES;
+    static constexpr bool FITS = LDS_BYTES <= 160 * 1024;
+};
+
+template <int IN, int OUT, uint32_t EPI, int NB, int KW, int LOADS, int ROWB, bool EVEN, bool SPLIT>
+__global__ __launch_bounds__(64 * NB * KW) void stream_kernel(const void* __restrict__ Xv,
+                                                             const void* __restrict__ Wv,
+                                                             const void* __restrict__ bias,
+                                                             void* __restrict__ Y, float* __restrict__ ws,
+                                                             unsigned* __restrict__ tickets, int M, int N,
+                                                             int K, int kper) {
     using S = typename Elem<IN>::storage;
+    using G = StreamGeom<IN, NB, KW, LOADS, ROWB>;
     constexpr bool F32 = IN == TLG_F32;
-    constexpr int EPV = Elem<IN>::per16;   // elements per 16-byte load
-    constexpr int KSTEP = 4 * EPV;         // k covered by one load across the 4 lane groups
-    constexpr int CK = LOADS * KSTEP;      // k per chunk
+    constexpr int THREADS = 64 * NB * KW;
+    constexpr int EPV = G::EPV, KSTEP = G::KSTEP, CK = G::CK, WCK = G::WCK, LDX = G::LDX;
+    constexpr int XVPR = WCK / EPV;              // 16-byte vectors per X chunk row
+    constexpr int XVEC = G::XROWS * XVPR;
+    constexpr int XPT = (XVEC + THREADS - 1) / THREADS;
+    constexpr int BN = 16 * NB;
     const S* __restrict__ X = static_cast<const S*>(Xv);
     const S* __restrict__ W = static_cast<const S*>(Wv);
 
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
+    S* xs = reinterpret_cast<S*>(lds);
+
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int nb = wave / KW, kw = wave % KW;
     const int r = lane & 15, g = lane >> 4;
-    const int n0 = blockIdx.x * 16;
-    const S* Wrow = W + (int64_t)min(n0 + r, N - 1) * K;
-    const int kbeg = w * kper;
+    const int tile = blockIdx.x, split = blockIdx.y;
+    const int n0 = tile * BN;
+    const S* Wrow = W + (int64_t)min(n0 + nb * 16 + r, N - 1) * K;
+    const int kbeg = split * kper;
     const int kend = min(kbeg + kper, K);
 
     f32x4 acc[ROWB];
 #pragma unroll
     for (int rb = 0; rb < ROWB; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int kc = kbeg; kc < kend; kc += CK) {
+    for (int kc = kbeg; kc < kend; kc += WCK) {
+        // X chunk first (cache-resident, coalesced), then this wave's W
+        // stream; the scheduling barrier keeps every load ahead of the first use.
+        u32x4 xr[XPT];
+#pragma unroll
+        for (int i = 0; i < XPT; ++i) {
+            const int v = t + THREADS * i;
+            const int row = v / XVPR, k = kc + (v % XVPR) * EPV;
+            if ((XVEC % THREADS == 0 || v < XVEC) && (EVEN || k < kend))
+                xr[i] = ldg16(X + (int64_t)min(row, M - 1) * K + k);
+            else
+                xr[i] = u32x4{0u, 0u, 0u, 0u};
+        }
+        const int kw0 = kc + kw * CK;
         u32x4 wv[LOADS];
 #pragma unroll
         for (int j = 0; j < LOADS; ++j) {
-            const int k = kc + j * KSTEP + g * EPV;
-            if (EVENK || k < kend)
+            const int k = kw0 + j * KSTEP + g * EPV;
+            if (EVEN || k < kend)
                 wv[j] = ldg16(Wrow + k);
             else
                 wv[j] = u32x4{0u, 0u, 0u, 0u};
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < XPT; ++i) {
+            const int v = t + THREADS * i;
+            if (XVEC % THREADS == 0 || v < XVEC)
+                *reinterpret_cast<u32x4*>(xs + (v / XVPR) * LDX + (v % XVPR) * EPV) = xr[i];
+        }
+        __syncthreads();
 #pragma unroll
         for (int rb = 0; rb < ROWB; ++rb) {
-            const S* Xrow = X + (int64_t)min(rb * 16 + r, M - 1) * K;
-            u32x4 xv[LOADS];
 #pragma unroll
             for (int j = 0; j < LOADS; ++j) {
-                const int k = kc + j * KSTEP + g * EPV;
-                if (EVENK || k < kend)
-                    xv[j] = ldg16(Xrow + k);
-                else
-                    xv[j] = u32x4{0u, 0u, 0u, 0u};
-            }
-#pragma unroll
-            for (int j = 0; j < LOADS; ++j) {
+                const u32x4 xv =
+                    *reinterpret_cast<const u32x4*>(xs + (rb * 16 + r) * LDX + kw * CK + j * KSTEP + g * EPV);
                 if constexpr (F32) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        acc[rb] = mfma16_f32(__uint_as_float(xv[j][i]), __uint_as_float(wv[j][i]), acc[rb]);
+                    for (int e = 0; e < 4; ++e)
+                        acc[rb] = mfma16_f32(__uint_as_float(xv[e]), __uint_as_float(wv[j][e]), acc[rb]);
                 } else {
-                    acc[rb] = mfma16_16bit<IN>(xv[j], wv[j], acc[rb]);
+                    acc[rb] = mfma16_16bit<IN>(xv, wv[j], acc[rb]);
                 }
             }
         }
+        if (kc + WCK < kend) __syncthreads();  // the next chunk overwrites xs
     }
 
-    // Fixed-order reduction of the wave partials.  A 16×16 MFMA accumulator
-    // holds column (lane % 16), rows 4*(lane / 16) + v.
-    __shared__ float red[WAVES][ROWB][4][64];
+    // In-workgroup K reduction: wave kw = 0 of each column block sums the KW
+    // partials in wave order.  A 16×16 MFMA accumulator holds column
+    // (lane % 16) and rows 4*(lane / 16) + e.
+    if constexpr (KW > 1) {
+        float* red = reinterpret_cast<float*>(lds + G::X_BYTES);  // [nb][kw][rb][e][lane]
 #pragma unroll
-    for (int rb = 0; rb < ROWB; ++rb)
+        for (int rb = 0; rb < ROWB; ++rb)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) red[w][rb][v][lane] = acc[rb][v];
-    __syncthreads();
-
-    for (int o = threadIdx.x; o < ROWB * 256; o += 64 * WAVES) {
-        const int rb = o >> 8, ml = (o >> 4) & 15, c = o & 15;
-        const int src = (ml >> 2) * 16 + c, v = ml & 3;
-        float s = 0.0f;
+            for (int e = 0; e < 4; ++e) red[(((nb * KW + kw) * ROWB + rb) * 4 + e) * 64 + lane] = acc[rb][e];
+        __syncthreads();
+        if (kw == 0) {
 #pragma unroll
-        for (int ww = 0; ww < WAVES; ++ww) s += red[ww][rb][v][src];
-        const int m = rb * 16 + ml, n = n0 + c;
-        if (m < M && n < N) {
-            float b = 0.0f;
-            if constexpr ((EPI & TLG_EPI_BIAS) != 0) b = load_elem<IN>(bias, n);
-            store_out<OUT>(Y, (int64_t)m * N + n, epilogue<EPI>(s, b));
+            for (int rb = 0; rb < ROWB; ++rb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float s = red[(((nb * KW) * ROWB + rb) * 4 + e) * 64 + lane];
+#pragma unroll
+                    for (int q = 1; q < KW; ++q) s += red[(((nb * KW + q) * ROWB + rb) * 4 + e) * 64 + lane];
+                    acc[rb][e] = s;
+                }
         }
+    }
+
+    const int n = n0 + nb * 16 + r;
+    if constexpr (!SPLIT) {
+        if (kw != 0) return;
+        float b = 0.0f;
+        if constexpr ((EPI & TLG_EPI_BIAS) != 0)
+            if (n < N) b = load_elem<IN>(bias, n);
+#pragma unroll
+        for (int rb = 0; rb < ROWB; ++rb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int m = rb * 16 + 4 * g + e;
+                if (m < M && n < N) store_out<OUT>(Y, (int64_t)m * N + n, epilogue<EPI>(acc[rb][e], b));
+            }
+    } else {
+        // Partials in fragment order [split][tile][nb][rb][lane] (one
+        // 16-byte store per lane); the reducing workgroup reads the same order.
+        f32x4* frag = reinterpret_cast<f32x4*>(ws);
+        const int64_t per_split = (int64_t)gridDim.x * NB * ROWB * 64;
+        const int64_t base = ((int64_t)(tile * NB + nb) * ROWB) * 64 + lane;
+        if (kw == 0)
+#pragma unroll
+            for (int rb = 0; rb < ROWB; ++rb) frag[split * per_split + base + rb * 64] = acc[rb];
+        // Release this workgroup's partials at device scope (one fence after
+        // the workgroup barrier covers every wave), then take the tile's ticket.
+        __syncthreads();
+        __shared__ unsigned last;
+        if (t == 0) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            last = atomicAdd(&tickets[tile], 1u) == gridDim.y - 1;
+            if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        }
+        __syncthreads();
+        if (!last || kw != 0) return;
+        const int splits = gridDim.y;
+        float b = 0.0f;
+        if constexpr ((EPI & TLG_EPI_BIAS) != 0)
+            if (n < N) b = load_elem<IN>(bias, n);
+#pragma unroll
+        for (int rb = 0; rb < ROWB; ++rb) {
+            f32x4 part[kStreamMaxSplit];  // every split's fragment in flight, then the ordered sum
+#pragma unroll
+            for (int z = 0; z < kStreamMaxSplit; ++z)
+                part[z] = z < splits ? frag[z * per_split + base + rb * 64] : f32x4{0.f, 0.f, 0.f, 0.f};
+            f32x4 s4 = part[0];
+#pragma unroll
+            for (int z = 1; z < kStreamMaxSplit; ++z)
+                if (z < splits) s4 += part[z];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int m = rb * 16 + 4 * g + e;
+                if (m < M && n < N) store_out<OUT>(Y, (int64_t)m * N + n, epilogue<EPI>(s4[e], b));
+            }
+        }
+        if (t == 0) __hip_atomic_store(&tickets[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
-template <int I, int WAVES, int LOADS>
-static int launch_stream_cfg(const tlg_plan& p, const void* X, const void* W, const void* bias, void* Y,
+template <int I, int NB, int KW, int LOADS>
+static int launch_stream_cfg(const tlg_plan& p, const void* X, const void* W, const void* bias, void* Y, void* ws,
                              hipStream_t stream) {
-    constexpr int epv = Elem<I>::per16;
-    constexpr int ck = LOADS * 4 * epv;
-    int kper = (int)ceil_div(ceil_div(p.K, WAVES), epv) * epv;
-    const bool evenk = (p.K % ((int64_t)WAVES * ck)) == 0;
-    if (evenk) kper = (int)(p.K / WAVES);
-    const dim3 grid((unsigned)p.grid_x), block(64 * WAVES);
+    const int S = p.split;
+    const int kper = (int)p.kper;
+    const bool even = (int64_t)kper * S == p.K && kper % (KW * LOADS * 4 * Elem<I>::per16) == 0;
+    const dim3 grid((unsigned)p.grid_x, (unsigned)S), block(64 * NB * KW);
+    unsigned* tickets = static_cast<unsigned*>(ws);
+    float* part = ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + stream_ticket_bytes(p.grid_x)) : nullptr;
     auto with_out = [&](auto f) {
         if constexpr (I == TLG_F32) return f(ic<TLG_F32>{});
         else if (p.out_dt == TLG_F32) return f(ic<TLG_F32>{});
@@ -131,18 +231,28 @@ static int launch_stream_cfg(const tlg_plan& p, const void* X, const void* W, co
         return with_epi(p.epi, [&](auto epi) {
             constexpr int O = decltype(out)::value;
             constexpr uint32_t E = (uint32_t)decltype(epi)::value;
-            auto go = [&](auto rowb, auto even) {
-                hipLaunchKernelGGL((stream_kernel<I, O, E, WAVES, LOADS, decltype(rowb)::value,
-                                                  decltype(even)::value>),
-                                   grid, block, 0, stream, X, W, bias, Y, (int)p.M, (int)p.N, (int)p.K, kper);
-                return check_launch("stream_kernel");
+            auto go = [&](auto rowb, auto ev, auto sp) -> int {
+                constexpr int RB = decltype(rowb)::value;
+                if constexpr (!StreamGeom<I, NB, KW, LOADS, RB>::FITS) {
+                    set_error("stream configuration does not fit in LDS for M=%lld", (long long)p.M);
+                    return TLG_ERR_UNSUPPORTED;
+                } else {
+                    hipLaunchKernelGGL((stream_kernel<I, O, E, NB, KW, LOADS, RB, decltype(ev)::value,
+                                                      decltype(sp)::value>),
+                                       grid, block, 0, stream, X, W, bias, Y, part, tickets, (int)p.M, (int)p.N,
+                                       (int)p.K, kper);
+                    return check_launch("stream_kernel");
+                }
             };
-            auto by_rowb = [&](auto even) {
-                if (p.rowb == 1) return go(ic<1>{}, even);
-                if (p.rowb == 2) return go(ic<2>{}, even);
-                return go(ic<4>{}, even);
+            auto by_split = [&](auto rowb, auto ev) {
+                return S > 1 ? go(rowb, ev, std::true_type{}) : go(rowb, ev, std::false_type{});
             };
-            return evenk ? by_rowb(std::true_type{}) : by_rowb(std::false_type{});
+            auto by_even = [&](auto rowb) {
+                return even ? by_split(rowb, std::true_type{}) : by_split(rowb, std::false_type{});
+            };
+            if (p.rowb == 1) return by_even(ic<1>{});
+            if (p.rowb == 2) return by_even(ic<2>{});
+            return by_even(ic<4>{});
         });
     });
 }
@@ -150,14 +260,20 @@ static int launch_stream_cfg(const tlg_plan& p, const void* X, const void* W, co
 // All stream launches for one input dtype; explicitly instantiated once per
 // dtype in its own translation unit.
 template <int I>
-int launch_stream_in(const tlg_plan& p, const void* X, const void* W, const void* bias, void* Y,
+int launch_stream_in(const tlg_plan& p, const void* X, const void* W, const void* bias, void* Y, void* ws,
                      hipStream_t stream) {
-    static_assert(kNumStream == 3, "stream configurations changed");
+    static_assert(kNumStream == 5, "stream configurations changed");
+#define TLG_STREAM_CASE(i) \
+    case i: return launch_stream_cfg<I, kStream[i].nb, kStream[i].kw, kStream[i].loads>(p, X, W, bias, Y, ws, stream);
     switch (p.tile) {
-    case 0: return launch_stream_cfg<I, kStream[0].waves, kStream[0].loads>(p, X, W, bias, Y, stream);
-    case 1: return launch_stream_cfg<I, kStream[1].waves, kStream[1].loads>(p, X, W, bias, Y, stream);
-    default: return launch_stream_cfg<I, kStream[2].waves, kStream[2].loads>(p, X, W, bias, Y, stream);
+        TLG_STREAM_CASE(0)
+        TLG_STREAM_CASE(1)
+        TLG_STREAM_CASE(2)
+        TLG_STREAM_CASE(3)
+        TLG_STREAM_CASE(4)
+    default: set_error("bad stream tile"); return TLG_ERR_INVALID_ARG;
     }
+#undef TLG_STREAM_CASE
 }
 
 }  // namespace tlg

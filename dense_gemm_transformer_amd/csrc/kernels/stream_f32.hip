@@ -3,6 +3,6 @@
 #include "stream.h"
 
 namespace tlg {
-template int launch_stream_in<TLG_F32>(const tlg_plan&, const void*, const void*, const void*, void*,
+template int launch_stream_in<TLG_F32>(const tlg_plan&, const void*, const void*, const void*, void*, void*,
                                         hipStream_t);
 }  // namespace tlg

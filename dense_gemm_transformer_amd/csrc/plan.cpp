@@ -12,6 +12,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <algorithm>
 #include <cstring>
 #include <new>
 #include <string>
@@ -91,6 +92,8 @@ static int fill_generic(tlg_plan& p) {
     return TLG_OK;
 }
 
+static int stream_rowb(int64_t M) { return M <= 16 ? 1 : M <= 32 ? 2 : 4; }
+
 static int fill_stream(tlg_plan& p, int tile, int split) {
     if (p.M > kStreamMaxM) {
         set_error("stream kernel handles M <= %d (got M=%lld)", kStreamMaxM, (long long)p.M);
@@ -109,24 +112,54 @@ static int fill_stream(tlg_plan& p, int tile, int split) {
         return TLG_ERR_INVALID_ARG;
     }
     const StreamCfg& c = kStream[tile];
-    if (split != 0 && split != c.waves) {
-        set_error("stream kernel splits K over its %d waves; split_k=%d not available", c.waves, split);
+    const int rowb = stream_rowb(p.M);
+    if (stream_lds_bytes(c, p.in_dt, rowb) > kLdsBytes) {
+        set_error("stream configuration %d does not fit in LDS for M=%lld", tile, (long long)p.M);
         return TLG_ERR_UNSUPPORTED;
     }
+    const int64_t bn = 16 * c.nb;
+    const int64_t wck = (int64_t)c.kw * c.loads * (p.in_dt == TLG_F32 ? 16 : 32);  // K per workgroup chunk
+    const int64_t tiles = ceil_div(p.N, bn);
+    const int64_t chunks = ceil_div(p.K, wck);
+    int64_t S = split;
+    if (S == 0) {  // fill rule: one workgroup per CU, each split at least one full chunk
+        S = std::min<int64_t>(std::min<int64_t>(ceil_div(kNumCUs, tiles), chunks), kStreamMaxSplit);
+    }
+    if (S < 1 || S > kStreamMaxSplit || S > chunks) {
+        set_error("stream split_k=%lld must be in 1..%lld", (long long)S,
+                  (long long)std::min<int64_t>(chunks, kStreamMaxSplit));
+        return TLG_ERR_UNSUPPORTED;
+    }
+    // Each split covers whole chunks; drop splits that would be empty.
+    p.kper = ceil_div(ceil_div(p.K, S), wck) * wck;
+    S = ceil_div(p.K, p.kper);
     p.variant = TLG_VARIANT_STREAM;
     p.tile = tile;
-    p.split = c.waves;
-    p.rowb = (int)ceil_div(p.M, 16);
-    p.bm = 16 * p.rowb;
-    p.bn = 16;
-    p.bk = c.loads * (p.in_dt == TLG_F32 ? 16 : 32);  // K per chunk per wave
-    p.threads = 64 * c.waves;
-    p.grid_x = ceil_div(p.N, 16);
-    p.grid_y = 1;
+    p.split = (int)S;
+    p.rowb = rowb;
+    p.bm = 16 * rowb;
+    p.bn = (int)bn;
+    p.bk = (int)wck;
+    p.threads = 64 * c.nb * c.kw;
+    p.grid_x = tiles;
+    p.grid_y = S;
     p.grid_z = 1;
     p.launches = 1;
-    p.ws_bytes = 0;
+    p.ws_bytes = S > 1 ? stream_ticket_bytes(tiles) + (size_t)S * tiles * bn * 16 * rowb * sizeof(float) : 0;
     return TLG_OK;
+}
+
+// Narrow-M choice: with enough 16-row tiles to fill the chip the whole K
+// range of a tile stays inside one workgroup (no inter-workgroup traffic,
+// whose device-scope fences cost several microseconds on a multi-XCD part);
+// otherwise 128-row tiles split K across workgroups.
+static int auto_stream(tlg_plan& p) {
+    const int rowb = stream_rowb(p.M);
+    if (ceil_div(p.N, 16) >= kNumCUs / 2) {
+        for (int cfg : {0, 1, 4})
+            if (stream_lds_bytes(kStream[cfg], p.in_dt, rowb) <= kLdsBytes) return fill_stream(p, cfg, 1);
+    }
+    return fill_stream(p, 2, 0);
 }
 
 static int fill_tiled(tlg_plan& p, int tile, int split) {
@@ -171,7 +204,7 @@ static int fill_tiled(tlg_plan& p, int tile, int split) {
 // (small M·N against a long K, as in the narrow GPT-2 layers).
 static int auto_plan(tlg_plan& p) {
     if (!rows_aligned16(p)) return fill_generic(p);
-    if (p.layout == TLG_NK && p.M <= kStreamMaxM) return fill_stream(p, 0, 0);
+    if (p.layout == TLG_NK && p.M <= kStreamMaxM) return auto_stream(p);
     const int big = 0, small = 1;
     const TileCfg& cb = tiled_cfg(p.in_dt, big);
     const int64_t tiles_big = ceil_div(p.M, cb.bm) * ceil_div(p.N, cb.bn);
@@ -245,7 +278,7 @@ int gemm_plan_ex(tlg_plan_t* out, int64_t M, int64_t N, int64_t K, tlg_dtype in_
                                   ? table_lookup(M, N, K, in_dt, out_dt, layout, epi_flags)
                                   : nullptr;
         if (row) {
-            rc = row->variant == TLG_VARIANT_STREAM  ? fill_stream(p, row->tile, 0)
+            rc = row->variant == TLG_VARIANT_STREAM  ? fill_stream(p, row->tile, row->split)
                  : row->variant == TLG_VARIANT_TILED ? fill_tiled(p, row->tile, row->split)
                                                      : fill_generic(p);
         } else if (split != 0 || tile_sel != 0) {
@@ -261,7 +294,11 @@ int gemm_plan_ex(tlg_plan_t* out, int64_t M, int64_t N, int64_t K, tlg_dtype in_
         }
         rc = fill_generic(p);
     } else if (variant == TLG_VARIANT_STREAM) {
-        rc = fill_stream(p, tile_sel ? tile_sel - 1 : 0, split);
+        if (tile_sel == 0 && split == 0)
+            rc = p.M <= kStreamMaxM && p.layout == TLG_NK && rows_aligned16(p) ? auto_stream(p)
+                                                                              : fill_stream(p, 0, 0);
+        else
+            rc = fill_stream(p, tile_sel ? tile_sel - 1 : 2, split);
     } else if (variant == TLG_VARIANT_TILED) {
         rc = fill_tiled(p, tile_sel ? tile_sel - 1 : 0, split);
     } else {
@@ -297,7 +334,7 @@ int gemm_plan_info(tlg_plan_t p, tlg_plan_info* info) {
     info->split_k = p->split;
     info->threads = p->threads;
     info->workgroups = p->grid_x * p->grid_y * p->grid_z +
-                       (p->launches > 1 ? ceil_div(p->M * p->N, 256 * 4) : 0);
+                       (p->launches > 1 ? ceil_div(p->M * p->N, 256 * 4) : 0);  // + split-K reducer
     info->launches = p->launches;
     info->workspace_bytes = p->ws_bytes;
     return TLG_OK;

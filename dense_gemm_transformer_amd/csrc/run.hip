@@ -13,17 +13,17 @@ namespace tlg {
 int launch_generic(const tlg_plan& p, const void* X, const void* W, const void* bias, void* Y,
                    hipStream_t stream);
 template <int I>
-int launch_stream_in(const tlg_plan& p, const void* X, const void* W, const void* bias, void* Y,
+int launch_stream_in(const tlg_plan& p, const void* X, const void* W, const void* bias, void* Y, void* ws,
                      hipStream_t stream);
 template <int I>
 int launch_tiled_in(const tlg_plan& p, const void* X, const void* W, const void* bias, void* Y, void* ws,
                     hipStream_t stream);
 
-static int launch_stream(const tlg_plan& p, const void* X, const void* W, const void* bias, void* Y,
+static int launch_stream(const tlg_plan& p, const void* X, const void* W, const void* bias, void* Y, void* ws,
                          hipStream_t s) {
-    if (p.in_dt == TLG_F32) return launch_stream_in<TLG_F32>(p, X, W, bias, Y, s);
-    if (p.in_dt == TLG_F16) return launch_stream_in<TLG_F16>(p, X, W, bias, Y, s);
-    return launch_stream_in<TLG_BF16>(p, X, W, bias, Y, s);
+    if (p.in_dt == TLG_F32) return launch_stream_in<TLG_F32>(p, X, W, bias, Y, ws, s);
+    if (p.in_dt == TLG_F16) return launch_stream_in<TLG_F16>(p, X, W, bias, Y, ws, s);
+    return launch_stream_in<TLG_BF16>(p, X, W, bias, Y, ws, s);
 }
 
 static int launch_tiled(const tlg_plan& p, const void* X, const void* W, const void* bias, void* Y, void* ws,
@@ -94,7 +94,7 @@ extern "C" int gemm_run(tlg_plan_t p, const void* X, const void* W, const void* 
     const hipStream_t s = static_cast<hipStream_t>(stream);
     switch (p->variant) {
     case TLG_VARIANT_GENERIC: return launch_generic(*p, X, W, bias, Y, s);
-    case TLG_VARIANT_STREAM: return launch_stream(*p, X, W, bias, Y, s);
+    case TLG_VARIANT_STREAM: return launch_stream(*p, X, W, bias, Y, workspace, s);
     case TLG_VARIANT_TILED: return launch_tiled(*p, X, W, bias, Y, workspace, s);
     default: set_error("gemm_run: corrupt plan"); return TLG_ERR_INVALID_ARG;
     }

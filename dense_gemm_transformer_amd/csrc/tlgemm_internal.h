@@ -40,20 +40,36 @@ constexpr TileCfg kTiled16[] = {
 constexpr int kNumTiledF32 = sizeof(kTiledF32) / sizeof(kTiledF32[0]);
 constexpr int kNumTiled16 = sizeof(kTiled16) / sizeof(kTiled16[0]);
 
-// Stream kernel: one workgroup owns 16 output columns (16 rows of W), its
-// waves split K, and each wave keeps `loads` 16-byte weight loads per lane in
-// flight per chunk.
+// Stream kernel: a workgroup has nb × kw waves; it owns 16·nb rows of W
+// (16 per wave) and one K range of the grid split, which its kw waves split
+// again.  Each wave keeps `loads` 16-byte weight loads per lane in flight per
+// chunk (a chunk is loads·32 fp16/bf16 or loads·16 fp32 elements of K).
 struct StreamCfg {
-    int waves;  // waves per workgroup = in-workgroup K split
+    int nb;     // 16-row column blocks per workgroup
+    int kw;     // waves splitting the workgroup's K range
     int loads;  // 16-byte loads per lane per chunk
 };
 constexpr StreamCfg kStream[] = {
-    {8, 16},  // 0: 512-wide fp16 chunks per wave (256 fp32)
-    {4, 16},  // 1
-    {8, 8},   // 2
+    {1, 8, 16},  // 0: 16-row tiles over all of K by 8 waves; no inter-workgroup traffic (M <= 16)
+    {1, 8, 4},   // 1: same with 128-wide fp16 chunks (room in LDS for X up to 32 rows)
+    {8, 1, 16},  // 2: 128-row tiles, K split across workgroups
+    {4, 1, 32},  // 3: 64-row tiles, 1024-wide fp16 chunks, K split across workgroups
+    {2, 4, 4},   // 4: 32-row tiles, 4-way in-workgroup split
 };
 constexpr int kNumStream = sizeof(kStream) / sizeof(kStream[0]);
-constexpr int kStreamMaxM = 64;  // 4 row blocks of 16
+constexpr int kStreamMaxM = 64;      // 4 row blocks of 16
+constexpr int kStreamMaxSplit = 16;  // K splits summed by the last workgroup of a tile
+constexpr int kLdsBytes = 160 * 1024;
+
+// LDS of one stream workgroup: the X chunk (16·rowb rows, padded by 16
+// bytes) plus the in-workgroup reduction buffer.  rowb is 1, 2 or 4.
+inline int64_t stream_lds_bytes(const StreamCfg& c, int in_dt, int rowb) {
+    const int64_t esize = in_dt == 0 ? 4 : 2, epv = 16 / esize;
+    const int64_t wck = (int64_t)c.kw * c.loads * 4 * epv;
+    const int64_t x = 16 * rowb * (wck + epv) * esize;
+    const int64_t red = c.kw > 1 ? (int64_t)c.nb * c.kw * rowb * 4 * 64 * 4 : 0;
+    return x + red;
+}
 
 // Generic kernel: 64×64 tile, 256 threads, 4×4 outputs per thread.
 constexpr int kGenericBM = 64, kGenericBN = 64, kGenericBK = 16;
@@ -66,7 +82,8 @@ struct tlg_plan {
     uint32_t epi;
     int variant;
     int tile;      // index into the variant's list
-    int split;     // K split (TILED: across workgroups; STREAM: waves)
+    int split;     // K split across workgroups (TILED, STREAM)
+    int64_t kper;  // K range per split (STREAM)
     int rowb;      // STREAM: 16-row blocks covering M
     int threads;
     int64_t grid_x, grid_y, grid_z;
@@ -79,4 +96,7 @@ namespace tlg {
 void set_error(const char* fmt, ...);
 int launch_plan(const tlg_plan& p, const void* X, const void* W, const void* bias, void* Y,
                 void* ws, void* stream);
+// Workspace of a split stream plan: one ticket per tile (a 256-byte aligned
+// block), then the fp32 partials [S][M][N].
+inline size_t stream_ticket_bytes(int64_t tiles) { return (size_t)ceil_div(tiles * 4, 256) * 256; }
 }  // namespace tlg

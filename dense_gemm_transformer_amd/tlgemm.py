@@ -227,7 +227,7 @@ def run(plan: Plan, X, W, bias=None, Y=None, workspace=None, stream=None):
         Y = torch.empty((plan.M, plan.N), dtype=torch_dtype(plan.out_dtype), device=X.device)
     need = plan.workspace_size
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=X.device)  # zero before first use
     s = stream if stream is not None else torch.cuda.current_stream(X.device)
     for name, t in (("X", X), ("W", W), ("Y", Y), ("bias", bias)):
         if t is not None and not (t.is_cuda and t.is_contiguous()):

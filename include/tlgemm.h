@@ -66,7 +66,7 @@ enum {
 typedef enum {
     TLG_VARIANT_AUTO = -1,
     TLG_VARIANT_GENERIC = 0, /* predicated LDS-tiled fp32-FMA kernel: any shape, any alignment */
-    TLG_VARIANT_STREAM = 1,  /* narrow M: weights streamed HBM->registers, MFMA, in-workgroup split-K */
+    TLG_VARIANT_STREAM = 1,  /* narrow M: weights streamed HBM->registers, MFMA, one-launch split-K */
     TLG_VARIANT_TILED = 2    /* LDS-tiled MFMA kernel, optional split-K across workgroups */
 } tlg_variant;
 
@@ -75,7 +75,7 @@ typedef struct tlg_plan* tlg_plan_t;
 /* Planner overrides (tests and tuning). Zero / TLG_VARIANT_AUTO means "planner's choice". */
 typedef struct {
     int variant; /* tlg_variant */
-    int split_k; /* split of K across workgroups (TILED) or waves (STREAM); 0 = planner */
+    int split_k; /* split of K across workgroups; 0 = planner */
     int tile;    /* index into the variant's tile list; 0 = planner, k>0 selects entry k-1 */
 } tlg_plan_opts;
 
@@ -119,8 +119,11 @@ int gemm_plan_info(tlg_plan_t p, tlg_plan_info* info);
  * TLG_EPI_BIAS) must be non-NULL device pointers, 16-byte aligned; bias must
  * be NULL when TLG_EPI_BIAS is not set.  Y must not overlap X, W or bias.
  * workspace: device memory of at least gemm_workspace_size(p) bytes when
- * that is non-zero (its contents need no initialisation and are scratch
- * after the call); it may be NULL when the size is 0.  A plan is immutable:
+ * that is non-zero; it may be NULL when the size is 0.  It must be
+ * zero-filled before its first use, and every completed run leaves it
+ * reusable: split stream plans keep one arrival counter per output tile in
+ * it, which the last workgroup of each tile resets to zero.  Runs in flight
+ * at the same time need distinct workspaces.  A plan is immutable:
  * concurrent runs of one plan are safe when each has its own workspace.
  */
 int gemm_run(tlg_plan_t p, const void* X, const void* W, const void* bias, void* Y,

@@ -33,7 +33,29 @@ def test_narrow_fp16_goes_to_stream():
     p = _plan(16, 4096, 4096, "f16", "f16")
     i = p.info
     assert i.variant == t.VARIANT_STREAM and i.workgroups == 256 and i.threads == 512
-    assert i.split_k == 8 and i.workspace_bytes == 0 and i.launches == 1
+    # 16-row tiles, 8 waves split all of K inside the workgroup: no split across workgroups
+    assert (i.tile_n, i.tile_k, i.split_k, i.launches, i.workspace_bytes) == (16, 4096, 1, 1, 0)
+
+
+def test_stream_split_rules():
+    # narrow N: 128-row tiles with K split across workgroups
+    i = _plan(16, 768, 3072, "f16").info
+    assert (i.variant, i.tile_n, i.split_k) == (t.VARIANT_STREAM, 128, 6)
+    assert i.workspace_bytes == 256 + 6 * 6 * 128 * 16 * 4  # tickets, then fragment-order partials
+    i = _plan(5, 1000, 1000, "f32").info  # fp32 chunk of 256: 4 chunks over 8 tiles
+    assert (i.variant, i.split_k) == (t.VARIANT_STREAM, 4)
+    i = _plan(16, 4096, 4096, "f16", variant=t.VARIANT_STREAM, tile=3, split_k=1).info
+    assert (i.split_k, i.workspace_bytes, i.workgroups) == (1, 0, 32)
+    with pytest.raises(t.TlgError):
+        _plan(16, 4096, 4096, "f16", variant=t.VARIANT_STREAM, tile=3, split_k=17)
+    i = _plan(16, 4096, 4096, "f16", variant=t.VARIANT_STREAM, tile=3, split_k=3).info  # 8 chunks over 3 splits
+    assert i.split_k == 3
+    # X for 64 rows over a 4096-wide chunk does not fit in LDS
+    with pytest.raises(t.TlgError) as e:
+        _plan(64, 4096, 4096, "f16", variant=t.VARIANT_STREAM, tile=1)
+    assert e.value.status == t.ERR_UNSUPPORTED
+    assert _plan(64, 4096, 4096, "f16").info.variant == t.VARIANT_STREAM
+    assert _plan(33, 4096, 4096, "bf16").info.tile_m == 64
 
 
 def test_square_fp32_goes_to_tiled():

@@ -51,12 +51,38 @@ def test_generic(pair, layout, epi):
 
 @pytest.mark.parametrize("pair", PAIRS, ids=lambda p: f"{p[0]}->{p[1]}")
 @pytest.mark.parametrize("epi", EPIS, ids=["none", "bias", "gelu", "bias+gelu"])
-@pytest.mark.parametrize("tile", [1, 2, 3])
+@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4, 5])
 def test_stream(pair, epi, tile):
-    for M, N, K in [(1, 16, 8), (16, 48, 512), (5, 50, 520), (17, 33, 1032), (40, 100, 264), (64, 16, 4096)]:
+    ran = 0
+    for M, N, K in [(1, 16, 8), (16, 48, 512), (5, 50, 520), (17, 36, 1032), (40, 100, 264), (64, 16, 4096),
+                    (3, 300, 3000)]:
         c = _case(2, M, N, K, pair, "NK", epi)
-        _, desc = _check(c, variant=tlgemm.VARIANT_STREAM, tile=tile)
+        try:
+            _, desc = _check(c, variant=tlgemm.VARIANT_STREAM, tile=tile)
+        except tlgemm.TlgError as e:  # configurations whose X chunk does not fit in LDS for this M
+            assert e.status == tlgemm.ERR_UNSUPPORTED and "LDS" in str(e), str(e)
+            continue
         assert "variant=stream" in desc
+        ran += 1
+    assert ran >= 2
+
+
+@pytest.mark.parametrize("pair", [("f32", "f32"), ("f16", "f16"), ("bf16", "f32")], ids=lambda p: f"{p[0]}->{p[1]}")
+@pytest.mark.parametrize("split", [1, 2, 3, 7])
+def test_stream_forced_split(pair, split):
+    """Cross-workgroup split-K with the last-arriving reduction, ragged K and N tails."""
+    for M, N, K in [(16, 260, 3000), (33, 520, 2048), (64, 132, 4104)]:
+        c = _case(5, M, N, K, pair, "NK", (True, True))
+        ck = 512 if pair[0] != "f32" else 256
+        if split > -(-K // ck):  # more splits than K chunks: refused by the planner
+            with pytest.raises(tlgemm.TlgError) as e:
+                run_case(c, variant=tlgemm.VARIANT_STREAM, tile=3, split_k=split)
+            assert e.value.status == tlgemm.ERR_UNSUPPORTED
+            continue
+        _, desc = _check(c, variant=tlgemm.VARIANT_STREAM, tile=3, split_k=split)
+        # each split covers whole chunks, so a split that would be empty is dropped
+        kper = -(-(-(-K // split)) // ck) * ck
+        assert f"split={-(-K // kper)} " in desc
 
 
 @pytest.mark.parametrize("pair", PAIRS, ids=lambda p: f"{p[0]}->{p[1]}")
@@ -122,10 +148,11 @@ def test_gpt2_stack_m8192_first_layer(dtype):
 
 # --- exact properties ------------------------------------------------------------------
 
-@pytest.mark.parametrize("variant,tile,split", [(tlgemm.VARIANT_GENERIC, 0, 0), (tlgemm.VARIANT_STREAM, 1, 0),
+@pytest.mark.parametrize("variant,tile,split", [(tlgemm.VARIANT_GENERIC, 0, 0), (tlgemm.VARIANT_STREAM, 0, 0),
+                                                 (tlgemm.VARIANT_STREAM, 3, 4), (tlgemm.VARIANT_STREAM, 5, 0),
                                                  (tlgemm.VARIANT_TILED, 1, 1), (tlgemm.VARIANT_TILED, 2, 4)])
 def test_identity_and_permutation_bitwise(variant, tile, split):
-    M, K = 48, 256
+    M, K = 48, 1024
     X = inputs.normal(5, (M, K), 1.0, "f32")
     perm = np.random.default_rng(1).permutation(K)
     for Wnp, want in [(np.eye(K, dtype=np.float32), X), (np.eye(K, dtype=np.float32)[perm], X[:, perm])]:
@@ -136,6 +163,7 @@ def test_identity_and_permutation_bitwise(variant, tile, split):
 
 def test_repeat_runs_bitwise():
     for c, kw in [(inputs.workload_fp16_narrow(), {}),
+                  (inputs.random_case(9, 16, 768, 3072, "f16"), dict(variant=tlgemm.VARIANT_STREAM, tile=3, split_k=6)),
                   (inputs.random_case(9, 128, 768, 3072, "f32", bias=True), {}),
                   (inputs.random_case(9, 100, 264, 512, "bf16", bias=True, gelu=True),
                    dict(variant=tlgemm.VARIANT_TILED, split_k=5, tile=2))]:
