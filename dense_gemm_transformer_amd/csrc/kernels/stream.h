@@ -1,4 +1,4 @@
-// Stream kernel for narrow M (M <= 64, weight out×in).
+// Stream kernel for narrow M (weight out×in): 16 to 64 rows per workgroup.
 //
 // "One multiply, one RTX 5090, eight kernels" ("The multiply", "Tiles, blocks
 // and SMs", "Filling the chip", "Where the time goes"): with 16 input rows
@@ -53,7 +53,7 @@ template <int IN, int OUT, uint32_t EPI, int NB, int KW, int LOADS, int ROWB, bo
 __global__ __launch_bounds__(64 * NB * KW) void stream_kernel(const void* __restrict__ Xv,
                                                              const void* __restrict__ Wv,
                                                              const void* __restrict__ bias,
-                                                             void* __restrict__ Y, float* __restrict__ ws,
+                                                             void* __restrict__ Yv, float* __restrict__ ws,
                                                              unsigned* __restrict__ tickets, int M, int N,
                                                              int K, int kper) {
     using S = typename Elem<IN>::storage;
@@ -67,6 +67,7 @@ __global__ __launch_bounds__(64 * NB * KW) void stream_kernel(const void* __rest
     constexpr int BN = 16 * NB;
     const S* __restrict__ X = static_cast<const S*>(Xv);
     const S* __restrict__ W = static_cast<const S*>(Wv);
+    void* __restrict__ Y = Yv;
 
     __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
     S* xs = reinterpret_cast<S*>(lds);
@@ -76,6 +77,12 @@ __global__ __launch_bounds__(64 * NB * KW) void stream_kernel(const void* __rest
     const int r = lane & 15, g = lane >> 4;
     const int tile = blockIdx.x, split = blockIdx.y;
     const int n0 = tile * BN;
+    // Grid z walks blocks of 16·ROWB rows of X (more than one only when M
+    // exceeds them, as for the 128-row layers); W is re-read per row block.
+    const int mb = blockIdx.z * G::XROWS;
+    X += (int64_t)mb * K;
+    Y = static_cast<char*>(Y) + (int64_t)mb * N * (OUT == TLG_F32 ? 4 : 2);
+    M = min(M - mb, G::XROWS);
     const S* Wrow = W + (int64_t)min(n0 + nb * 16 + r, N - 1) * K;
     const int kbeg = split * kper;
     const int kend = min(kbeg + kper, K);
@@ -173,8 +180,10 @@ __global__ __launch_bounds__(64 * NB * KW) void stream_kernel(const void* __rest
         // Partials in fragment order [split][tile][nb][rb][lane] (one
         // 16-byte store per lane); the reducing workgroup reads the same order.
         f32x4* frag = reinterpret_cast<f32x4*>(ws);
-        const int64_t per_split = (int64_t)gridDim.x * NB * ROWB * 64;
-        const int64_t base = ((int64_t)(tile * NB + nb) * ROWB) * 64 + lane;
+        const int64_t tiles = (int64_t)gridDim.x * gridDim.z;
+        const int64_t tid = (int64_t)blockIdx.z * gridDim.x + tile;  // ticket of this (row block, tile)
+        const int64_t per_split = tiles * NB * ROWB * 64;
+        const int64_t base = ((tid * NB + nb) * ROWB) * 64 + lane;
         if (kw == 0)
 #pragma unroll
             for (int rb = 0; rb < ROWB; ++rb) frag[split * per_split + base + rb * 64] = acc[rb];
@@ -184,7 +193,7 @@ __global__ __launch_bounds__(64 * NB * KW) void stream_kernel(const void* __rest
         __shared__ unsigned last;
         if (t == 0) {
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-            last = atomicAdd(&tickets[tile], 1u) == gridDim.y - 1;
+            last = atomicAdd(&tickets[tid], 1u) == gridDim.y - 1;
             if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         }
         __syncthreads();
@@ -209,7 +218,7 @@ __global__ __launch_bounds__(64 * NB * KW) void stream_kernel(const void* __rest
                 if (m < M && n < N) store_out<OUT>(Y, (int64_t)m * N + n, epilogue<EPI>(s4[e], b));
             }
         }
-        if (t == 0) __hip_atomic_store(&tickets[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (t == 0) __hip_atomic_store(&tickets[tid], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -219,9 +228,10 @@ static int launch_stream_cfg(const tlg_plan& p, const void* X, const void* W, co
     const int S = p.split;
     const int kper = (int)p.kper;
     const bool even = (int64_t)kper * S == p.K && kper % (KW * LOADS * 4 * Elem<I>::per16) == 0;
-    const dim3 grid((unsigned)p.grid_x, (unsigned)S), block(64 * NB * KW);
+    const dim3 grid((unsigned)p.grid_x, (unsigned)S, (unsigned)p.grid_z), block(64 * NB * KW);
     unsigned* tickets = static_cast<unsigned*>(ws);
-    float* part = ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + stream_ticket_bytes(p.grid_x)) : nullptr;
+    float* part =
+        ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + stream_ticket_bytes(p.grid_x * p.grid_z)) : nullptr;
     auto with_out = [&](auto f) {
         if constexpr (I == TLG_F32) return f(ic<TLG_F32>{});
         else if (p.out_dt == TLG_F32) return f(ic<TLG_F32>{});

@@ -241,15 +241,29 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
                                                            const void* __restrict__ bias,
                                                            void* __restrict__ Y, int64_t MN, int N) {
     const int64_t base = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (base >= MN) return;
+    // Every split's values in flight at once (in groups of 8), then the sum in split order.
+    float v[4][8];
+    float s[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int z0 = 0; z0 < splits; z0 += 8) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                v[e][q] = (z0 + q < splits && base + e < MN) ? ws[(int64_t)(z0 + q) * MN + base + e] : 0.0f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (z0 + q < splits) s[e] += v[e][q];
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int64_t idx = base + e;
         if (idx >= MN) return;
-        float s = 0.0f;
-        for (int z = 0; z < splits; ++z) s += ws[(int64_t)z * MN + idx];
         float b = 0.0f;
         if constexpr ((EPI & TLG_EPI_BIAS) != 0) b = load_elem<IN>(bias, idx % N);
-        store_out<OUT>(Y, idx, epilogue<EPI>(s, b));
+        store_out<OUT>(Y, idx, epilogue<EPI>(s[e], b));
     }
 }
 

@@ -92,11 +92,13 @@ static int fill_generic(tlg_plan& p) {
     return TLG_OK;
 }
 
-static int stream_rowb(int64_t M) { return M <= 16 ? 1 : M <= 32 ? 2 : 4; }
+// 16-row blocks of X per stream workgroup: all of M when it is at most 64,
+// otherwise 32-row blocks walked by grid z.
+static int stream_rowb(int64_t M) { return M <= 16 ? 1 : M <= 32 ? 2 : M <= kStreamMaxM ? 4 : 2; }
 
 static int fill_stream(tlg_plan& p, int tile, int split) {
-    if (p.M > kStreamMaxM) {
-        set_error("stream kernel handles M <= %d (got M=%lld)", kStreamMaxM, (long long)p.M);
+    if (p.M > kStreamMaxRows) {
+        set_error("stream kernel handles M <= %d (got M=%lld)", kStreamMaxRows, (long long)p.M);
         return TLG_ERR_UNSUPPORTED;
     }
     if (p.layout != TLG_NK) {
@@ -143,9 +145,10 @@ static int fill_stream(tlg_plan& p, int tile, int split) {
     p.threads = 64 * c.nb * c.kw;
     p.grid_x = tiles;
     p.grid_y = S;
-    p.grid_z = 1;
+    p.grid_z = ceil_div(p.M, 16 * rowb);
     p.launches = 1;
-    p.ws_bytes = S > 1 ? stream_ticket_bytes(tiles) + (size_t)S * tiles * bn * 16 * rowb * sizeof(float) : 0;
+    const int64_t slots = tiles * p.grid_z;  // (row block, tile) pairs, one ticket each
+    p.ws_bytes = S > 1 ? stream_ticket_bytes(slots) + (size_t)S * slots * bn * 16 * rowb * sizeof(float) : 0;
     return TLG_OK;
 }
 
@@ -155,7 +158,7 @@ static int fill_stream(tlg_plan& p, int tile, int split) {
 // otherwise 128-row tiles split K across workgroups.
 static int auto_stream(tlg_plan& p) {
     const int rowb = stream_rowb(p.M);
-    if (ceil_div(p.N, 16) >= kNumCUs / 2) {
+    if (ceil_div(p.N, 16) * ceil_div(p.M, 16 * rowb) >= kNumCUs / 2) {
         for (int cfg : {0, 1, 4})
             if (stream_lds_bytes(kStream[cfg], p.in_dt, rowb) <= kLdsBytes) return fill_stream(p, cfg, 1);
     }
@@ -205,6 +208,12 @@ static int fill_tiled(tlg_plan& p, int tile, int split) {
 static int auto_plan(tlg_plan& p) {
     if (!rows_aligned16(p)) return fill_generic(p);
     if (p.layout == TLG_NK && p.M <= kStreamMaxM) return auto_stream(p);
+    // Up to a few hundred rows with few output columns the stream kernel's
+    // grid (16-column tiles × 32-row blocks) still fits one workgroup per CU:
+    // latency-bound shapes with no LDS pipeline to fill.  Wider outputs make
+    // every tile re-read X, and the tiled kernel with split-K wins.
+    if (p.layout == TLG_NK && p.M <= kStreamMaxRows && ceil_div(p.N, 16) * ceil_div(p.M, 32) <= kNumCUs)
+        return auto_stream(p);
     const int big = 0, small = 1;
     const TileCfg& cb = tiled_cfg(p.in_dt, big);
     const int64_t tiles_big = ceil_div(p.M, cb.bm) * ceil_div(p.N, cb.bn);
@@ -295,8 +304,8 @@ int gemm_plan_ex(tlg_plan_t* out, int64_t M, int64_t N, int64_t K, tlg_dtype in_
         rc = fill_generic(p);
     } else if (variant == TLG_VARIANT_STREAM) {
         if (tile_sel == 0 && split == 0)
-            rc = p.M <= kStreamMaxM && p.layout == TLG_NK && rows_aligned16(p) ? auto_stream(p)
-                                                                              : fill_stream(p, 0, 0);
+            rc = p.M <= kStreamMaxRows && p.layout == TLG_NK && rows_aligned16(p) ? auto_stream(p)
+                                                                                : fill_stream(p, 0, 0);
         else
             rc = fill_stream(p, tile_sel ? tile_sel - 1 : 2, split);
     } else if (variant == TLG_VARIANT_TILED) {

@@ -57,7 +57,8 @@ constexpr StreamCfg kStream[] = {
     {2, 4, 4},   // 4: 32-row tiles, 4-way in-workgroup split
 };
 constexpr int kNumStream = sizeof(kStream) / sizeof(kStream[0]);
-constexpr int kStreamMaxM = 64;      // 4 row blocks of 16
+constexpr int kStreamMaxM = 64;      // rows of X one stream workgroup covers (4 blocks of 16)
+constexpr int kStreamMaxRows = 256;  // beyond this the tiled kernel always wins (W re-read per row block)
 constexpr int kStreamMaxSplit = 16;  // K splits summed by the last workgroup of a tile
 constexpr int kLdsBytes = 160 * 1024;
 

@@ -66,12 +66,24 @@ def test_square_fp32_goes_to_tiled():
 
 
 @pytest.mark.parametrize("N,K", [(2304, 768), (768, 768), (3072, 768), (768, 3072)])
-def test_gpt2_layer_shapes_fill_the_chip(N, K):
+def test_gpt2_layer_shapes_m128(N, K):
+    """128-row layers: 768 outputs fit one stream grid (16-column tiles × 32-row
+    blocks, all of K per workgroup); wider layers take the tiled kernel with split-K."""
     i = _plan(128, N, K, "f32", bias=True).info
-    assert i.variant == t.VARIANT_TILED
-    tiles = -(-128 // i.tile_m) * -(-N // i.tile_n)
-    assert tiles * i.split_k >= 256 or K // (i.tile_k * i.split_k) < 8
-    assert i.workspace_bytes == (i.split_k * 128 * N * 4 if i.split_k > 1 else 0)
+    if N == 768:
+        assert i.variant == t.VARIANT_STREAM and (i.tile_m, i.tile_n) == (32, 16)
+        assert i.workgroups == (N // 16) * 4 and i.split_k == 1 and i.workspace_bytes == 0
+    else:
+        assert i.variant == t.VARIANT_TILED and i.split_k > 1
+        tiles = -(-128 // i.tile_m) * -(-N // i.tile_n)
+        assert tiles * i.split_k >= 256 or K // (i.tile_k * i.split_k) < 8
+        assert i.workspace_bytes == i.split_k * 128 * N * 4
+
+
+def test_large_m_goes_to_tiled():
+    for N, K in [(2304, 768), (768, 768), (3072, 768), (768, 3072)]:
+        i = _plan(8192, N, K, "bf16", bias=True).info
+        assert i.variant == t.VARIANT_TILED and i.split_k == 1
 
 
 def test_misaligned_rows_go_to_generic():
@@ -84,8 +96,9 @@ def test_forced_variants_and_errors():
     p = _plan(100, 64, 64, "bf16", variant=t.VARIANT_GENERIC)
     assert p.info.variant == t.VARIANT_GENERIC
     with pytest.raises(t.TlgError) as e:
-        _plan(100, 64, 64, "bf16", variant=t.VARIANT_STREAM)
+        _plan(300, 64, 64, "bf16", variant=t.VARIANT_STREAM)  # more rows than the stream kernel walks
     assert e.value.status == t.ERR_UNSUPPORTED
+    assert _plan(100, 64, 64, "bf16", variant=t.VARIANT_STREAM).info.variant == t.VARIANT_STREAM
     with pytest.raises(t.TlgError) as e:
         _plan(10, 64, 64, "f32", layout="KN", variant=t.VARIANT_STREAM)
     assert e.value.status == t.ERR_UNSUPPORTED

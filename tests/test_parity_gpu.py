@@ -55,7 +55,7 @@ def test_generic(pair, layout, epi):
 def test_stream(pair, epi, tile):
     ran = 0
     for M, N, K in [(1, 16, 8), (16, 48, 512), (5, 50, 520), (17, 36, 1032), (40, 100, 264), (64, 16, 4096),
-                    (3, 300, 3000)]:
+                    (3, 300, 3000), (100, 40, 264), (130, 36, 520)]:
         c = _case(2, M, N, K, pair, "NK", epi)
         try:
             _, desc = _check(c, variant=tlgemm.VARIANT_STREAM, tile=tile)
@@ -71,7 +71,7 @@ def test_stream(pair, epi, tile):
 @pytest.mark.parametrize("split", [1, 2, 3, 7])
 def test_stream_forced_split(pair, split):
     """Cross-workgroup split-K with the last-arriving reduction, ragged K and N tails."""
-    for M, N, K in [(16, 260, 3000), (33, 520, 2048), (64, 132, 4104)]:
+    for M, N, K in [(16, 260, 3000), (33, 520, 2048), (64, 132, 4104), (130, 100, 2056)]:
         c = _case(5, M, N, K, pair, "NK", (True, True))
         ck = 512 if pair[0] != "f32" else 256
         if split > -(-K // ck):  # more splits than K chunks: refused by the planner
