@@ -281,7 +281,7 @@ int launch_stream_in(const tlg_plan& p, const void* X, const void* W, const void
         TLG_STREAM_CASE(2)
         TLG_STREAM_CASE(3)
         TLG_STREAM_CASE(4)
-    default: set_error("bad stream tile"); return TLG_ERR_INVALID_ARG;
+    default: set_error("bad stream tile"); return (int)TLG_ERR_INVALID_ARG;
     }
 #undef TLG_STREAM_CASE
 }

@@ -8,9 +8,9 @@
 //  * A workgroup computes a BM×BN tile with WM×WN waves; each wave owns a
 //    (BM/WM)×(BN/WN) block of 32×32 MFMA accumulators (fp32:
 //    v_mfma_f32_32x32x2_f32; fp16/bf16: v_mfma_f32_32x32x16_*).
-//  * K advances in slices of BK (64 bytes of each operand row).  The next
-//    slice is loaded with 16-byte global loads into registers while the
-//    current slice is multiplied from LDS; two LDS buffers, one barrier per
+//  * K advances in slices of BK (64 to 256 bytes of each operand row),
+//    fetched with 16-byte global loads into registers two slices ahead of
+//    the one being multiplied from LDS; two LDS buffers, one barrier per
 //    slice.
 //  * LDS rows are k-contiguous with a 16-byte pad (stride 80 B), so the
 //    16-byte operand reads of 16 consecutive rows hit 64 distinct banks.
@@ -45,7 +45,7 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_kernel(const void* __restr
     constexpr int THREADS = 64 * WM * WN;
     constexpr int EPV = Elem<IN>::per16;  // elements per 16 bytes
     constexpr int VPR = BK / EPV;         // 16-byte vectors per tile row
-    static_assert(BK * (int)sizeof(S) == 64, "one slice is 64 bytes of each operand row");
+    static_assert(BK * (int)sizeof(S) % 64 == 0, "a slice is a multiple of 64 bytes of each operand row");
     constexpr int LDA = BK + EPV;         // padded LDS row (elements)
     constexpr bool B_NMAJOR = (LAYOUT == TLG_KN) && F32;  // fp32 [K][N] stays n-contiguous
     constexpr int LDBN = BN + 8;                         // its padded row (floats)
@@ -53,7 +53,12 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_kernel(const void* __restr
     constexpr int TM = WTM / 32, TN = WTN / 32;
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile is a multiple of 32×32");
     constexpr int AV = BM * VPR / THREADS;
-    constexpr int BV = (LAYOUT == TLG_NK) ? BN * VPR / THREADS : BK * (BN / EPV) / THREADS;
+    // A 16-bit [K][N] operand is moved as 8×8 blocks (8 rows of k, 8 columns
+    // of n), transposed in registers so LDS receives 16-byte runs of k.
+    constexpr bool B_T16 = (LAYOUT == TLG_KN) && !F32;
+    constexpr int NBK = BK / 8, TBLK = (BK / 8) * (BN / 8);
+    constexpr int BPT = (TBLK + THREADS - 1) / THREADS;  // 8×8 blocks per thread
+    constexpr int BV = B_T16 ? 8 * BPT : (LAYOUT == TLG_NK) ? BN * VPR / THREADS : BK * (BN / EPV) / THREADS;
     static_assert(AV * THREADS == BM * VPR && BV >= 1, "tile loads divide evenly over the threads");
     constexpr int A_ELEMS = BM * LDA;
     constexpr int B_ELEMS = B_NMAJOR ? BK * LDBN : BN * LDA;
@@ -84,8 +89,7 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_kernel(const void* __restr
     const int kend = min(kbeg + kper, K);
     const int nslices = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
 
-    u32x4 ra[AV], rbv[BV];
-    auto gload = [&](int s) {
+    auto gload = [&](int s, u32x4 (&ra)[AV], u32x4 (&rbv)[BV]) {
         const int k0 = kbeg + s * BK;
 #pragma unroll
         for (int i = 0; i < AV; ++i) {
@@ -107,6 +111,16 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_kernel(const void* __restr
                     rbv[i] = ldg16(W + (int64_t)n * K + k);
                 else
                     rbv[i] = u32x4{0u, 0u, 0u, 0u};
+            } else if constexpr (B_T16) {
+                // block q = t + THREADS*(i/8), row i%8 of it: k = kc*8 + i%8, n = nb*8..+7
+                const int q = t + THREADS * (i / 8);
+                const int kc = q % NBK, nb = q / NBK;
+                const int k = k0 + kc * 8 + (i % 8);
+                const int n = EVEN ? n0 + nb * 8 : min(n0 + nb * 8, N - 8);
+                if ((TBLK % THREADS == 0 || q < TBLK) && (EVEN || k < kend))
+                    rbv[i] = ldg16(W + (int64_t)k * N + n);
+                else
+                    rbv[i] = u32x4{0u, 0u, 0u, 0u};
             } else {
                 constexpr int NV = BN / EPV;
                 const int kr = v / NV, nv = v % NV;
@@ -119,7 +133,7 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_kernel(const void* __restr
             }
         }
     };
-    auto lstore = [&](int buf) {
+    auto lstore = [&](int buf, const u32x4 (&ra)[AV], const u32x4 (&rbv)[BV]) {
         S* As = lds[buf];
         S* Bs = lds[buf] + A_ELEMS;
 #pragma unroll
@@ -136,11 +150,24 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_kernel(const void* __restr
                 constexpr int NV = BN / EPV;
                 *reinterpret_cast<u32x4*>(Bs + (v / NV) * LDBN + (v % NV) * EPV) = rbv[i];
             } else {
-                constexpr int NV = BN / EPV;
-                const int kr = v / NV, nb = (v % NV) * EPV;
+                // Transpose one 8×8 block: column c gathers half c of rows
+                // 0..7, packed two rows per dword (v_perm), then one 16-byte
+                // store per column.  Eight consecutive lanes write one row's
+                // eight 16-byte runs; the next eight lanes write a row 8 below
+                // (288 dwords on: the other 32 banks), so stores are conflict-free.
+                if (i % 8 != 0) continue;
+                const int q = t + THREADS * (i / 8);
+                if (TBLK % THREADS != 0 && q >= TBLK) continue;
+                const int kc = q % NBK, nb = q / NBK;
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    Bs[(nb + e) * LDA + kr] = (S)((rbv[i][e >> 1] >> (16 * (e & 1))) & 0xffffu);
+                for (int c = 0; c < 8; ++c) {
+                    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+                    u32x4 col;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        col[j] = __builtin_amdgcn_perm(rbv[i + 2 * j + 1][c >> 1], rbv[i + 2 * j][c >> 1], sel);
+                    *reinterpret_cast<u32x4*>(Bs + (nb * 8 + c) * LDA + kc * 8) = col;
+                }
             }
         }
     };
@@ -182,33 +209,95 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_kernel(const void* __restr
                         for (int j = 0; j < TN; ++j) acc[i][j] = mfma32_f32(a[i][e], b[j][e], acc[i][j]);
             }
         } else {
-#pragma unroll
-            for (int kq = 0; kq < BK / 16; ++kq) {
-                u32x4 a[TM], b[TN];
+            // Operand fragments for k-step kq+1 are read from LDS before the
+            // MFMAs of k-step kq issue, so LDS latency overlaps the math.
+            constexpr int KQ = BK / 16;
+            u32x4 a[2][TM], b[2][TN];
+            auto frag = [&](int kq, u32x4(&fa)[TM], u32x4(&fb)[TN]) {
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
-                    a[i] = *reinterpret_cast<const u32x4*>(As + (wm0 + i * 32 + r) * LDA + kq * 16 + 8 * g);
+                    fa[i] = *reinterpret_cast<const u32x4*>(As + (wm0 + i * 32 + r) * LDA + kq * 16 + 8 * g);
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
-                    b[j] = *reinterpret_cast<const u32x4*>(Bs + (wn0 + j * 32 + r) * LDA + kq * 16 + 8 * g);
+                    fb[j] = *reinterpret_cast<const u32x4*>(Bs + (wn0 + j * 32 + r) * LDA + kq * 16 + 8 * g);
+            };
+            frag(0, a[0], b[0]);
+#pragma unroll
+            for (int kq = 0; kq < KQ; ++kq) {
+                if (kq + 1 < KQ) frag(kq + 1, a[(kq + 1) & 1], b[(kq + 1) & 1]);
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
 #pragma unroll
-                    for (int j = 0; j < TN; ++j) acc[i][j] = mfma32_16bit<IN>(a[i], b[j], acc[i][j]);
+                    for (int j = 0; j < TN; ++j)
+                        acc[i][j] = mfma32_16bit<IN>(a[kq & 1][i], b[kq & 1][j], acc[i][j]);
             }
+            // Ask the scheduler for an interleaved issue order: the first
+            // k-step's reads, then one LDS read between MFMAs, the rest MFMAs.
+            constexpr int NR = KQ * (TM + TN), NM = KQ * TM * TN, NI = NR - (TM + TN);
+            constexpr int PER = NM / (NI > 0 ? NI : 1);
+            __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);
+#pragma unroll
+            for (int q = 0; q < NI; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, NM - NI * PER, 0);
         }
     };
 
+    // Two slices of loads in flight: while slice s is multiplied from one LDS
+    // buffer, slice s+1 waits in registers for the other buffer and slice s+2
+    // is being fetched.  The loop is unrolled by two so each register set is
+    // named statically.  Buffer b is rewritten only after the barrier that
+    // follows its last read.
+    // Every compute and load in the loop is unconditional, which keeps the
+    // accumulators in place across iterations and lets each wait cover only
+    // the slice about to be stored.
     if (nslices > 0) {
-        gload(0);
-        lstore(0);
+        u32x4 ra0[AV], rb0[BV], ra1[AV], rb1[BV];
+        gload(0, ra0, rb0);
+        if (nslices > 1) gload(1, ra1, rb1);
+        lstore(0, ra0, rb0);
         __syncthreads();
-        for (int s = 0; s < nslices; ++s) {
-            const int cur = s & 1;
-            if (s + 1 < nslices) gload(s + 1);
-            compute(cur);
-            if (s + 1 < nslices) lstore(cur ^ 1);
+        // Steady state: pairs whose two prefetches are in range, so the loads
+        // are unconditional and the wait before each LDS store covers only
+        // the older slice.
+        // Scheduling barriers pin the phase order (the compiler would sink the
+        // prefetch below the store, shortening its lead and forcing a full
+        // wait); inside compute() LDS reads and MFMAs still interleave freely.
+        int s = 0;
+        for (; s + 3 < nslices; s += 2) {
+            gload(s + 2, ra0, rb0);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(0);
+            __builtin_amdgcn_sched_barrier(0);
+            lstore(1, ra1, rb1);  // slice s+1
             __syncthreads();
+            gload(s + 3, ra1, rb1);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(1);
+            __builtin_amdgcn_sched_barrier(0);
+            lstore(0, ra0, rb0);  // slice s+2
+            __syncthreads();
+        }
+        // Tail: slice s is in buffer 0, slice s+1 (if any) in ra1.
+        const int rem = nslices - s;  // 1, 2 or 3
+        if (rem == 3) {
+            gload(s + 2, ra0, rb0);
+            compute(0);
+            lstore(1, ra1, rb1);
+            __syncthreads();
+            compute(1);
+            lstore(0, ra0, rb0);
+            __syncthreads();
+            compute(0);
+        } else if (rem == 2) {
+            compute(0);
+            lstore(1, ra1, rb1);
+            __syncthreads();
+            compute(1);
+        } else {
+            compute(0);
         }
     }
 
@@ -279,9 +368,14 @@ static int launch_tiled_cfg(const tlg_plan& p, const void* X, const void* W, con
                            grid, block, 0, stream, X, W, bias, Y, ws, (int)p.M, (int)p.N, (int)p.K, kper);
         return check_launch("tiled_kernel");
     };
+    auto go_split = [&](auto ev) {
+        hipLaunchKernelGGL((tiled_kernel<I, TLG_F32, L, 0u, BM, BN, BK, WM, WN, decltype(ev)::value, true>), grid,
+                           block, 0, stream, X, W, nullptr, nullptr, ws, (int)p.M, (int)p.N, (int)p.K, kper);
+        return check_launch("tiled_kernel");
+    };
     int rc;
-    if (S > 1)
-        rc = even ? go(std::true_type{}, std::true_type{}) : go(std::false_type{}, std::true_type{});
+    if (S > 1)  // partials carry no epilogue: the reducer applies it
+        rc = even ? go_split(std::true_type{}) : go_split(std::false_type{});
     else
         rc = even ? go(std::true_type{}, std::false_type{}) : go(std::false_type{}, std::false_type{});
     if (rc != TLG_OK || S == 1) return rc;
@@ -309,13 +403,21 @@ int launch_tiled_in(const tlg_plan& p, const void* X, const void* W, const void*
                 constexpr int O = decltype(out)::value, L = decltype(lay)::value;
                 constexpr uint32_t E = (uint32_t)decltype(epi)::value;
                 constexpr const TileCfg* T = I == TLG_F32 ? kTiledF32 : kTiled16;
-                static_assert(kNumTiledF32 == 3 && kNumTiled16 == 3, "tile lists changed");
-                constexpr TileCfg c0 = T[0], c1 = T[1], c2 = T[2];
+                static_assert(kNumTiledF32 == 5 && kNumTiled16 == 5, "tile lists changed");
+#define TLG_TILED_CASE(i)                                                                                 \
+    case i: {                                                                                             \
+        constexpr TileCfg c = T[i];                                                                       \
+        return launch_tiled_cfg<I, O, L, E, c.bm, c.bn, c.bk, c.wm, c.wn>(p, X, W, bias, Y, wsf, stream); \
+    }
                 switch (p.tile) {
-                case 0: return launch_tiled_cfg<I, O, L, E, c0.bm, c0.bn, c0.bk, c0.wm, c0.wn>(p, X, W, bias, Y, wsf, stream);
-                case 1: return launch_tiled_cfg<I, O, L, E, c1.bm, c1.bn, c1.bk, c1.wm, c1.wn>(p, X, W, bias, Y, wsf, stream);
-                default: return launch_tiled_cfg<I, O, L, E, c2.bm, c2.bn, c2.bk, c2.wm, c2.wn>(p, X, W, bias, Y, wsf, stream);
+                    TLG_TILED_CASE(0)
+                    TLG_TILED_CASE(1)
+                    TLG_TILED_CASE(2)
+                    TLG_TILED_CASE(3)
+                    TLG_TILED_CASE(4)
+                default: set_error("bad tiled tile"); return (int)TLG_ERR_INVALID_ARG;
                 }
+#undef TLG_TILED_CASE
             });
         });
     });

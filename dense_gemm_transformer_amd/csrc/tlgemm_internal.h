@@ -28,14 +28,20 @@ struct TileCfg {
 // fp32 operands: v_mfma_f32_32x32x2_f32, wave tile (bm/wm)×(bn/wn).
 constexpr TileCfg kTiledF32[] = {
     {128, 128, 16, 2, 2},  // 0: square and wide shapes
-    {64, 64, 16, 2, 2},    // 1: narrow grids (M = 128 layers), pairs with split-K
-    {256, 128, 16, 4, 2},  // 2: large M
+    {64, 64, 16, 2, 2},    // 1: narrow grids, pairs with split-K
+    {256, 128, 16, 2, 2},  // 2: 128×64 wave tiles
+    {128, 128, 32, 2, 2},  // 3: deeper K slice
+    {256, 256, 16, 2, 2},  // 4: 128×128 wave tiles
 };
-// 16-bit operands: v_mfma_f32_32x32x16_{f16,bf16}.
+// 16-bit operands: v_mfma_f32_32x32x16_{f16,bf16}.  A slice of 32 elements
+// is only 256 MFMA cycles per wave, too short to hide one slice of load
+// latency, so the default slice is 64 or 128 elements deep.
 constexpr TileCfg kTiled16[] = {
-    {128, 128, 32, 2, 2},
-    {64, 64, 32, 2, 2},
-    {256, 128, 32, 4, 2},
+    {128, 128, 64, 2, 2},   // 0
+    {64, 64, 64, 2, 2},     // 1: narrow grids, pairs with split-K
+    {256, 128, 64, 2, 2},   // 2
+    {128, 128, 128, 2, 2},  // 3
+    {256, 256, 64, 2, 2},   // 4
 };
 constexpr int kNumTiledF32 = sizeof(kTiledF32) / sizeof(kTiledF32[0]);
 constexpr int kNumTiled16 = sizeof(kTiled16) / sizeof(kTiled16[0]);
