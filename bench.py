@@ -254,7 +254,7 @@ def main(argv=None) -> int:
                      "frac": round(sq_tflops / PEAK_F32_TFLOPS, 4), "traffic": measured_traffic("tiled_f32"),
                      "traffic_unit": "bytes per launch (L2<->memory, rocprofv3 FETCH_SIZE+WRITE_SIZE)",
                      "algorithmic_bytes_per_launch": 3 * sq.M * sq.N * 4,
-                     "kernel": "tiled_kernel (fp32, 128x128x16)",
+                     "kernel": f"tiled_kernel fp32 {plan.info.tile_m}x{plan.info.tile_n}x{plan.info.tile_k}",
                      "algorithmic_flops_per_launch": sq.flops},
         "cpu_baseline": cpu,
         "parity": {"square_f32_err": sq_err, "square_f32_pass": None if sq_err is None else sq_err <= tol32,
@@ -271,7 +271,8 @@ def main(argv=None) -> int:
                         "roofline": {"bound": "hbm", "achieved": round(n_gbs, 1), "peak": PEAK_HBM_GBS,
                                      "unit": "GB/s", "frac": round(n_gbs / PEAK_HBM_GBS, 4),
                                      "traffic": measured_traffic("stream_f16"),
-                                     "kernel": "stream_kernel (fp16, 128-row tiles x 8 K-splits)",
+                                     "kernel": f"stream_kernel fp16 {nplan.info.tile_m}x{nplan.info.tile_n}, "
+                                               f"{nplan.info.threads // 64} waves over K",
                                      "algorithmic_bytes_per_launch": n_bytes},
                         "timing": "HIP events over back-to-back launches (includes launch gaps)",
                         "plan": nplan.describe()},

@@ -61,15 +61,27 @@ def test_stream_split_rules():
 def test_square_fp32_goes_to_tiled():
     p = _plan(4096, 4096, 4096, "f32", "f32", "KN")
     i = p.info
-    assert i.variant == t.VARIANT_TILED and (i.tile_m, i.tile_n) == (128, 128)
-    assert i.workgroups == 1024 and i.split_k == 1 and i.workspace_bytes == 0
+    assert i.variant == t.VARIANT_TILED and (i.tile_m, i.tile_n) == (256, 256)  # measured table row
+    assert i.workgroups == 256 and i.split_k == 1 and i.workspace_bytes == 0
+    # an unlisted square shape falls back to the fill rule's 128×128 tiles
+    i = _plan(2048, 2048, 2048, "f32", "f32", "KN").info
+    assert (i.tile_m, i.tile_n, i.workgroups) == (128, 128, 256)
+
+
+def test_dispatch_table_rows_are_exact_shape_matches():
+    # the table lists the 128x768x768 fp32 layer with bias; without bias the fill rule applies
+    with_bias = _plan(128, 768, 768, "f32", bias=True).describe()
+    assert "variant=stream" in with_bias
+    assert _plan(128, 2304, 768, "f32", bias=True).info.tile_n == 32  # measured: 32-column stream tiles
+    assert _plan(128, 2304, 768, "f32").info.variant == t.VARIANT_TILED  # no table row without bias
 
 
 @pytest.mark.parametrize("N,K", [(2304, 768), (768, 768), (3072, 768), (768, 3072)])
 def test_gpt2_layer_shapes_m128(N, K):
-    """128-row layers: 768 outputs fit one stream grid (16-column tiles × 32-row
-    blocks, all of K per workgroup); wider layers take the tiled kernel with split-K."""
-    i = _plan(128, N, K, "f32", bias=True).info
+    """Without a table row (no bias): 768 outputs fit one stream grid (16-column
+    tiles × 32-row blocks, all of K per workgroup); wider layers take the tiled
+    kernel with split-K.  With bias the measured rows all pick stream plans."""
+    i = _plan(128, N, K, "f32").info
     if N == 768:
         assert i.variant == t.VARIANT_STREAM and (i.tile_m, i.tile_n) == (32, 16)
         assert i.workgroups == (N // 16) * 4 and i.split_k == 1 and i.workspace_bytes == 0
@@ -78,6 +90,8 @@ def test_gpt2_layer_shapes_m128(N, K):
         tiles = -(-128 // i.tile_m) * -(-N // i.tile_n)
         assert tiles * i.split_k >= 256 or K // (i.tile_k * i.split_k) < 8
         assert i.workspace_bytes == i.split_k * 128 * N * 4
+    j = _plan(128, N, K, "f32", bias=True, gelu=(N == 3072)).info
+    assert j.variant == t.VARIANT_STREAM and j.workspace_bytes == 0
 
 
 def test_large_m_goes_to_tiled():
