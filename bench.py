@@ -44,19 +44,19 @@ METRIC = "TFLOP/s (% MFMA peak) @4096³ fp32; µs + HBM GB/s @16×4096×4096 fp1
 # --narrow-launches 32 --no-cpu-baseline --no-parity` (profiles/hbm_traffic_mi355x.md).
 # FETCH_SIZE is scaled by 1.998 and WRITE_SIZE by 1.0: the factors that make
 # the same counters read 32 MiB for a 32 MiB device-to-device copy.  Each
-# entry holds the hash of the kernel sources it was taken on; after any change
-# to them the figure no longer applies and the bench reports null.
+# entry holds the hash of the kernel sources and the tile it was taken on;
+# after a change to either the figure no longer applies and the bench reports null.
 FETCH_SCALE, WRITE_SCALE = 1.998, 1.0
 TRAFFIC = {
-    "tiled_f32": {"sources": ("common.h", "tiled.h"), "sha": "1811ab1945c5e821",
-                  "fetch_kib": 208729.8, "write_kib": 90368.0},
-    "stream_f16": {"sources": ("common.h", "stream.h"), "sha": "6061837eb9e47d14",
-                   "fetch_kib": 16927.5, "write_kib": 128.0},
+    "tiled_f32": {"sources": ("common.h", "tiled.h"), "sha": "fdee2f0433c1b7c2",
+                  "tile": "128x128x16", "fetch_kib": 391738.5, "write_kib": 65536.0},
+    "stream_f16": {"sources": ("common.h", "stream.h"), "sha": "559ea57f1276632e",
+                   "tile": "16x16x4096", "fetch_kib": 16927.5, "write_kib": 128.0},
 }
 
 
-def measured_traffic(key: str):
-    """HBM bytes per launch for a kernel, or None if its sources changed since the counters were taken."""
+def measured_traffic(key: str, tile: str):
+    """HBM bytes per launch for a kernel, or None if its sources or tile changed since the counters were taken."""
     import hashlib
 
     rec = TRAFFIC[key]
@@ -64,9 +64,14 @@ def measured_traffic(key: str):
     for name in rec["sources"]:
         with open(os.path.join(ROOT, "dense_gemm_transformer_amd", "csrc", "kernels", name), "rb") as f:
             h.update(f.read())
-    if h.hexdigest()[:16] != rec["sha"]:
+    if h.hexdigest()[:16] != rec["sha"] or tile != rec["tile"]:
         return None
     return int((rec["fetch_kib"] * FETCH_SCALE + rec["write_kib"] * WRITE_SCALE) * 1024)
+def tile_str(plan) -> str:
+    i = plan.info
+    return f"{i.tile_m}x{i.tile_n}x{i.tile_k}"
+
+
 PEAK_F32_TFLOPS = 157.3      # MI355X dense fp32 matrix
 PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16/fp16 matrix
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
@@ -251,7 +256,8 @@ def main(argv=None) -> int:
         "config": {"workload": "fp32 GEMM C=A.B, M=N=K=4096, row-major A[M][K] and B[K][N], U(-1,1), warm",
                    "M": sq.M, "N": sq.N, "K": sq.K, "layout": "KN", "plan": plan.describe()},
         "roofline": {"bound": "mfma", "achieved": round(sq_tflops, 3), "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(sq_tflops / PEAK_F32_TFLOPS, 4), "traffic": measured_traffic("tiled_f32"),
+                     "frac": round(sq_tflops / PEAK_F32_TFLOPS, 4),
+                     "traffic": measured_traffic("tiled_f32", tile_str(plan)),
                      "traffic_unit": "bytes per launch (L2<->memory, rocprofv3 FETCH_SIZE+WRITE_SIZE)",
                      "algorithmic_bytes_per_launch": 3 * sq.M * sq.N * 4,
                      "kernel": f"tiled_kernel fp32 {plan.info.tile_m}x{plan.info.tile_n}x{plan.info.tile_k}",
@@ -270,7 +276,7 @@ def main(argv=None) -> int:
                         "GB/s": round(n_gbs, 1),
                         "roofline": {"bound": "hbm", "achieved": round(n_gbs, 1), "peak": PEAK_HBM_GBS,
                                      "unit": "GB/s", "frac": round(n_gbs / PEAK_HBM_GBS, 4),
-                                     "traffic": measured_traffic("stream_f16"),
+                                     "traffic": measured_traffic("stream_f16", tile_str(nplan)),
                                      "kernel": f"stream_kernel fp16 {nplan.info.tile_m}x{nplan.info.tile_n}, "
                                                f"{nplan.info.threads // 64} waves over K",
                                      "algorithmic_bytes_per_launch": n_bytes},

@@ -76,6 +76,26 @@ template <uint32_t EPI> __device__ inline float epilogue(float acc, float b) {
 // ---- 16-byte global loads --------------------------------------------------------
 __device__ inline u32x4 ldg16(const void* p) { return *static_cast<const u32x4*>(p); }
 
+// Raw buffer loads: a uniform 128-bit descriptor (base, byte count) in scalar
+// registers, a per-lane 32-bit byte offset and a uniform 32-bit offset.  A
+// kernel that issues many loads from one operand then holds one vector
+// register of address instead of a 64-bit address per load.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ u32x4 buffer_load16(i32x4 rsrc, uint32_t voffset, int soffset, int aux) __asm(
+    "llvm.amdgcn.raw.buffer.load.v4i32");
+// Descriptor for the bytes [p, p + bytes), bytes < 2^31: every field is read
+// from the first lane (the arguments are uniform by construction, and this
+// keeps the descriptor in scalar registers), stride 0, 32-bit data format.
+__device__ inline i32x4 buffer_rsrc(const void* p, int64_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    r[3] = 0x00020000;
+    return r;
+}
+
 // ---- MFMA wrappers -----------------------------------------------------------------
 // 16x16 output block, fp32 accumulate.
 __device__ inline f32x4 mfma16_f32(float a, float b, f32x4 c) {

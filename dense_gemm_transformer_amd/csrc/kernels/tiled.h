@@ -9,9 +9,13 @@
 //    (BM/WM)×(BN/WN) block of 32×32 MFMA accumulators (fp32:
 //    v_mfma_f32_32x32x2_f32; fp16/bf16: v_mfma_f32_32x32x16_*).
 //  * K advances in slices of BK (64 to 256 bytes of each operand row),
-//    fetched with 16-byte global loads into registers two slices ahead of
-//    the one being multiplied from LDS; two LDS buffers, one barrier per
-//    slice.
+//    fetched with 16-byte loads into registers two slices ahead of the one
+//    being multiplied from LDS; two LDS buffers, one barrier per slice.
+//    With one wave per SIMD nothing else hides the issue time of those
+//    loads and of the LDS stores, so both are spread between the MFMAs of
+//    the current slice (scheduling group barriers), and exact-fit tiles load
+//    through buffer descriptors: one lane offset per operand instead of a
+//    64-bit address per load, which keeps the loop free of register spills.
 //  * LDS rows are k-contiguous with a 16-byte pad (stride 80 B), so the
 //    16-byte operand reads of 16 consecutive rows hit 64 distinct banks.
 //    A row-major [K][N] fp32 operand stays n-contiguous (stride BN+8 floats,
@@ -63,7 +67,14 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_kernel(const void* __restr
     constexpr int A_ELEMS = BM * LDA;
     constexpr int B_ELEMS = B_NMAJOR ? BK * LDBN : BN * LDA;
 
-    __shared__ __attribute__((aligned(16))) S lds[2][A_ELEMS + B_ELEMS];
+    // Four LDS arrays (A and B operand, two buffers each): separate objects,
+    // so the compiler sees that stores into one buffer never alias operand
+    // reads from the other, and every access lies within 64 KiB of its
+    // operand's base (the reach of the DS offset field).
+    __shared__ __attribute__((aligned(16))) S lds_a0[A_ELEMS];
+    __shared__ __attribute__((aligned(16))) S lds_a1[A_ELEMS];
+    __shared__ __attribute__((aligned(16))) S lds_b0[B_ELEMS];
+    __shared__ __attribute__((aligned(16))) S lds_b1[B_ELEMS];
 
     const S* __restrict__ X = static_cast<const S*>(Xv);
     const S* __restrict__ W = static_cast<const S*>(Wv);
@@ -89,8 +100,40 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_kernel(const void* __restr
     const int kend = min(kbeg + kper, K);
     const int nslices = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
 
+    // EVEN (exact-fit tiles, every operand region below 2 GiB, checked by the
+    // host) loads through buffer descriptors: a uniform base per operand tile
+    // plus one 32-bit lane offset, the per-load offsets uniform.
+    constexpr int NV = BN / EPV;
+    constexpr int ES = (int)sizeof(S);
+    static_assert(THREADS % VPR == 0 && (!B_T16 || THREADS % NBK == 0) && (!B_NMAJOR || THREADS % NV == 0),
+                  "each thread's loads share one lane offset");
+    const uint32_t a_lane = (uint32_t)(((t / VPR) * K + (t % VPR) * EPV) * ES);
+    const uint32_t b_lane = LAYOUT == TLG_NK ? (uint32_t)(((t / VPR) * K + (t % VPR) * EPV) * ES)
+                            : B_T16        ? (uint32_t)(((t % NBK) * 8 * N + (t / NBK) * 8) * ES)
+                                           : (uint32_t)(((t / NV) * N + (t % NV) * EPV) * ES);
+    i32x4 rsrc_a = {0, 0, 0, 0}, rsrc_b = {0, 0, 0, 0};
+    if constexpr (EVEN) {
+        rsrc_a = buffer_rsrc(X + (int64_t)m0 * K, (int64_t)BM * K * ES);
+        rsrc_b = LAYOUT == TLG_NK ? buffer_rsrc(W + (int64_t)n0 * K, (int64_t)BN * K * ES)
+                                  : buffer_rsrc(W + n0, ((int64_t)K * N - n0) * ES);
+    }
     auto gload = [&](int s, u32x4 (&ra)[AV], u32x4 (&rbv)[BV]) {
         const int k0 = kbeg + s * BK;
+        if constexpr (EVEN) {
+#pragma unroll
+            for (int i = 0; i < AV; ++i)
+                ra[i] = buffer_load16(rsrc_a, a_lane, (k0 + i * (THREADS / VPR) * K) * ES, 0);
+#pragma unroll
+            for (int i = 0; i < BV; ++i) {
+                if constexpr (LAYOUT == TLG_NK)
+                    rbv[i] = buffer_load16(rsrc_b, b_lane, (k0 + i * (THREADS / VPR) * K) * ES, 0);
+                else if constexpr (B_T16)  // block row i % 8 of block column group i / 8
+                    rbv[i] = buffer_load16(rsrc_b, b_lane, ((k0 + i % 8) * N + (i / 8) * (THREADS / NBK) * 8) * ES, 0);
+                else
+                    rbv[i] = buffer_load16(rsrc_b, b_lane, (k0 + i * (THREADS / NV)) * N * ES, 0);
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < AV; ++i) {
             const int v = t + THREADS * i;
@@ -122,7 +165,6 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_kernel(const void* __restr
                 else
                     rbv[i] = u32x4{0u, 0u, 0u, 0u};
             } else {
-                constexpr int NV = BN / EPV;
                 const int kr = v / NV, nv = v % NV;
                 const int k = k0 + kr;
                 const int n = EVEN ? n0 + nv * EPV : min(n0 + nv * EPV, N - EPV);
@@ -134,8 +176,8 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_kernel(const void* __restr
         }
     };
     auto lstore = [&](int buf, const u32x4 (&ra)[AV], const u32x4 (&rbv)[BV]) {
-        S* As = lds[buf];
-        S* Bs = lds[buf] + A_ELEMS;
+        S* As = buf ? lds_a1 : lds_a0;
+        S* Bs = buf ? lds_b1 : lds_b0;
 #pragma unroll
         for (int i = 0; i < AV; ++i) {
             const int v = t + THREADS * i;
@@ -147,7 +189,6 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_kernel(const void* __restr
             if constexpr (LAYOUT == TLG_NK) {
                 *reinterpret_cast<u32x4*>(Bs + (v / VPR) * LDA + (v % VPR) * EPV) = rbv[i];
             } else if constexpr (B_NMAJOR) {
-                constexpr int NV = BN / EPV;
                 *reinterpret_cast<u32x4*>(Bs + (v / NV) * LDBN + (v % NV) * EPV) = rbv[i];
             } else {
                 // Transpose one 8×8 block: column c gathers half c of rows
@@ -181,9 +222,9 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_kernel(const void* __restr
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    auto compute = [&](int buf) {
-        const S* As = lds[buf];
-        const S* Bs = lds[buf] + A_ELEMS;
+    auto compute = [&](int buf, auto mid) {
+        const S* As = buf ? lds_a1 : lds_a0;
+        const S* Bs = buf ? lds_b1 : lds_b0;
         if constexpr (F32) {
 #pragma unroll
             for (int kq = 0; kq < BK / 8; ++kq) {
@@ -207,9 +248,10 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_kernel(const void* __restr
                     for (int i = 0; i < TM; ++i)
 #pragma unroll
                         for (int j = 0; j < TN; ++j) acc[i][j] = mfma32_f32(a[i][e], b[j][e], acc[i][j]);
+                if (kq == (BK / 8) / 2 - 1) mid();
             }
         } else {
-            // Operand fragments for k-step kq+1 are read from LDS before the
+            // Operand fragments for k-step kq+1 are read from LDS while the
             // MFMAs of k-step kq issue, so LDS latency overlaps the math.
             constexpr int KQ = BK / 16;
             u32x4 a[2][TM], b[2][TN];
@@ -230,18 +272,69 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_kernel(const void* __restr
 #pragma unroll
                     for (int j = 0; j < TN; ++j)
                         acc[i][j] = mfma32_16bit<IN>(a[kq & 1][i], b[kq & 1][j], acc[i][j]);
+                if (kq == KQ / 2 - 1) mid();
             }
-            // Ask the scheduler for an interleaved issue order: the first
-            // k-step's reads, then one LDS read between MFMAs, the rest MFMAs.
-            constexpr int NR = KQ * (TM + TN), NM = KQ * TM * TN, NI = NR - (TM + TN);
-            constexpr int PER = NM / (NI > 0 ? NI : 1);
-            __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);
+        }
+    };
+
+    // Issue order of one phase (one slice multiplied from LDS while the next
+    // is stored to the other buffer and the one after is loaded): the first
+    // k-step's operand reads, then every MFMA followed by its share of the
+    // other work — the global loads over the first half of the MFMAs, the next
+    // k-step's operand reads inside each k-step, and the LDS stores (16-bit
+    // [K][N] operands: four transposing permutes before each) over the second
+    // half.  Whole phase as one scheduling region for 16-bit inputs; fp32
+    // splits it at the middle k-step (measured: 2803 vs 3809 cycles per
+    // 256×256×64 bf16 slice, 8481 vs 8564 per 256×256×16 fp32 slice).
+    constexpr int NKQ = F32 ? BK / 8 : BK / 16;
+    constexpr int FR = F32 ? TM + (B_NMAJOR ? 4 : 1) * TN : TM + TN;
+    constexpr int NMF = F32 ? NKQ * 4 * TM * TN : NKQ * TM * TN;
+    constexpr int MPK = NMF / NKQ, HALF = NMF / 2;
+    constexpr int NVM = AV + BV, NDW = AV + BV;
+    constexpr int SV = HALF / NVM > 0 ? HALF / NVM : 1;
+    constexpr int SR = MPK / FR > 0 ? MPK / FR : 1;
+    constexpr int SW = HALF / NDW > 0 ? HALF / NDW : 1;
+    auto slot = [&](int m, bool loads, bool stores) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        if (loads && m % SV == 0 && m / SV < NVM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        if (m / MPK < NKQ - 1 && (m % MPK) % SR == 0 && (m % MPK) / SR < FR)
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // next k-step's operand read
+        if (stores && m >= HALF && (m - HALF) % SW == 0 && (m - HALF) / SW < NDW) {
+            if (B_T16 && (m - HALF) / SW >= AV) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+        }
+    };
+    auto whole_phase = [&]() {
+        __builtin_amdgcn_sched_group_barrier(0x100, FR, 0);
 #pragma unroll
-            for (int q = 0; q < NI; ++q) {
-                __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, NM - NI * PER, 0);
+        for (int m = 0; m < NMF; ++m) slot(m, true, true);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto first_half = [&]() {
+        __builtin_amdgcn_sched_group_barrier(0x100, FR, 0);
+#pragma unroll
+        for (int m = 0; m < HALF; ++m) slot(m, true, false);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto second_half = [&]() {
+#pragma unroll
+        for (int m = HALF; m < NMF; ++m) slot(m, false, true);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto nothing = [] {};
+    // One steady-state phase: multiply buffer cb, store `st` into the other
+    // buffer, load slice ls into `ld`.
+    auto phase = [&](int cb, int ls, u32x4 (&lda)[AV], u32x4 (&ldb)[BV], const u32x4 (&sta)[AV],
+                     const u32x4 (&stb)[BV]) {
+        gload(ls, lda, ldb);
+        if constexpr (F32) {
+            compute(cb, first_half);
+            lstore(cb ^ 1, sta, stb);
+            second_half();
+        } else {
+            compute(cb, nothing);
+            lstore(cb ^ 1, sta, stb);
+            whole_phase();
         }
     };
 
@@ -262,42 +355,31 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_kernel(const void* __restr
         // Steady state: pairs whose two prefetches are in range, so the loads
         // are unconditional and the wait before each LDS store covers only
         // the older slice.
-        // Scheduling barriers pin the phase order (the compiler would sink the
-        // prefetch below the store, shortening its lead and forcing a full
-        // wait); inside compute() LDS reads and MFMAs still interleave freely.
         int s = 0;
         for (; s + 3 < nslices; s += 2) {
-            gload(s + 2, ra0, rb0);
-            __builtin_amdgcn_sched_barrier(0);
-            compute(0);
-            __builtin_amdgcn_sched_barrier(0);
-            lstore(1, ra1, rb1);  // slice s+1
+            phase(0, s + 2, ra0, rb0, ra1, rb1);  // multiply s, store s+1, load s+2
             __syncthreads();
-            gload(s + 3, ra1, rb1);
-            __builtin_amdgcn_sched_barrier(0);
-            compute(1);
-            __builtin_amdgcn_sched_barrier(0);
-            lstore(0, ra0, rb0);  // slice s+2
+            phase(1, s + 3, ra1, rb1, ra0, rb0);  // multiply s+1, store s+2, load s+3
             __syncthreads();
         }
         // Tail: slice s is in buffer 0, slice s+1 (if any) in ra1.
         const int rem = nslices - s;  // 1, 2 or 3
         if (rem == 3) {
             gload(s + 2, ra0, rb0);
-            compute(0);
+            compute(0, nothing);
             lstore(1, ra1, rb1);
             __syncthreads();
-            compute(1);
+            compute(1, nothing);
             lstore(0, ra0, rb0);
             __syncthreads();
-            compute(0);
+            compute(0, nothing);
         } else if (rem == 2) {
-            compute(0);
+            compute(0, nothing);
             lstore(1, ra1, rb1);
             __syncthreads();
-            compute(1);
+            compute(1, nothing);
         } else {
-            compute(0);
+            compute(0, nothing);
         }
     }
 
@@ -361,7 +443,10 @@ static int launch_tiled_cfg(const tlg_plan& p, const void* X, const void* W, con
                             float* ws, hipStream_t stream) {
     const int S = p.split;
     const int kper = (int)(ceil_div(ceil_div(p.K, S), BK) * BK);
-    const bool even = p.M % BM == 0 && p.N % BN == 0 && (int64_t)kper * S == p.K;
+    const int64_t es = I == TLG_F32 ? 4 : 2;
+    const bool fits32 = (int64_t)BM * p.K * es < INT32_MAX &&
+                        (L == TLG_NK ? (int64_t)BN * p.K * es : p.K * p.N * es) < INT32_MAX;
+    const bool even = p.M % BM == 0 && p.N % BN == 0 && (int64_t)kper * S == p.K && fits32;
     const dim3 grid((unsigned)(p.grid_x * p.grid_y), (unsigned)S), block(64 * WM * WN);
     auto go = [&](auto ev, auto sp) {
         hipLaunchKernelGGL((tiled_kernel<I, O, L, E, BM, BN, BK, WM, WN, decltype(ev)::value, decltype(sp)::value>),
