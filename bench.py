@@ -15,6 +15,13 @@ the CPU oracle on sampled outputs, and both come with their roofline
 fraction: MFMA fp32 peak 157.3 TFLOP/s for the square GEMM, HBM 8 TB/s for
 the narrow one.
 
+Beside them (skipped with ``--no-extra``): the achievable ceilings from
+probe kernels (launch floor, plain 32 MiB read cold and warm, MFMA issue
+rate); the fp32 linear 128×768×768 + bias warm and cold; the four GPT-2-small
+linears at M = 128 (fp32), each warm and as a layer warm and cold; and one
+pass of the batched GPT-2-small stack at M = 8192 (12 layers × 4 linears, 48
+launches) in fp32 and bf16, with tokens/s.
+
 The oracle (plain C, double accumulation) is timed on this host's cores on
 a bounded row sample of the square workload and reported as
 ``cpu_baseline``; it is a reference point, not a target.
@@ -141,6 +148,214 @@ def cpu_baseline(case, budget_s: float = 15.0):
             "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
 
 
+def dev_tensor(torch, a, dt, dev):
+    """Host storage array (bf16 as raw uint16 bits) -> device tensor."""
+    if dt == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def host_f64(torch, t):
+    from dense_gemm_transformer_amd import inputs
+
+    t = t.cpu()
+    if t.dtype == torch.bfloat16:
+        return inputs.widen(t.view(torch.int16).numpy().view(np.uint16), "bf16")
+    return t.numpy().astype(np.float64)
+
+
+def median_span_ms(torch, fn, reps: int, stream) -> float:
+    """Median over ``reps`` of the HIP-event span of one call of ``fn()`` on ``stream``."""
+    spans = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        b.synchronize()
+        spans.append(a.elapsed_time(b))
+    return float(np.median(spans))
+
+
+def bench_ceilings(torch, dev, stream, cold_bufs):
+    """Achievable ceilings beside the datasheet peaks: launch floor, plain read, MFMA issue rate."""
+    import ctypes
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "dense_gemm_transformer_amd", "libtlgceil.so"))
+    vp, s = ctypes.c_void_p, ctypes.c_void_p(stream.cuda_stream)
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    sink = torch.zeros(512, dtype=torch.float32, device=dev)
+
+    def ok(rc):
+        if rc != 0:
+            raise RuntimeError(f"ceiling probe failed with status {rc}")
+
+    empty_ms = time_launches(lambda i: ok(lib.tlg_ceil_empty(256, vp(flag.data_ptr()), s)), 2000, stream)
+    nbytes = cold_bufs[0].numel() * cold_bufs[0].element_size()
+
+    def read(buf):
+        ok(lib.tlg_ceil_read(vp(buf.data_ptr()), ctypes.c_size_t(nbytes), vp(sink.data_ptr()), s))
+
+    for i in range(4 * len(cold_bufs)):
+        read(cold_bufs[i % len(cold_bufs)])
+    cold_ms = time_launches(lambda i: read(cold_bufs[i % len(cold_bufs)]), 2000, stream)
+    warm_ms = time_launches(lambda i: read(cold_bufs[0]), 2000, stream)
+    mfma = {}
+    for name, bf16, iters, flop in (("f32", 0, 2000, 4096), ("bf16", 1, 4000, 32768)):
+        call = lambda i: ok(lib.tlg_ceil_mfma(bf16, 256, iters, vp(sink.data_ptr()), s))
+        call(0)
+        ms = time_launches(call, 10, stream)
+        mfma[name] = 256 * 4 * iters * 16 * flop / (ms * 1e-3) / 1e12
+    return {"empty_kernel_event_us": round(empty_ms * 1e3, 3),
+            "read_cold_us": round(cold_ms * 1e3, 3), "read_cold_GB/s": round(nbytes / (cold_ms * 1e-3) / 1e9, 1),
+            "read_warm_us": round(warm_ms * 1e3, 3), "read_bytes": nbytes,
+            "mfma_f32_TFLOP/s": round(mfma["f32"], 1), "mfma_bf16_TFLOP/s": round(mfma["bf16"], 1),
+            "method": "HIP events over back-to-back launches of the probes in libtlgceil.so: empty kernel "
+                      "(256 workgroups), plain read of 32 MiB (256 workgroups x 8 waves x 16 loads of 16 B, "
+                      f"cold = rotating {len(cold_bufs)} buffers), 16 independent 32x32 MFMA chains per wave "
+                      "on all CUs"}
+
+
+def bench_c1(torch, dev, stream, no_parity: bool):
+    """fp32 linear 128x768x768 + bias: warm (one W) and cold (128 rotated copies of W, 302 MB)."""
+    import oracle
+    from dense_gemm_transformer_amd import inputs, tlgemm
+
+    c = inputs.workload_fp32_linear_128x768()
+    X, W0, b = (dev_tensor(torch, a, "f32", dev) for a in (c.X, c.W, c.b))
+    Y = torch.empty((c.M, c.N), dtype=torch.float32, device=dev)
+    plan = tlgemm.Plan.create(c.M, c.N, c.K, "f32", "f32", "NK", True, False)
+    ws_bytes = plan.workspace_size
+    ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    copies = [W0] + [W0.clone() for _ in range(127)]
+    run = lambda w: plan.run_ptrs(X.data_ptr(), w.data_ptr(), b.data_ptr(), Y.data_ptr(),
+                                  ws.data_ptr() if ws_bytes else 0, ws_bytes, stream.cuda_stream)
+    run(W0)
+    torch.cuda.synchronize()
+    err = None
+    if not no_parity:
+        ref = oracle.linear_case(c)
+        err = float(np.max(np.abs(host_f64(torch, Y) - ref)) / np.max(np.abs(ref)))
+    for i in range(256):
+        run(copies[i % len(copies)])
+    cold = time_launches(lambda i: run(copies[i % len(copies)]), 1024, stream)
+    warm = time_launches(lambda i: run(W0), 1024, stream)
+    return {"workload": "fp32 linear Y=X.W^T+b, M=128, K=768, N=768, W out x in, N(0,1)/N(0,0.02)",
+            "warm_us": round(warm * 1e3, 3), "cold_us": round(cold * 1e3, 3),
+            "TFLOP/s_warm": round(c.flops / (warm * 1e-3) / 1e12, 2),
+            "floor_us": round(c.flops / (PEAK_F32_TFLOPS * 1e12) * 1e6, 3),
+            "parity_err": err, "parity_pass": None if err is None else err <= 1e-5, "plan": plan.describe(),
+            "timing": "HIP events over back-to-back launches (includes launch gaps)"}
+
+
+def bench_c3(torch, dev, stream, no_parity: bool, copies: int = 12):
+    """GPT-2-small layer at M=128, fp32: each linear warm, and the four as a layer, warm and cold."""
+    import oracle
+    from dense_gemm_transformer_amd import inputs, tlgemm
+
+    cases = inputs.workload_gpt2_layer(M=128, dtype="f32")
+    gemms = []
+    for c in cases:
+        X, W, b = (dev_tensor(torch, a, "f32", dev) for a in (c.X, c.W, c.b))
+        plan = tlgemm.Plan.create(c.M, c.N, c.K, "f32", "f32", "NK", True, c.gelu)
+        ws_bytes = plan.workspace_size
+        gemms.append({"case": c, "X": X, "b": b, "Ws": [W] + [W.clone() for _ in range(copies - 1)],
+                      "Y": torch.empty((c.M, c.N), dtype=torch.float32, device=dev), "plan": plan,
+                      "ws": torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev), "ws_bytes": ws_bytes})
+
+    def run(g, w):
+        g["plan"].run_ptrs(g["X"].data_ptr(), w.data_ptr(), g["b"].data_ptr(), g["Y"].data_ptr(),
+                           g["ws"].data_ptr() if g["ws_bytes"] else 0, g["ws_bytes"], stream.cuda_stream)
+
+    out = {"workload": "GPT-2-small layer linears at M=128, fp32, bias on all, tanh-GELU on fc; "
+                       f"cold = {copies} rotated weight sets ({copies} x 28.3 MB)", "gemms": {}}
+    for g in gemms:
+        run(g, g["Ws"][0])
+    torch.cuda.synchronize()
+    for g in gemms:
+        c = g["case"]
+        err = None
+        if not no_parity:
+            ref = oracle.linear_case(c)
+            err = float(np.max(np.abs(host_f64(torch, g["Y"]) - ref)) / np.max(np.abs(ref)))
+        warm = time_launches(lambda i: run(g, g["Ws"][0]), 512, stream)
+        out["gemms"][c.name] = {"warm_us": round(warm * 1e3, 3),
+                                "TFLOP/s_warm": round(c.flops / (warm * 1e-3) / 1e12, 2),
+                                "floor_us": round(c.flops / (PEAK_F32_TFLOPS * 1e12) * 1e6, 3),
+                                "parity_err": err, "plan": g["plan"].describe()}
+
+    def layer(l):
+        for g in gemms:
+            run(g, g["Ws"][l % copies])
+
+    for l in range(2 * copies):
+        layer(l)
+    warm = time_launches(lambda i: layer(0), 256, stream)
+    cold = time_launches(lambda i: layer(i), 256, stream)
+    flops = sum(g["case"].flops for g in gemms)
+    out.update({"layer_warm_us": round(warm * 1e3, 3), "layer_cold_us": round(cold * 1e3, 3),
+                "layer_TFLOP/s_cold": round(flops / (cold * 1e-3) / 1e12, 2),
+                "timing": "HIP events over back-to-back layers of four launches (includes launch gaps)"})
+    out["parity_pass"] = None if no_parity else all(v["parity_err"] <= 1e-5 for v in out["gemms"].values())
+    return out
+
+
+def bench_c5(torch, dev, stream, dtype: str, no_parity: bool, layers: int = 12, reps: int = 20):
+    """Batched GPT-2-small stack at M=8192: one pass = 12 layers x 4 linears, 48 launches on one stream."""
+    from dense_gemm_transformer_amd import inputs, tlgemm
+
+    M, w = 8192, 5
+    peak = PEAK_F32_TFLOPS if dtype == "f32" else PEAK_BF16_TFLOPS
+    xs, plans, ys, wb = [], [], [], []
+    for g, (name, N, K, gelu) in enumerate(inputs.GPT2_LINEARS):
+        x0 = dev_tensor(torch, inputs.gpt2_activation(w, 0, g, M, dtype), dtype, dev)
+        # later layers read row-rotated copies of layer 0's activations: distinct memory, same values
+        xs.append([x0] + [torch.roll(x0, shifts=97 * l, dims=0).contiguous() for l in range(1, layers)])
+        plans.append(tlgemm.Plan.create(M, N, K, dtype, dtype, "NK", True, gelu))
+        ys.append(torch.empty((M, N), dtype=tlgemm.torch_dtype(dtype), device=dev))
+    for l in range(layers):
+        row = []
+        for g in range(4):
+            W, b = inputs.gpt2_weights(w, l, g, dtype)
+            row.append((dev_tensor(torch, W, dtype, dev), dev_tensor(torch, b, dtype, dev)))
+        wb.append(row)
+    wss = [torch.zeros(max(p.workspace_size, 1), dtype=torch.uint8, device=dev) for p in plans]
+
+    def one_pass():
+        for l in range(layers):
+            for g in range(4):
+                p, (W, b) = plans[g], wb[l][g]
+                p.run_ptrs(xs[g][l].data_ptr(), W.data_ptr(), b.data_ptr(), ys[g].data_ptr(),
+                           wss[g].data_ptr() if p.workspace_size else 0, p.workspace_size, stream.cuda_stream)
+
+    errs = {}
+    if not no_parity:  # layer 0 of each linear, sampled against the oracle
+        for g, (name, N, K, gelu) in enumerate(inputs.GPT2_LINEARS):
+            p, (W, b) = plans[g], wb[0][g]
+            p.run_ptrs(xs[g][0].data_ptr(), W.data_ptr(), b.data_ptr(), ys[g].data_ptr(),
+                       wss[g].data_ptr() if p.workspace_size else 0, p.workspace_size, stream.cuda_stream)
+            torch.cuda.synchronize()
+            Wh, bh = inputs.gpt2_weights(w, 0, g, dtype)
+            case = inputs.LinearCase(name, M, N, K, dtype, dtype, "NK", True, gelu,
+                                     inputs.gpt2_activation(w, 0, g, M, dtype), Wh, bh)
+            errs[name] = sampled_parity(case, host_f64(torch, ys[g]), npts=1000)
+    for _ in range(3):
+        one_pass()
+    ms = median_span_ms(torch, one_pass, reps, stream)
+    flops = layers * sum(2 * M * N * K for _, N, K, _ in inputs.GPT2_LINEARS)
+    tol = 1e-5 if dtype == "f32" else 1e-2
+    return {"workload": f"GPT-2-small stack, M=8192 (64 x 128 tokens), {layers} layers x "
+                        "{qkv, attn-out, fc+GELU, proj}, bias on all, " + dtype + " in and out",
+            "pass_ms": round(ms, 4), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2),
+            "frac_mfma_peak": round(flops / (ms * 1e-3) / 1e12 / peak, 4),
+            "tokens_per_s": round(M / (ms * 1e-3), 1), "flops_per_pass": flops,
+            "parity_err_layer0": errs or None,
+            "parity_pass": None if not errs else all(e <= tol for e in errs.values()),
+            "plans": [p.describe() for p in plans],
+            "timing": f"median over {reps} passes of the HIP-event span of one pass (48 launches, one stream); "
+                      "12 distinct weight sets, activations of later layers are row-rotated copies of layer 0's"}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -149,6 +364,8 @@ def main(argv=None) -> int:
     ap.add_argument("--narrow-launches", type=int, default=2000, help="timed cold narrow launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the ceiling probes and the 128-row layer and M=8192 stack workloads")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -232,6 +449,20 @@ def main(argv=None) -> int:
     n_gbs = n_bytes / (n_ms * 1e-3) / 1e9
     log(f"narrow fp16: {nplan.describe()} cold {n_ms * 1e3:.2f} us ({n_gbs:.0f} GB/s), warm {warm_ms * 1e3:.2f} us, "
         f"parity {n_err}")
+
+    extra = {}
+    if not args.no_extra:
+        log("ceilings: launch floor, plain 32 MiB read, MFMA issue rate")
+        extra["ceilings"] = bench_ceilings(torch, dev, stream, Ws)
+        del Ws, W0
+        log("fp32 linear 128x768x768 + bias")
+        extra["linear_128x768x768_f32"] = bench_c1(torch, dev, stream, args.no_parity)
+        log("GPT-2 layer at M=128, fp32")
+        extra["gpt2_layer_m128_f32"] = bench_c3(torch, dev, stream, args.no_parity)
+        for dt in ("f32", "bf16"):
+            log(f"GPT-2 stack at M=8192, {dt}")
+            extra[f"gpt2_stack_m8192_{dt}"] = bench_c5(torch, dev, stream, dt, args.no_parity)
+            torch.cuda.empty_cache()
     clocks_after = read_clocks()
 
     cpu = None
@@ -282,8 +513,10 @@ def main(argv=None) -> int:
                                      "algorithmic_bytes_per_launch": n_bytes},
                         "timing": "HIP events over back-to-back launches (includes launch gaps)",
                         "plan": nplan.describe()},
-        "clocks": {"before": clocks_before, "after": clocks_after},
+        "clocks": {"before": clocks_before, "after": clocks_after,
+                   "state": "UNPINNED" + (" (changed during the run)" if clocks_before != clocks_after else "")},
     }
+    out.update(extra)
     print(json.dumps(out), flush=True)
     return 0
 

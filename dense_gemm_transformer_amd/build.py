@@ -3,8 +3,9 @@
     python -m dense_gemm_transformer_amd.build [--force] [-j N]
 
 Each source compiles to an object under ``_build/`` in parallel; the objects
-link into ``dense_gemm_transformer_amd/libtlgemm.so``.  Works without a GPU
-(hipcc cross-compiles for gfx950).
+link into ``dense_gemm_transformer_amd/libtlgemm.so``.  The benchmark's
+hardware-ceiling probes link separately into ``libtlgceil.so``.  Works
+without a GPU (hipcc cross-compiles for gfx950).
 """
 
 from __future__ import annotations
@@ -22,6 +23,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtlgemm.so")
+CEIL_LIB = os.path.join(PKG, "libtlgceil.so")
+CEIL_SOURCES = ["ceilings.hip"]
 
 ARCH = "gfx950"
 SOURCES = [
@@ -71,20 +74,26 @@ def _compile(src: str, force: bool) -> str:
     return obj
 
 
-def build(force: bool = True, jobs: int | None = None, verbose: bool = False) -> str:
-    """Compile every source for gfx950 and link the shared library; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    jobs = jobs or min(len(SOURCES), max(1, (os.cpu_count() or 2)))
-    with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, force), SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(lib: str, objs: list[str]) -> None:
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(force: bool = True, jobs: int | None = None, verbose: bool = False) -> str:
+    """Compile every source for gfx950 and link the shared libraries; returns the GEMM library's path."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + CEIL_SOURCES
+    jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 2)))
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, force), srcs))
+    _link(LIB, objs[:len(SOURCES)])
+    _link(CEIL_LIB, objs[len(SOURCES):])
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CEIL_LIB}")
     return LIB
 
 

@@ -1,0 +1,112 @@
+// Hardware ceilings measured beside the datasheet peaks, for the benchmark's
+// reports: the launch floor (an empty kernel), the rate of a plain read of a
+// buffer, and the MFMA issue rate with no memory traffic.  These kernels are
+// measurement probes: no GEMM path calls them.  They sit in their own shared
+// library (libtlgceil.so) with a C ABI of plain pointers and sizes.
+//
+// "Optimizing a GPT-2-class transformer on a GPU" (Act V) and "One multiply,
+// one RTX 5090, eight kernels" ("Where the time goes", "What was not
+// measured") time an empty kernel and loads-only / math-only variants to
+// locate where a kernel's time goes; these are the gfx950 counterparts.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tlgceil.h"
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__global__ void empty_kernel(int* flag) {
+    if (threadIdx.x == 0x7fffffff) flag[0] = 1;  // never true: keeps the kernel non-trivial to the compiler
+}
+
+// Each workgroup of 8 waves reads one 128 KiB block: every load instruction
+// of a wave covers 1 KiB of consecutive bytes, all 16 loads of a lane are in
+// flight before the first is used.  The xor of the data is stored only if it
+// equals a value it never takes, so the loads cannot be dropped.
+constexpr int kReadLoads = 16, kReadWaves = 8;
+constexpr size_t kReadBlock = (size_t)kReadWaves * kReadLoads * 1024;
+
+__global__ __launch_bounds__(64 * kReadWaves) void read_kernel(const char* __restrict__ base, float* __restrict__ sink) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const char* p = base + (size_t)blockIdx.x * kReadBlock;
+    u32x4 v[kReadLoads];
+#pragma unroll
+    for (int j = 0; j < kReadLoads; ++j)
+        v[j] = *reinterpret_cast<const u32x4*>(p + ((size_t)w * kReadLoads + j) * 1024 + lane * 16);
+    uint32_t x = 0;
+#pragma unroll
+    for (int j = 0; j < kReadLoads; ++j) x ^= v[j][0] ^ v[j][1] ^ v[j][2] ^ v[j][3];
+    if (x == 0x9e3779b9u) sink[threadIdx.x] = 1.0f;
+}
+
+// Sixteen independent 32x32 accumulators per wave, so consecutive MFMAs never
+// wait on each other; the operands stay in registers.  One wave per SIMD
+// (256 threads per workgroup, one workgroup per CU when the grid is the CU count).
+template <bool BF16>
+__global__ __launch_bounds__(256) void mfma_kernel(int iters, float* __restrict__ sink) {
+    f32x16 acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][e] = 0.0f;
+    const float a = 1.0f + threadIdx.x * 1e-7f, b = 1.0f - threadIdx.x * 1e-7f;
+    u32x4 ra, rb;
+    for (int e = 0; e < 4; ++e) {
+        ra[e] = 0x3f803f80u + threadIdx.x;
+        rb[e] = 0x3f803f80u - threadIdx.x;
+    }
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if constexpr (BF16)
+                acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ra),
+                                                                 __builtin_bit_cast(bf16x8, rb), acc[i], 0, 0, 0);
+            else
+                acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc[i], 0, 0, 0);
+        }
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s += acc[i][e];
+    if (s == 1234.5f) sink[threadIdx.x] = s;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Empty kernel over `grid` workgroups of 64 threads.
+int tlg_ceil_empty(int grid, int* flag, void* stream) {
+    if (grid <= 0 || !flag) return -1;
+    hipLaunchKernelGGL(empty_kernel, dim3(grid), dim3(64), 0, (hipStream_t)stream, flag);
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+// Read `bytes` bytes from `p` (16-byte aligned, a multiple of 128 KiB).
+// `sink` must hold 512 floats.
+int tlg_ceil_read(const void* p, size_t bytes, float* sink, void* stream) {
+    if (!p || !sink || bytes == 0 || bytes % kReadBlock != 0 || reinterpret_cast<uintptr_t>(p) % 16 != 0) return -1;
+    hipLaunchKernelGGL(read_kernel, dim3((unsigned)(bytes / kReadBlock)), dim3(64 * kReadWaves), 0,
+                       (hipStream_t)stream, static_cast<const char*>(p), sink);
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+// MFMA issue probe: `grid` workgroups of 4 waves, each wave issuing
+// 16·iters MFMAs (bf16 != 0: 32x32x16 bf16, 32768 flop each; else 32x32x2
+// fp32, 4096 flop each).  `sink` must hold 256 floats.
+int tlg_ceil_mfma(int bf16, int grid, int iters, float* sink, void* stream) {
+    if (grid <= 0 || iters <= 0 || !sink) return -1;
+    if (bf16)
+        hipLaunchKernelGGL(mfma_kernel<true>, dim3(grid), dim3(256), 0, (hipStream_t)stream, iters, sink);
+    else
+        hipLaunchKernelGGL(mfma_kernel<false>, dim3(grid), dim3(256), 0, (hipStream_t)stream, iters, sink);
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+}  // extern "C"

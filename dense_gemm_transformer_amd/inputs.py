@@ -10,7 +10,8 @@ Recipe (one source of truth for tests and the benchmark):
   a seeded generator but never say which one ("Optimizing a GPT-2-class
   transformer on a GPU", Results), so the draws differ from theirs.
 * Seeds: ``1000 * workload + 10 * layer + tensor`` with tensor X = 1, W = 2,
-  b = 3.
+  b = 3, plus ``100000 * g`` for the g-th linear of a GPT-2 layer (qkv 0,
+  attn-out 1, fc 2, proj 3), so that no two tensors of a stack share a seed.
 * Values are drawn in float64, rounded to float32 with round-to-nearest-even,
   then (for half formats) rounded again to float16 / bfloat16 with
   round-to-nearest-even. The stored values are exactly what the kernels read;
@@ -31,8 +32,8 @@ DTYPES = ("f32", "f16", "bf16")
 TENSOR_X, TENSOR_W, TENSOR_B = 1, 2, 3
 
 
-def seed_for(workload: int, layer: int, tensor: int) -> int:
-    return 1000 * workload + 10 * layer + tensor
+def seed_for(workload: int, layer: int, tensor: int, gemm: int = 0) -> int:
+    return 1000 * workload + 10 * layer + tensor + 100_000 * gemm
 
 
 def _rng(seed: int) -> np.random.Generator:
@@ -115,13 +116,6 @@ class LinearCase:
         return 2 * self.M * self.N * self.K
 
 
-def _gpt2_linear(name, workload, layer, tensor_base, M, N, K, dt, out_dt, gelu):
-    X = normal(seed_for(workload, layer, tensor_base + TENSOR_X), (M, K), 1.0, dt)
-    W = normal(seed_for(workload, layer, tensor_base + TENSOR_W), (N, K), 0.02, dt)
-    b = normal(seed_for(workload, layer, tensor_base + TENSOR_B), (N,), 0.02, dt)
-    return LinearCase(name, M, N, K, dt, out_dt, "NK", True, gelu, X, W, b)
-
-
 # GPT-2-small linear shapes: (name, N, K, gelu) with d_model 768, d_ff 3072.
 GPT2_LINEARS = (
     ("qkv", 2304, 768, False),
@@ -129,6 +123,20 @@ GPT2_LINEARS = (
     ("fc", 3072, 768, True),
     ("proj", 768, 3072, False),
 )
+
+
+def gpt2_weights(workload: int, layer: int, gemm: int, dtype: str):
+    """Weight ``[N][K]`` and bias ``[N]`` of linear ``gemm`` of a GPT-2 layer, both ~ N(0, 0.02)."""
+    _, N, K, _ = GPT2_LINEARS[gemm]
+    W = normal(seed_for(workload, layer, TENSOR_W, gemm), (N, K), 0.02, dtype)
+    b = normal(seed_for(workload, layer, TENSOR_B, gemm), (N,), 0.02, dtype)
+    return W, b
+
+
+def gpt2_activation(workload: int, layer: int, gemm: int, M: int, dtype: str):
+    """Input ``[M][K]`` ~ N(0, 1) of linear ``gemm`` of a GPT-2 layer."""
+    K = GPT2_LINEARS[gemm][2]
+    return normal(seed_for(workload, layer, TENSOR_X, gemm), (M, K), 1.0, dtype)
 
 
 def workload_fp32_linear_128x768(workload: int = 1) -> LinearCase:
@@ -152,9 +160,10 @@ def workload_fp16_narrow(workload: int = 2, copy: int = 0, M: int = 16, N: int =
 def workload_gpt2_layer(workload: int = 3, M: int = 128, dtype: str = "f32", layer: int = 0):
     """The four GPT-2-small linears of one layer at M rows (bias on all, GELU on fc)."""
     cases = []
-    for i, (name, N, K, gelu) in enumerate(GPT2_LINEARS):
-        cases.append(_gpt2_linear(f"{name}_{M}x{N}x{K}_{dtype}", workload, layer, 3 * i, M, N, K,
-                                  dtype, dtype, gelu))
+    for g, (name, N, K, gelu) in enumerate(GPT2_LINEARS):
+        W, b = gpt2_weights(workload, layer, g, dtype)
+        X = gpt2_activation(workload, layer, g, M, dtype)
+        cases.append(LinearCase(f"{name}_{M}x{N}x{K}_{dtype}", M, N, K, dtype, dtype, "NK", True, gelu, X, W, b))
     return cases
 
 

@@ -25,6 +25,17 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), name
 
 
+def test_ceiling_probe_library_exports_its_header():
+    """The benchmark's probe library loads without a GPU and exports what include/tlgceil.h declares."""
+    hdr = os.path.join(os.path.dirname(HEADER), "tlgceil.h")
+    text = re.sub(r"/\*.*?\*/", "", open(hdr).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(tlg_ceil_\w+)\s*\(", text)))
+    assert names == ["tlg_ceil_empty", "tlg_ceil_mfma", "tlg_ceil_read"]
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(t.LIB_PATH), "libtlgceil.so"))
+    for name in names:
+        assert hasattr(lib, name), name
+
+
 def _plan(*a, **k):
     return t.Plan.create(*a, **k)
 
