@@ -54,16 +54,46 @@ template <int DT> __device__ inline void store_out(void* Y, int64_t idx, float v
     }
 }
 
+// 16 bytes of output from 16 / sizeof(element) fp32 values (same rounding as store_out).
+template <int DT> __device__ inline u32x4 pack16(const float* v) {
+    u32x4 o;
+    if constexpr (DT == TLG_F32) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) o[u] = __float_as_uint(v[u]);
+    } else if constexpr (DT == TLG_F16) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const _Float16 lo = (_Float16)v[2 * u], hi = (_Float16)v[2 * u + 1];
+            o[u] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            o[u] = (uint32_t)f32_to_bf16_rne(v[2 * u]) | ((uint32_t)f32_to_bf16_rne(v[2 * u + 1]) << 16);
+    }
+    return o;
+}
+
 template <int DT> __device__ inline float load_elem(const void* p, int64_t idx) {
     return Elem<DT>::to_f32(static_cast<const typename Elem<DT>::storage*>(p)[idx]);
 }
 
 // ---- fused epilogue ----------------------------------------------------------------
 // Bias first, then the tanh form of GELU, evaluated in fp32.
+// tanh from its exponential identity tanh(u) = 1 - 2 / (e^(2u) + 1), with the
+// hardware base-2 exponential and reciprocal (each within about 1 ulp): e^(2u)
+// overflows to +inf or underflows to 0 for large |u|, which gives exactly ±1,
+// and NaN propagates.  Near u = 0 the subtraction cancels, leaving an absolute
+// error of a few 1e-8, which GELU's factor y/2 keeps far below fp32 parity.
+__device__ inline float tanh_fast(float u) {
+    const float e = __builtin_amdgcn_exp2f(u * 2.8853900817779268f);  // 2/ln(2): 2^(2u·log2 e) = e^(2u)
+    return 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
+}
+
 __device__ inline float gelu_tanh(float y) {
     const float c = 0.7978845608028654f;  // sqrt(2/pi)
     const float u = c * (y + 0.044715f * y * y * y);
-    return 0.5f * y * (1.0f + tanhf(u));
+    return 0.5f * y * (1.0f + tanh_fast(u));
 }
 
 template <uint32_t EPI> __device__ inline float epilogue(float acc, float b) {

@@ -37,9 +37,18 @@
 
 namespace tlg {
 
+// Waves per SIMD the register allocation must allow: a wave tile of up to
+// 64×64 (64 accumulator registers) leaves room for two waves, up to 32×32 for
+// four, so LDS rather than registers limits how many workgroups share a CU.
+template <int BM, int BN, int WM, int WN>
+constexpr int tiled_occupancy() {
+    constexpr int acc = (BM / WM) * (BN / WN) / 64;
+    return acc <= 16 ? 4 : acc <= 64 ? 2 : 1;
+}
+
 template <int IN, int OUT, int LAYOUT, uint32_t EPI, int BM, int BN, int BK, int WM, int WN, bool EVEN,
           bool SPLIT>
-__global__ __launch_bounds__(64 * WM * WN) void tiled_kernel(const void* __restrict__ Xv,
+__global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) void tiled_kernel(const void* __restrict__ Xv,
                                                             const void* __restrict__ Wv,
                                                             const void* __restrict__ bias,
                                                             void* __restrict__ Y, float* __restrict__ ws,
@@ -385,6 +394,69 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_kernel(const void* __restr
 
     // ---- epilogue: a 32×32 accumulator holds column (lane % 32) and rows
     // 8*(e/4) + 4*(lane/32) + e%4 for register e.
+    if constexpr (EVEN) {
+        // Exact-fit tiles leave through LDS: each wave stages 16 rows × WTN of
+        // its tile (fp32, row stride WTN+8 floats, so the two half-waves'
+        // writes land on disjoint banks), then every lane takes whole 16-byte
+        // runs of one row, applies bias and GELU, converts and stores them:
+        // full-line writes and one store per 16 bytes instead of one per element.
+        // Two waves share each A-operand array, free once every wave is past
+        // its last multiply.
+        constexpr int SW = WTN + 8;
+        constexpr int STG = 16 * SW;
+        static_assert(2 * STG * 4 <= A_ELEMS * (int)sizeof(S), "staging fits in the A-operand buffers");
+        constexpr int OB = SPLIT ? 4 : (OUT == TLG_F32 ? 4 : 2);  // bytes per written element
+        constexpr int EPC = 16 / OB;                               // elements per 16-byte store
+        constexpr int CPR = WTN / EPC;                             // 16-byte runs per staged row
+        static_assert(64 % CPR == 0 && (16 * CPR) % 64 == 0, "runs divide evenly over the lanes");
+        __syncthreads();
+        float* stg = reinterpret_cast<float*>((wave >> 1) ? lds_a1 : lds_a0) + (wave & 1) * STG;
+        const int col = (lane % CPR) * EPC;  // the same columns for every run of this lane
+        const int ncol = n0 + wn0 + col;
+        float bcol[EPC];
+#pragma unroll
+        for (int q = 0; q < EPC; ++q) {
+            bcol[q] = 0.0f;
+            if constexpr (!SPLIT && (EPI & TLG_EPI_BIAS) != 0) bcol[q] = load_elem<IN>(bias, ncol + q);
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int e = 8 * h; e < 8 * h + 8; ++e)
+                        stg[(8 * ((e >> 2) & 1) + 4 * g + (e & 3)) * SW + j * 32 + r] = acc[i][j][e];
+                // LDS operations of one wave complete in order: the reads
+                // below see these writes, and the next half's writes follow them.
+#pragma unroll
+                for (int q = 0; q < (16 * CPR) / 64; ++q) {
+                    const int row = (lane + 64 * q) / CPR;
+                    const float* src = stg + row * SW + col;
+                    float v[EPC];
+#pragma unroll
+                    for (int u = 0; u < EPC; u += 4) {
+                        const f32x4 x = *reinterpret_cast<const f32x4*>(src + u);
+                        v[u] = x[0], v[u + 1] = x[1], v[u + 2] = x[2], v[u + 3] = x[3];
+                    }
+                    const int64_t m = m0 + wm0 + i * 32 + 16 * h + row;
+                    u32x4 out;
+                    if constexpr (SPLIT) {
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) out[u] = __float_as_uint(v[u]);
+                        *reinterpret_cast<u32x4*>(ws + ((int64_t)z * M + m) * N + ncol) = out;
+                    } else {
+#pragma unroll
+                        for (int u = 0; u < EPC; ++u) v[u] = epilogue<EPI>(v[u], bcol[u]);
+                        out = pack16<OUT>(v);
+                        *reinterpret_cast<u32x4*>(static_cast<char*>(Y) + (m * N + ncol) * OB) = out;
+                    }
+                }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -392,11 +464,11 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_kernel(const void* __restr
             const int n = n0 + wn0 + j * 32 + r;
             float b = 0.0f;
             if constexpr (!SPLIT && (EPI & TLG_EPI_BIAS) != 0)
-                if (EVEN || n < N) b = load_elem<IN>(bias, n);
+                if (n < N) b = load_elem<IN>(bias, n);
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int m = m0 + wm0 + i * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
-                if (!EVEN && (m >= M || n >= N)) continue;
+                if (m >= M || n >= N) continue;
                 if constexpr (SPLIT)
                     ws[((int64_t)z * M + m) * N + n] = acc[i][j][e];
                 else
