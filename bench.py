@@ -177,6 +177,32 @@ def median_span_ms(torch, fn, reps: int, stream) -> float:
     return float(np.median(spans))
 
 
+def graph_span_ms(torch, launch, reps: int, outputs):
+    """Capture ``launch(stream_handle)`` in a HIP graph on a side stream; median event span of one replay.
+
+    The replayed outputs are compared bitwise with an eager run first (the
+    kernels are deterministic, so a replay must reproduce them exactly).
+    """
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        launch(side.cuda_stream)
+    side.synchronize()
+    want = [o.clone() for o in outputs]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        launch(side.cuda_stream)
+    for o in outputs:
+        o.zero_()
+    graph.replay()
+    torch.cuda.synchronize()
+    same = all(torch.equal(o, w) for o, w in zip(outputs, want))
+    for _ in range(3):
+        graph.replay()
+    ms = median_span_ms(torch, graph.replay, reps, torch.cuda.current_stream())
+    del graph
+    return ms, same
+
+
 def bench_ceilings(torch, dev, stream, cold_bufs):
     """Achievable ceilings beside the datasheet peaks: launch floor, plain read, MFMA issue rate."""
     import ctypes
@@ -263,9 +289,10 @@ def bench_c3(torch, dev, stream, no_parity: bool, copies: int = 12):
                       "Y": torch.empty((c.M, c.N), dtype=torch.float32, device=dev), "plan": plan,
                       "ws": torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev), "ws_bytes": ws_bytes})
 
-    def run(g, w):
+    def run(g, w, sh=None):
         g["plan"].run_ptrs(g["X"].data_ptr(), w.data_ptr(), g["b"].data_ptr(), g["Y"].data_ptr(),
-                           g["ws"].data_ptr() if g["ws_bytes"] else 0, g["ws_bytes"], stream.cuda_stream)
+                           g["ws"].data_ptr() if g["ws_bytes"] else 0, g["ws_bytes"],
+                           stream.cuda_stream if sh is None else sh)
 
     out = {"workload": "GPT-2-small layer linears at M=128, fp32, bias on all, tanh-GELU on fc; "
                        f"cold = {copies} rotated weight sets ({copies} x 28.3 MB)", "gemms": {}}
@@ -293,9 +320,16 @@ def bench_c3(torch, dev, stream, no_parity: bool, copies: int = 12):
     warm = time_launches(lambda i: layer(0), 256, stream)
     cold = time_launches(lambda i: layer(i), 256, stream)
     flops = sum(g["case"].flops for g in gemms)
+    single_ms = median_span_ms(torch, lambda: layer(0), 200, stream)
+    graph_ms, graph_same = graph_span_ms(torch, lambda sh: [run(g, g["Ws"][0], sh) for g in gemms], 200,
+                                         [g["Y"] for g in gemms])
+    out.update({"layer_single_eager_us": round(single_ms * 1e3, 3), "layer_single_graph_us": round(graph_ms * 1e3, 3),
+                "layer_graph_bitwise_equal": graph_same})
     out.update({"layer_warm_us": round(warm * 1e3, 3), "layer_cold_us": round(cold * 1e3, 3),
                 "layer_TFLOP/s_cold": round(flops / (cold * 1e-3) / 1e12, 2),
-                "timing": "HIP events over back-to-back layers of four launches (includes launch gaps)"})
+                "timing": "HIP events over back-to-back layers of four launches (includes launch gaps); "
+                          "layer_single_eager_us / layer_single_graph_us: median event span of one isolated layer, "
+                          "launched eagerly or replayed from a HIP graph of its four launches (warm weights)"})
     out["parity_pass"] = None if no_parity else all(v["parity_err"] <= 1e-5 for v in out["gemms"].values())
     return out
 
@@ -321,12 +355,13 @@ def bench_c5(torch, dev, stream, dtype: str, no_parity: bool, layers: int = 12, 
         wb.append(row)
     wss = [torch.zeros(max(p.workspace_size, 1), dtype=torch.uint8, device=dev) for p in plans]
 
-    def one_pass():
+    def one_pass(sh=None):
         for l in range(layers):
             for g in range(4):
                 p, (W, b) = plans[g], wb[l][g]
                 p.run_ptrs(xs[g][l].data_ptr(), W.data_ptr(), b.data_ptr(), ys[g].data_ptr(),
-                           wss[g].data_ptr() if p.workspace_size else 0, p.workspace_size, stream.cuda_stream)
+                           wss[g].data_ptr() if p.workspace_size else 0, p.workspace_size,
+                           stream.cuda_stream if sh is None else sh)
 
     errs = {}
     if not no_parity:  # layer 0 of each linear, sampled against the oracle
@@ -342,6 +377,7 @@ def bench_c5(torch, dev, stream, dtype: str, no_parity: bool, layers: int = 12, 
     for _ in range(3):
         one_pass()
     ms = median_span_ms(torch, one_pass, reps, stream)
+    graph_ms, graph_same = graph_span_ms(torch, one_pass, reps, ys)
     flops = layers * sum(2 * M * N * K for _, N, K, _ in inputs.GPT2_LINEARS)
     tol = 1e-5 if dtype == "f32" else 1e-2
     return {"workload": f"GPT-2-small stack, M=8192 (64 x 128 tokens), {layers} layers x "
@@ -349,11 +385,14 @@ def bench_c5(torch, dev, stream, dtype: str, no_parity: bool, layers: int = 12, 
             "pass_ms": round(ms, 4), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2),
             "frac_mfma_peak": round(flops / (ms * 1e-3) / 1e12 / peak, 4),
             "tokens_per_s": round(M / (ms * 1e-3), 1), "flops_per_pass": flops,
+            "pass_ms_graph": round(graph_ms, 4), "TFLOP/s_graph": round(flops / (graph_ms * 1e-3) / 1e12, 2),
+            "graph_bitwise_equal": graph_same,
             "parity_err_layer0": errs or None,
             "parity_pass": None if not errs else all(e <= tol for e in errs.values()),
             "plans": [p.describe() for p in plans],
             "timing": f"median over {reps} passes of the HIP-event span of one pass (48 launches, one stream); "
-                      "12 distinct weight sets, activations of later layers are row-rotated copies of layer 0's"}
+                      "12 distinct weight sets, activations of later layers are row-rotated copies of layer 0's; "
+                      "pass_ms_graph: the same 48 launches captured once in a HIP graph, median replay span"}
 
 
 def main(argv=None) -> int:
