@@ -20,7 +20,9 @@ probe kernels (launch floor, plain 32 MiB read cold and warm, MFMA issue
 rate); the fp32 linear 128×768×768 + bias warm and cold; the four GPT-2-small
 linears at M = 128 (fp32), each warm and as a layer warm and cold; and one
 pass of the batched GPT-2-small stack at M = 8192 (12 layers × 4 linears, 48
-launches) in fp32 and bf16, with tokens/s.
+launches) in fp32 and bf16, with tokens/s; and the backward GEMMs of one
+GPT-2-small layer at 8192 tokens (dX with the [K][N] weight layout, dW with the
+transposed first operand accumulated onto the previous gradient).
 
 The oracle (plain C, double accumulation) is timed on this host's cores on
 a bounded row sample of the square workload and reported as
@@ -395,6 +397,68 @@ def bench_c5(torch, dev, stream, dtype: str, no_parity: bool, layers: int = 12, 
                       "pass_ms_graph: the same 48 launches captured once in a HIP graph, median replay span"}
 
 
+def bench_backward(torch, dev, stream, dtype: str, no_parity: bool, reps: int = 20):
+    """Backward GEMMs of the four GPT-2-small linears at 8192 tokens: dX = dY·W (weight read [K][N]) and
+    dW = dYᵀ·X accumulated onto an existing gradient (first operand stored transposed, residual flag)."""
+    from dense_gemm_transformer_amd import inputs, tlgemm
+
+    T, w = 8192, 6
+    peak = PEAK_F32_TFLOPS if dtype == "f32" else PEAK_BF16_TFLOPS
+    jobs = []
+    for g, (name, N, K, _) in enumerate(inputs.GPT2_LINEARS):
+        W, _b = inputs.gpt2_weights(w, 0, g, dtype)                             # [out][in]
+        dY = inputs.normal(inputs.seed_for(w, 1, 1, g), (T, N), 1.0, dtype)   # [tokens][out]
+        X = inputs.gpt2_activation(w, 0, g, T, dtype)                          # [tokens][in]
+        G = inputs.normal(inputs.seed_for(w, 1, 2, g), (N, K), 0.02, dtype)    # gradient so far
+        d = {k: dev_tensor(torch, a, dtype, dev) for k, a in (("W", W), ("dY", dY), ("X", X), ("G", G))}
+        dx = tlgemm.Plan.create(T, K, N, dtype, dtype, "KN")                 # [T][in] = [T][out]·[out][in]
+        dw = tlgemm.Plan.create(N, K, T, dtype, dtype, "AT_KN", residual=True)  # [out][in] += dYᵀ·X
+        outs = {"dX": torch.empty((T, K), dtype=tlgemm.torch_dtype(dtype), device=dev), "dW": d["G"].clone()}
+        wss = [torch.zeros(max(p.workspace_size, 1), dtype=torch.uint8, device=dev) for p in (dx, dw)]
+        jobs.append((name, dx, dw, d, outs, wss, (dY, W, X, G)))
+
+    def one_pass():
+        for name, dx, dw, d, outs, wss, _ in jobs:
+            dx.run_ptrs(d["dY"].data_ptr(), d["W"].data_ptr(), 0, outs["dX"].data_ptr(),
+                        wss[0].data_ptr() if dx.workspace_size else 0, dx.workspace_size, stream.cuda_stream)
+            dw.run_ptrs(d["dY"].data_ptr(), d["X"].data_ptr(), 0, outs["dW"].data_ptr(),
+                        wss[1].data_ptr() if dw.workspace_size else 0, dw.workspace_size, stream.cuda_stream)
+
+    errs = {}
+    if not no_parity:  # one pass from the initial gradients, sampled against the oracle
+        import oracle
+
+        one_pass()
+        torch.cuda.synchronize()
+        rng = np.random.default_rng(0)
+        tol = 1e-5 if dtype == "f32" else 1e-2
+        for name, dx, dw, d, outs, wss, (dY, W, X, G) in jobs:
+            for key, out, A, B, lay, R in (("dX", outs["dX"], dY, W, "KN", None),
+                                           ("dW", outs["dW"], dY, X, "AT_KN", G)):
+                M, N = out.shape
+                mi, ni = rng.integers(0, M, 1000), rng.integers(0, N, 1000)
+                ref = oracle.linear_points(A, B, None, dtype=dtype, layout=lay, mi=mi, ni=ni, residual=R,
+                                           out_dtype=dtype)
+                y = host_f64(torch, out)
+                errs[f"{name}.{key}"] = float(np.max(np.abs(y[mi, ni] - ref)) / np.max(np.abs(ref)))
+        for name, dx, dw, d, outs, wss, _ in jobs:  # back to the initial gradients for timing
+            outs["dW"].copy_(d["G"])
+    for _ in range(2):
+        one_pass()
+    ms = median_span_ms(torch, one_pass, reps, stream)
+    flops = sum(2 * 2 * T * N * K for _, N, K, _ in inputs.GPT2_LINEARS)
+    return {"workload": f"GPT-2-small backward GEMMs at {T} tokens, one layer: dX = dY.W ([K][N] weight) and "
+                        f"dW += dY^T.X (first operand stored transposed, residual accumulate) for qkv, attn-out, "
+                        f"fc, proj; {dtype}",
+            "pass_ms": round(ms, 4), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2),
+            "frac_mfma_peak": round(flops / (ms * 1e-3) / 1e12 / peak, 4), "flops_per_pass": flops,
+            "parity_err": errs or None,
+            "parity_pass": None if not errs else all(e <= (1e-5 if dtype == "f32" else 1e-2) for e in errs.values()),
+            "plans": [p.describe() for job in jobs for p in (job[1], job[2])],
+            "timing": f"median over {reps} passes of the HIP-event span of one pass (8 launches, one stream); "
+                      "dW accumulates onto itself from pass to pass"}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -501,6 +565,10 @@ def main(argv=None) -> int:
         for dt in ("f32", "bf16"):
             log(f"GPT-2 stack at M=8192, {dt}")
             extra[f"gpt2_stack_m8192_{dt}"] = bench_c5(torch, dev, stream, dt, args.no_parity)
+            torch.cuda.empty_cache()
+        for dt in ("f32", "bf16"):
+            log(f"GPT-2 backward GEMMs at 8192 tokens, {dt}")
+            extra[f"gpt2_backward_t8192_{dt}"] = bench_backward(torch, dev, stream, dt, args.no_parity)
             torch.cuda.empty_cache()
     clocks_after = read_clocks()
 

@@ -78,6 +78,20 @@ template <int DT> __device__ inline float load_elem(const void* p, int64_t idx) 
     return Elem<DT>::to_f32(static_cast<const typename Elem<DT>::storage*>(p)[idx]);
 }
 
+// The inverse of pack16: 16 bytes of stored output as 16 / sizeof(element) fp32 values.
+template <int DT> __device__ inline void unpack16(u32x4 w, float* v) {
+    if constexpr (DT == TLG_F32) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = __uint_as_float(w[u]);
+    } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            v[2 * u] = Elem<DT>::to_f32((uint16_t)(w[u] & 0xffffu));
+            v[2 * u + 1] = Elem<DT>::to_f32((uint16_t)(w[u] >> 16));
+        }
+    }
+}
+
 // ---- fused epilogue ----------------------------------------------------------------
 // Bias first, then the tanh form of GELU, evaluated in fp32.
 // tanh from its exponential identity tanh(u) = 1 - 2 / (e^(2u) + 1), with the
@@ -155,8 +169,10 @@ template <int DT> __device__ inline f32x16 mfma32_16bit(u32x4 a, u32x4 b, f32x16
 // ---- host-side dispatch helpers ----------------------------------------------------
 template <int V> using ic = std::integral_constant<int, V>;
 
+// Only the compile-time part of the flags selects a kernel; the residual is a
+// run-time argument.
 template <class F> inline int with_epi(uint32_t epi, F&& f) {
-    switch (epi) {
+    switch (epi & kEpiKernel) {
     case 0: return f(ic<0>{});
     case TLG_EPI_BIAS: return f(ic<TLG_EPI_BIAS>{});
     case TLG_EPI_GELU_TANH: return f(ic<TLG_EPI_GELU_TANH>{});
@@ -176,8 +192,12 @@ template <class F> inline int with_types(int in_dt, int out_dt, F&& f) {
 }
 
 template <class F> inline int with_layout(int layout, F&& f) {
-    if (layout == TLG_NK) return f(ic<TLG_NK>{});
-    return f(ic<TLG_KN>{});
+    switch (layout) {
+    case TLG_NK: return f(ic<TLG_NK>{});
+    case TLG_KN: return f(ic<TLG_KN>{});
+    case TLG_AT_NK: return f(ic<TLG_AT_NK>{});
+    default: return f(ic<TLG_AT_KN>{});
+    }
 }
 
 int check_launch(const char* what);

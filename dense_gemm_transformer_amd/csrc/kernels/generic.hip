@@ -1,5 +1,5 @@
 // Generic predicated kernel: any M, N, K, any row alignment, every dtype
-// pair, both weight layouts, fused epilogue.  It is the correctness fallback
+// pair, all four operand layouts, fused epilogue and residual.  It is the correctness fallback
 // the planner uses when rows are not 16-byte aligned.
 //
 // Shared-memory block tiling and register tiling as on "Writing a CUDA
@@ -15,7 +15,7 @@ namespace tlg {
 template <int IN, int OUT, int LAYOUT, uint32_t EPI>
 __global__ __launch_bounds__(256) void generic_kernel(const void* __restrict__ X, const void* __restrict__ W,
                                                      const void* __restrict__ bias, void* __restrict__ Y,
-                                                     int M, int N, int K) {
+                                                     int M, int N, int K, int resid) {
     constexpr int BM = kGenericBM, BN = kGenericBN, BK = kGenericBK;
     __shared__ float As[BK][BM + 1];  // [k][m]
     __shared__ float Bs[BK][BN + 1];  // [k][n]
@@ -30,12 +30,13 @@ __global__ __launch_bounds__(256) void generic_kernel(const void* __restrict__ X
             const int e = t + 256 * i;
             const int r = e / BK, kk = e % BK;
             const int m = m0 + r, k = k0 + kk;
-            As[kk][r] = (m < M && k < K) ? load_elem<IN>(X, (int64_t)m * K + k) : 0.0f;
+            const int64_t xi = layout_a_transposed(LAYOUT) ? (int64_t)k * M + m : (int64_t)m * K + k;
+            As[kk][r] = (m < M && k < K) ? load_elem<IN>(X, xi) : 0.0f;
         }
 #pragma unroll
         for (int i = 0; i < (BN * BK) / 256; ++i) {
             const int e = t + 256 * i;
-            if constexpr (LAYOUT == TLG_NK) {
+            if constexpr (!layout_b_kn(LAYOUT)) {
                 const int c = e / BK, kk = e % BK;
                 const int n = n0 + c, k = k0 + kk;
                 Bs[kk][c] = (n < N && k < K) ? load_elem<IN>(W, (int64_t)n * K + k) : 0.0f;
@@ -71,7 +72,9 @@ __global__ __launch_bounds__(256) void generic_kernel(const void* __restrict__ X
             if (n >= N) continue;
             float b = 0.0f;
             if constexpr ((EPI & TLG_EPI_BIAS) != 0) b = load_elem<IN>(bias, n);
-            store_out<OUT>(Y, (int64_t)m * N + n, epilogue<EPI>(acc[i][j], b));
+            float v = epilogue<EPI>(acc[i][j], b);
+            if (resid) v += load_elem<OUT>(Y, (int64_t)m * N + n);
+            store_out<OUT>(Y, (int64_t)m * N + n, v);
         }
     }
 }
@@ -81,12 +84,17 @@ int launch_generic(const tlg_plan& p, const void* X, const void* W, const void* 
     const dim3 grid((unsigned)p.grid_x, (unsigned)p.grid_y, 1);
     return with_types(p.in_dt, p.out_dt, [&](auto in, auto out) {
         return with_layout(p.layout, [&](auto lay) {
-            return with_epi(p.epi, [&](auto epi) {
-                hipLaunchKernelGGL((generic_kernel<decltype(in)::value, decltype(out)::value,
-                                                   decltype(lay)::value, (uint32_t)decltype(epi)::value>),
-                                   grid, dim3(256), 0, stream, X, W, bias, Y, (int)p.M, (int)p.N, (int)p.K);
+            constexpr int L = decltype(lay)::value;
+            auto go = [&](auto epi) {
+                hipLaunchKernelGGL((generic_kernel<decltype(in)::value, decltype(out)::value, L,
+                                                   (uint32_t)decltype(epi)::value>),
+                                   grid, dim3(256), 0, stream, X, W, bias, Y, (int)p.M, (int)p.N, (int)p.K,
+                                   (int)((p.epi & TLG_EPI_RESIDUAL) != 0));
                 return check_launch("generic_kernel");
-            });
+            };
+            // the planner admits no bias or GELU with a transposed first operand
+            if constexpr (layout_a_transposed(L)) return go(ic<0>{});
+            else return with_epi(p.epi, go);
         });
     });
 }

@@ -55,7 +55,7 @@ __global__ __launch_bounds__(64 * NB * KW) void stream_kernel(const void* __rest
                                                              const void* __restrict__ bias,
                                                              void* __restrict__ Yv, float* __restrict__ ws,
                                                              unsigned* __restrict__ tickets, int M, int N,
-                                                             int K, int kper) {
+                                                             int K, int kper, int resid) {
     using S = typename Elem<IN>::storage;
     using G = StreamGeom<IN, NB, KW, LOADS, ROWB>;
     constexpr bool F32 = IN == TLG_F32;
@@ -174,7 +174,11 @@ __global__ __launch_bounds__(64 * NB * KW) void stream_kernel(const void* __rest
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int m = rb * 16 + 4 * g + e;
-                if (m < M && n < N) store_out<OUT>(Y, (int64_t)m * N + n, epilogue<EPI>(acc[rb][e], b));
+                if (m < M && n < N) {
+                    float v = epilogue<EPI>(acc[rb][e], b);
+                    if (resid) v += load_elem<OUT>(Y, (int64_t)m * N + n);
+                    store_out<OUT>(Y, (int64_t)m * N + n, v);
+                }
             }
     } else {
         // Partials in fragment order [split][tile][nb][rb][lane] (one
@@ -215,7 +219,11 @@ __global__ __launch_bounds__(64 * NB * KW) void stream_kernel(const void* __rest
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int m = rb * 16 + 4 * g + e;
-                if (m < M && n < N) store_out<OUT>(Y, (int64_t)m * N + n, epilogue<EPI>(s4[e], b));
+                if (m < M && n < N) {
+                    float v = epilogue<EPI>(s4[e], b);
+                    if (resid) v += load_elem<OUT>(Y, (int64_t)m * N + n);
+                    store_out<OUT>(Y, (int64_t)m * N + n, v);
+                }
             }
         }
         if (t == 0) __hip_atomic_store(&tickets[tid], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -250,7 +258,7 @@ static int launch_stream_cfg(const tlg_plan& p, const void* X, const void* W, co
                     hipLaunchKernelGGL((stream_kernel<I, O, E, NB, KW, LOADS, RB, decltype(ev)::value,
                                                       decltype(sp)::value>),
                                        grid, block, 0, stream, X, W, bias, Y, part, tickets, (int)p.M, (int)p.N,
-                                       (int)p.K, kper);
+                                       (int)p.K, kper, (int)((p.epi & TLG_EPI_RESIDUAL) != 0));
                     return check_launch("stream_kernel");
                 }
             };

@@ -40,19 +40,23 @@ namespace tlg {
 // Waves per SIMD the register allocation must allow: a wave tile of up to
 // 64×64 (64 accumulator registers) leaves room for two waves, up to 32×32 for
 // four, so LDS rather than registers limits how many workgroups share a CU.
-template <int BM, int BN, int WM, int WN>
+// With both 16-bit operands transposed in registers (transposed first operand
+// and [K][N] weight) the staging needs more room: one step less.
+template <int IN, int LAYOUT, int BM, int BN, int WM, int WN>
 constexpr int tiled_occupancy() {
     constexpr int acc = (BM / WM) * (BN / WN) / 64;
-    return acc <= 16 ? 4 : acc <= 64 ? 2 : 1;
+    constexpr int occ = acc <= 16 ? 4 : acc <= 64 ? 2 : 1;
+    constexpr bool two_transposes = IN != TLG_F32 && layout_a_transposed(LAYOUT) && layout_b_kn(LAYOUT);
+    return two_transposes && occ > 1 ? occ / 2 : occ;
 }
 
 template <int IN, int OUT, int LAYOUT, uint32_t EPI, int BM, int BN, int BK, int WM, int WN, bool EVEN,
           bool SPLIT>
-__global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) void tiled_kernel(const void* __restrict__ Xv,
+__global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<IN, LAYOUT, BM, BN, WM, WN>())) void tiled_kernel(const void* __restrict__ Xv,
                                                             const void* __restrict__ Wv,
                                                             const void* __restrict__ bias,
                                                             void* __restrict__ Y, float* __restrict__ ws,
-                                                            int M, int N, int K, int kper) {
+                                                            int M, int N, int K, int kper, int resid) {
     using S = typename Elem<IN>::storage;
     constexpr bool F32 = IN == TLG_F32;
     constexpr int THREADS = 64 * WM * WN;
@@ -60,20 +64,30 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) 
     constexpr int VPR = BK / EPV;         // 16-byte vectors per tile row
     static_assert(BK * (int)sizeof(S) % 64 == 0, "a slice is a multiple of 64 bytes of each operand row");
     constexpr int LDA = BK + EPV;         // padded LDS row (elements)
-    constexpr bool B_NMAJOR = (LAYOUT == TLG_KN) && F32;  // fp32 [K][N] stays n-contiguous
-    constexpr int LDBN = BN + 8;                         // its padded row (floats)
+    constexpr bool KNB = layout_b_kn(LAYOUT);         // weight stored [K][N]
+    constexpr bool AT = layout_a_transposed(LAYOUT);  // first operand stored [K][M]
+    constexpr bool B_NMAJOR = KNB && F32;             // fp32 [K][N] stays n-contiguous
+    constexpr int LDBN = BN + 8;                      // its padded row (floats)
+    constexpr bool A_MMAJOR = AT && F32;              // fp32 [K][M] stays m-contiguous
+    constexpr int LDAM = BM + 8;                      // its padded row (floats)
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int TM = WTM / 32, TN = WTN / 32;
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile is a multiple of 32×32");
-    constexpr int AV = BM * VPR / THREADS;
-    // A 16-bit [K][N] operand is moved as 8×8 blocks (8 rows of k, 8 columns
-    // of n), transposed in registers so LDS receives 16-byte runs of k.
-    constexpr bool B_T16 = (LAYOUT == TLG_KN) && !F32;
-    constexpr int NBK = BK / 8, TBLK = (BK / 8) * (BN / 8);
-    constexpr int BPT = (TBLK + THREADS - 1) / THREADS;  // 8×8 blocks per thread
-    constexpr int BV = B_T16 ? 8 * BPT : (LAYOUT == TLG_NK) ? BN * VPR / THREADS : BK * (BN / EPV) / THREADS;
-    static_assert(AV * THREADS == BM * VPR && BV >= 1, "tile loads divide evenly over the threads");
-    constexpr int A_ELEMS = BM * LDA;
+    // A 16-bit [K][N] weight (or [K][M] first operand) is moved as 8×8 blocks
+    // (8 rows of k, 8 columns of n or m), transposed in registers so LDS
+    // receives 16-byte runs of k.
+    constexpr bool B_T16 = KNB && !F32;
+    constexpr bool A_T16 = AT && !F32;
+    constexpr int NBK = BK / 8;
+    constexpr int TBLK = NBK * (BN / 8), BPT = (TBLK + THREADS - 1) / THREADS;    // weight blocks, per thread
+    constexpr int TBLKA = NBK * (BM / 8), APT = (TBLKA + THREADS - 1) / THREADS;  // A blocks, per thread
+    constexpr int MV = BM / EPV, NV = BN / EPV;  // 16-byte vectors per [K][M] / [K][N] row of the tile
+    constexpr int AV = A_T16 ? 8 * APT : A_MMAJOR ? BK * MV / THREADS : BM * VPR / THREADS;
+    constexpr int BV = B_T16 ? 8 * BPT : !KNB ? BN * VPR / THREADS : BK * NV / THREADS;
+    static_assert(AV >= 1 && BV >= 1, "every thread loads");
+    static_assert(A_T16 || AV * THREADS == (A_MMAJOR ? BK * MV : BM * VPR), "A loads divide evenly");
+    static_assert(B_T16 || BV * THREADS == (KNB ? BK * NV : BN * VPR), "weight loads divide evenly");
+    constexpr int A_ELEMS = A_MMAJOR ? BK * LDAM : BM * LDA;
     constexpr int B_ELEMS = B_NMAJOR ? BK * LDBN : BN * LDA;
 
     // Four LDS arrays (A and B operand, two buffers each): separate objects,
@@ -111,30 +125,43 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) 
 
     // EVEN (exact-fit tiles, every operand region below 2 GiB, checked by the
     // host) loads through buffer descriptors: a uniform base per operand tile
-    // plus one 32-bit lane offset, the per-load offsets uniform.
-    constexpr int NV = BN / EPV;
+    // plus one 32-bit lane offset, the per-load offsets uniform.  Threads past
+    // the last 8×8 block of a transposed operand load the tile's first block
+    // (and drop it): the scalar offset is not range-checked, so an unused lane
+    // must still point inside the operand.
     constexpr int ES = (int)sizeof(S);
-    static_assert(THREADS % VPR == 0 && (!B_T16 || THREADS % NBK == 0) && (!B_NMAJOR || THREADS % NV == 0),
+    static_assert(THREADS % VPR == 0 && (!(A_T16 || B_T16) || THREADS % NBK == 0) &&
+                      (!B_NMAJOR || THREADS % NV == 0) && (!A_MMAJOR || THREADS % MV == 0),
                   "each thread's loads share one lane offset");
-    const uint32_t a_lane = (uint32_t)(((t / VPR) * K + (t % VPR) * EPV) * ES);
-    const uint32_t b_lane = LAYOUT == TLG_NK ? (uint32_t)(((t / VPR) * K + (t % VPR) * EPV) * ES)
-                            : B_T16        ? (uint32_t)(((t % NBK) * 8 * N + (t / NBK) * 8) * ES)
-                                           : (uint32_t)(((t / NV) * N + (t % NV) * EPV) * ES);
+    static_assert(!EVEN || ((!A_T16 || APT == 1) && (!B_T16 || BPT == 1)), "one 8×8 block per thread");
+    const int ta = (TBLKA % THREADS == 0 || t < TBLKA) ? t : 0;
+    const int tb = (TBLK % THREADS == 0 || t < TBLK) ? t : 0;
+    const uint32_t a_lane = A_T16      ? (uint32_t)(((ta % NBK) * 8 * M + (ta / NBK) * 8) * ES)
+                            : A_MMAJOR ? (uint32_t)(((t / MV) * M + (t % MV) * EPV) * ES)
+                                       : (uint32_t)(((t / VPR) * K + (t % VPR) * EPV) * ES);
+    const uint32_t b_lane = !KNB  ? (uint32_t)(((t / VPR) * K + (t % VPR) * EPV) * ES)
+                            : B_T16 ? (uint32_t)(((tb % NBK) * 8 * N + (tb / NBK) * 8) * ES)
+                                    : (uint32_t)(((t / NV) * N + (t % NV) * EPV) * ES);
     i32x4 rsrc_a = {0, 0, 0, 0}, rsrc_b = {0, 0, 0, 0};
     if constexpr (EVEN) {
-        rsrc_a = buffer_rsrc(X + (int64_t)m0 * K, (int64_t)BM * K * ES);
-        rsrc_b = LAYOUT == TLG_NK ? buffer_rsrc(W + (int64_t)n0 * K, (int64_t)BN * K * ES)
-                                  : buffer_rsrc(W + n0, ((int64_t)K * N - n0) * ES);
+        rsrc_a = AT ? buffer_rsrc(X + m0, ((int64_t)K * M - m0) * ES) : buffer_rsrc(X + (int64_t)m0 * K, (int64_t)BM * K * ES);
+        rsrc_b = KNB ? buffer_rsrc(W + n0, ((int64_t)K * N - n0) * ES) : buffer_rsrc(W + (int64_t)n0 * K, (int64_t)BN * K * ES);
     }
     auto gload = [&](int s, u32x4 (&ra)[AV], u32x4 (&rbv)[BV]) {
         const int k0 = kbeg + s * BK;
         if constexpr (EVEN) {
 #pragma unroll
-            for (int i = 0; i < AV; ++i)
-                ra[i] = buffer_load16(rsrc_a, a_lane, (k0 + i * (THREADS / VPR) * K) * ES, 0);
+            for (int i = 0; i < AV; ++i) {
+                if constexpr (A_T16)  // row i of the thread's 8×8 block
+                    ra[i] = buffer_load16(rsrc_a, a_lane, (k0 + i) * M * ES, 0);
+                else if constexpr (A_MMAJOR)
+                    ra[i] = buffer_load16(rsrc_a, a_lane, (k0 + i * (THREADS / MV)) * M * ES, 0);
+                else
+                    ra[i] = buffer_load16(rsrc_a, a_lane, (k0 + i * (THREADS / VPR) * K) * ES, 0);
+            }
 #pragma unroll
             for (int i = 0; i < BV; ++i) {
-                if constexpr (LAYOUT == TLG_NK)
+                if constexpr (!KNB)
                     rbv[i] = buffer_load16(rsrc_b, b_lane, (k0 + i * (THREADS / VPR) * K) * ES, 0);
                 else if constexpr (B_T16)  // block row i % 8 of block column group i / 8
                     rbv[i] = buffer_load16(rsrc_b, b_lane, ((k0 + i % 8) * N + (i / 8) * (THREADS / NBK) * 8) * ES, 0);
@@ -143,20 +170,42 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) 
             }
             return;
         }
+        // Ragged tiles: out-of-range rows and columns are clamped to valid
+        // ones (their outputs are never stored), K past the range loads zeros.
 #pragma unroll
         for (int i = 0; i < AV; ++i) {
             const int v = t + THREADS * i;
-            const int row = v / VPR, k = k0 + (v % VPR) * EPV;
-            const int m = EVEN ? m0 + row : min(m0 + row, M - 1);
-            if (EVEN || k < kend)
-                ra[i] = ldg16(X + (int64_t)m * K + k);
-            else
-                ra[i] = u32x4{0u, 0u, 0u, 0u};
+            if constexpr (A_T16) {
+                // block q = t + THREADS*(i/8), row i%8 of it: k = kc*8 + i%8, m = mb*8..+7
+                const int q = t + THREADS * (i / 8);
+                const int kc = q % NBK, mb = q / NBK;
+                const int k = k0 + kc * 8 + (i % 8);
+                const int m = min(m0 + mb * 8, M - 8);
+                if ((TBLKA % THREADS == 0 || q < TBLKA) && k < kend)
+                    ra[i] = ldg16(X + (int64_t)k * M + m);
+                else
+                    ra[i] = u32x4{0u, 0u, 0u, 0u};
+            } else if constexpr (A_MMAJOR) {
+                const int kr = v / MV, mv = v % MV;
+                const int k = k0 + kr;
+                const int m = min(m0 + mv * EPV, M - EPV);
+                if (k < kend)
+                    ra[i] = ldg16(X + (int64_t)k * M + m);
+                else
+                    ra[i] = u32x4{0u, 0u, 0u, 0u};
+            } else {
+                const int row = v / VPR, k = k0 + (v % VPR) * EPV;
+                const int m = min(m0 + row, M - 1);
+                if (k < kend)
+                    ra[i] = ldg16(X + (int64_t)m * K + k);
+                else
+                    ra[i] = u32x4{0u, 0u, 0u, 0u};
+            }
         }
 #pragma unroll
         for (int i = 0; i < BV; ++i) {
             const int v = t + THREADS * i;
-            if constexpr (LAYOUT == TLG_NK) {
+            if constexpr (!KNB) {
                 const int row = v / VPR, k = k0 + (v % VPR) * EPV;
                 const int n = EVEN ? n0 + row : min(n0 + row, N - 1);
                 if (EVEN || k < kend)
@@ -184,40 +233,53 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) 
             }
         }
     };
+    // Transpose one 8×8 block (rows i0..i0+7 of `rows`: 8 values of k each
+    // along m or n) into LDS rows that run along k: column c gathers half c of
+    // rows 0..7, packed two rows per dword (v_perm), then one 16-byte store per
+    // column.  Eight consecutive lanes write one row's eight 16-byte runs; the
+    // next eight lanes write a row 8 below (288 dwords on: the other 32 banks),
+    // so the stores are conflict-free.
+    auto store_t8 = [&](S* dst, const auto& rows, int i0, int q) {
+        const int kc = q % NBK, cb = q / NBK;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+            u32x4 col;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                col[j] = __builtin_amdgcn_perm(rows[i0 + 2 * j + 1][c >> 1], rows[i0 + 2 * j][c >> 1], sel);
+            *reinterpret_cast<u32x4*>(dst + (cb * 8 + c) * LDA + kc * 8) = col;
+        }
+    };
     auto lstore = [&](int buf, const u32x4 (&ra)[AV], const u32x4 (&rbv)[BV]) {
         S* As = buf ? lds_a1 : lds_a0;
         S* Bs = buf ? lds_b1 : lds_b0;
 #pragma unroll
         for (int i = 0; i < AV; ++i) {
             const int v = t + THREADS * i;
-            *reinterpret_cast<u32x4*>(As + (v / VPR) * LDA + (v % VPR) * EPV) = ra[i];
+            if constexpr (A_T16) {
+                if (i % 8 != 0) continue;
+                const int q = t + THREADS * (i / 8);
+                if (TBLKA % THREADS != 0 && q >= TBLKA) continue;
+                store_t8(As, ra, i, q);
+            } else if constexpr (A_MMAJOR) {
+                *reinterpret_cast<u32x4*>(As + (v / MV) * LDAM + (v % MV) * EPV) = ra[i];
+            } else {
+                *reinterpret_cast<u32x4*>(As + (v / VPR) * LDA + (v % VPR) * EPV) = ra[i];
+            }
         }
 #pragma unroll
         for (int i = 0; i < BV; ++i) {
             const int v = t + THREADS * i;
-            if constexpr (LAYOUT == TLG_NK) {
+            if constexpr (!KNB) {
                 *reinterpret_cast<u32x4*>(Bs + (v / VPR) * LDA + (v % VPR) * EPV) = rbv[i];
             } else if constexpr (B_NMAJOR) {
                 *reinterpret_cast<u32x4*>(Bs + (v / NV) * LDBN + (v % NV) * EPV) = rbv[i];
             } else {
-                // Transpose one 8×8 block: column c gathers half c of rows
-                // 0..7, packed two rows per dword (v_perm), then one 16-byte
-                // store per column.  Eight consecutive lanes write one row's
-                // eight 16-byte runs; the next eight lanes write a row 8 below
-                // (288 dwords on: the other 32 banks), so stores are conflict-free.
                 if (i % 8 != 0) continue;
                 const int q = t + THREADS * (i / 8);
                 if (TBLK % THREADS != 0 && q >= TBLK) continue;
-                const int kc = q % NBK, nb = q / NBK;
-#pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-                    u32x4 col;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        col[j] = __builtin_amdgcn_perm(rbv[i + 2 * j + 1][c >> 1], rbv[i + 2 * j][c >> 1], sel);
-                    *reinterpret_cast<u32x4*>(Bs + (nb * 8 + c) * LDA + kc * 8) = col;
-                }
+                store_t8(Bs, rbv, i, q);
             }
         }
     };
@@ -239,8 +301,15 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) 
             for (int kq = 0; kq < BK / 8; ++kq) {
                 f32x4 a[TM], b[TN];
 #pragma unroll
-                for (int i = 0; i < TM; ++i)
-                    a[i] = *reinterpret_cast<const f32x4*>(As + (wm0 + i * 32 + r) * LDA + kq * 8 + 4 * g);
+                for (int i = 0; i < TM; ++i) {
+                    if constexpr (A_MMAJOR) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            a[i][e] = As[(kq * 8 + 4 * g + e) * LDAM + wm0 + i * 32 + r];
+                    } else {
+                        a[i] = *reinterpret_cast<const f32x4*>(As + (wm0 + i * 32 + r) * LDA + kq * 8 + 4 * g);
+                    }
+                }
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
                     if constexpr (B_NMAJOR) {
@@ -296,7 +365,7 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) 
     // splits it at the middle k-step (measured: 2803 vs 3809 cycles per
     // 256×256×64 bf16 slice, 8481 vs 8564 per 256×256×16 fp32 slice).
     constexpr int NKQ = F32 ? BK / 8 : BK / 16;
-    constexpr int FR = F32 ? TM + (B_NMAJOR ? 4 : 1) * TN : TM + TN;
+    constexpr int FR = F32 ? (A_MMAJOR ? 4 : 1) * TM + (B_NMAJOR ? 4 : 1) * TN : TM + TN;
     constexpr int NMF = F32 ? NKQ * 4 * TM * TN : NKQ * TM * TN;
     constexpr int MPK = NMF / NKQ, HALF = NMF / 2;
     constexpr int NVM = AV + BV, NDW = AV + BV;
@@ -309,7 +378,8 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) 
         if (m / MPK < NKQ - 1 && (m % MPK) % SR == 0 && (m % MPK) / SR < FR)
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // next k-step's operand read
         if (stores && m >= HALF && (m - HALF) % SW == 0 && (m - HALF) / SW < NDW) {
-            if (B_T16 && (m - HALF) / SW >= AV) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            const int w = (m - HALF) / SW;  // LDS stores: A's first, then the weight's
+            if ((A_T16 && w < AV) || (B_T16 && w >= AV)) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
             __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
         }
     };
@@ -394,24 +464,36 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) 
 
     // ---- epilogue: a 32×32 accumulator holds column (lane % 32) and rows
     // 8*(e/4) + 4*(lane/32) + e%4 for register e.
-    if constexpr (EVEN) {
-        // Exact-fit tiles leave through LDS: each wave stages 16 rows × WTN of
-        // its tile (fp32, row stride WTN+8 floats, so the two half-waves'
-        // writes land on disjoint banks), then every lane takes whole 16-byte
-        // runs of one row, applies bias and GELU, converts and stores them:
-        // full-line writes and one store per 16 bytes instead of one per element.
-        // Two waves share each A-operand array, free once every wave is past
-        // its last multiply.
-        constexpr int SW = WTN + 8;
-        constexpr int STG = 16 * SW;
-        static_assert(2 * STG * 4 <= A_ELEMS * (int)sizeof(S), "staging fits in the A-operand buffers");
+    // Exact-fit tiles leave through LDS: each wave stages 16 rows × WTN of its
+    // tile (fp32, row stride WTN+8 floats, so the two half-waves' writes land
+    // on disjoint banks), then every lane takes whole 16-byte runs of one row,
+    // applies bias, GELU and the residual, converts and stores them: full-line
+    // writes and one store per 16 bytes instead of one per element.  The
+    // operand buffers are free once every wave is past its last multiply: two
+    // waves share each A array where it is large enough, else each wave takes
+    // one of the four arrays; where neither fits, the per-element path below.
+    constexpr int SROW = WTN + 8;  // staged row stride (floats)
+    constexpr int STG = 16 * SROW;
+    constexpr int STAGE = 2 * STG * 4 <= A_ELEMS * (int)sizeof(S) ? 2
+                          : (WM * WN == 4 && STG * 4 <= A_ELEMS * (int)sizeof(S) &&
+                             STG * 4 <= B_ELEMS * (int)sizeof(S))
+                              ? 1
+                              : 0;
+    if constexpr (EVEN && STAGE > 0) {
         constexpr int OB = SPLIT ? 4 : (OUT == TLG_F32 ? 4 : 2);  // bytes per written element
         constexpr int EPC = 16 / OB;                               // elements per 16-byte store
         constexpr int CPR = WTN / EPC;                             // 16-byte runs per staged row
         static_assert(64 % CPR == 0 && (16 * CPR) % 64 == 0, "runs divide evenly over the lanes");
         __syncthreads();
-        float* stg = reinterpret_cast<float*>((wave >> 1) ? lds_a1 : lds_a0) + (wave & 1) * STG;
-        const int col = (lane % CPR) * EPC;  // the same columns for every run of this lane
+        float* stg = STAGE == 2 ? reinterpret_cast<float*>((wave >> 1) ? lds_a1 : lds_a0) + (wave & 1) * STG
+                     : reinterpret_cast<float*>(wave == 0 ? lds_a0 : wave == 1 ? lds_a1 : wave == 2 ? lds_b0 : lds_b1);
+        // Opaque copy of the lane index: everything the epilogue derives from
+        // it is computed here, after the loop, instead of being hoisted in
+        // front of it and held in registers through it (which spilled the
+        // 256×256 bf16 loop once the residual read was added).
+        int el = lane;
+        asm volatile("" : "+v"(el));
+        const int col = (el % CPR) * EPC;  // the same columns for every run of this lane
         const int ncol = n0 + wn0 + col;
         float bcol[EPC];
 #pragma unroll
@@ -427,13 +509,13 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) 
                 for (int j = 0; j < TN; ++j)
 #pragma unroll
                     for (int e = 8 * h; e < 8 * h + 8; ++e)
-                        stg[(8 * ((e >> 2) & 1) + 4 * g + (e & 3)) * SW + j * 32 + r] = acc[i][j][e];
+                        stg[(8 * ((e >> 2) & 1) + 4 * g + (e & 3)) * SROW + j * 32 + r] = acc[i][j][e];
                 // LDS operations of one wave complete in order: the reads
                 // below see these writes, and the next half's writes follow them.
 #pragma unroll
                 for (int q = 0; q < (16 * CPR) / 64; ++q) {
-                    const int row = (lane + 64 * q) / CPR;
-                    const float* src = stg + row * SW + col;
+                    const int row = (el + 64 * q) / CPR;
+                    const float* src = stg + row * SROW + col;
                     float v[EPC];
 #pragma unroll
                     for (int u = 0; u < EPC; u += 4) {
@@ -449,8 +531,15 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) 
                     } else {
 #pragma unroll
                         for (int u = 0; u < EPC; ++u) v[u] = epilogue<EPI>(v[u], bcol[u]);
+                        u32x4* dst = reinterpret_cast<u32x4*>(static_cast<char*>(Y) + (m * N + ncol) * OB);
+                        if (resid) {
+                            float rv[EPC];
+                            unpack16<OUT>(*dst, rv);
+#pragma unroll
+                            for (int u = 0; u < EPC; ++u) v[u] += rv[u];
+                        }
                         out = pack16<OUT>(v);
-                        *reinterpret_cast<u32x4*>(static_cast<char*>(Y) + (m * N + ncol) * OB) = out;
+                        *dst = out;
                     }
                 }
             }
@@ -469,10 +558,13 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) 
             for (int e = 0; e < 16; ++e) {
                 const int m = m0 + wm0 + i * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
                 if (m >= M || n >= N) continue;
-                if constexpr (SPLIT)
+                if constexpr (SPLIT) {
                     ws[((int64_t)z * M + m) * N + n] = acc[i][j][e];
-                else
-                    store_out<OUT>(Y, (int64_t)m * N + n, epilogue<EPI>(acc[i][j][e], b));
+                } else {
+                    float v = epilogue<EPI>(acc[i][j][e], b);
+                    if (resid) v += load_elem<OUT>(Y, (int64_t)m * N + n);
+                    store_out<OUT>(Y, (int64_t)m * N + n, v);
+                }
             }
         }
     }
@@ -482,7 +574,7 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) 
 template <int IN, int OUT, uint32_t EPI>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws, int splits,
                                                            const void* __restrict__ bias,
-                                                           void* __restrict__ Y, int64_t MN, int N) {
+                                                           void* __restrict__ Y, int64_t MN, int N, int resid) {
     const int64_t base = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (base >= MN) return;
     // Every split's values in flight at once (in groups of 8), then the sum in split order.
@@ -506,7 +598,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
         if (idx >= MN) return;
         float b = 0.0f;
         if constexpr ((EPI & TLG_EPI_BIAS) != 0) b = load_elem<IN>(bias, idx % N);
-        store_out<OUT>(Y, idx, epilogue<EPI>(s[e], b));
+        float y = epilogue<EPI>(s[e], b);
+        if (resid) y += load_elem<OUT>(Y, idx);
+        store_out<OUT>(Y, idx, y);
     }
 }
 
@@ -516,18 +610,20 @@ static int launch_tiled_cfg(const tlg_plan& p, const void* X, const void* W, con
     const int S = p.split;
     const int kper = (int)(ceil_div(ceil_div(p.K, S), BK) * BK);
     const int64_t es = I == TLG_F32 ? 4 : 2;
-    const bool fits32 = (int64_t)BM * p.K * es < INT32_MAX &&
-                        (L == TLG_NK ? (int64_t)BN * p.K * es : p.K * p.N * es) < INT32_MAX;
+    // exact-fit tiles address each operand through a 32-bit buffer range
+    const bool fits32 = (layout_a_transposed(L) ? p.K * p.M * es : (int64_t)BM * p.K * es) < INT32_MAX &&
+                        (layout_b_kn(L) ? p.K * p.N * es : (int64_t)BN * p.K * es) < INT32_MAX;
+    const int resid = (p.epi & TLG_EPI_RESIDUAL) != 0;
     const bool even = p.M % BM == 0 && p.N % BN == 0 && (int64_t)kper * S == p.K && fits32;
     const dim3 grid((unsigned)(p.grid_x * p.grid_y), (unsigned)S), block(64 * WM * WN);
     auto go = [&](auto ev, auto sp) {
         hipLaunchKernelGGL((tiled_kernel<I, O, L, E, BM, BN, BK, WM, WN, decltype(ev)::value, decltype(sp)::value>),
-                           grid, block, 0, stream, X, W, bias, Y, ws, (int)p.M, (int)p.N, (int)p.K, kper);
+                           grid, block, 0, stream, X, W, bias, Y, ws, (int)p.M, (int)p.N, (int)p.K, kper, resid);
         return check_launch("tiled_kernel");
     };
     auto go_split = [&](auto ev) {
         hipLaunchKernelGGL((tiled_kernel<I, TLG_F32, L, 0u, BM, BN, BK, WM, WN, decltype(ev)::value, true>), grid,
-                           block, 0, stream, X, W, nullptr, nullptr, ws, (int)p.M, (int)p.N, (int)p.K, kper);
+                           block, 0, stream, X, W, nullptr, nullptr, ws, (int)p.M, (int)p.N, (int)p.K, kper, 0);
         return check_launch("tiled_kernel");
     };
     int rc;
@@ -538,7 +634,7 @@ static int launch_tiled_cfg(const tlg_plan& p, const void* X, const void* W, con
     if (rc != TLG_OK || S == 1) return rc;
     const int64_t MN = p.M * p.N;
     hipLaunchKernelGGL((splitk_reduce_kernel<I, O, E>), dim3((unsigned)ceil_div(MN, 1024)), dim3(256), 0, stream,
-                       (const float*)ws, S, bias, Y, MN, (int)p.N);
+                       (const float*)ws, S, bias, Y, MN, (int)p.N, resid);
     return check_launch("splitk_reduce_kernel");
 }
 
@@ -556,7 +652,7 @@ int launch_tiled_in(const tlg_plan& p, const void* X, const void* W, const void*
     };
     return with_out([&](auto out) {
         return with_layout(p.layout, [&](auto lay) {
-            return with_epi(p.epi, [&](auto epi) {
+            auto by_epi = [&](auto epi) {
                 constexpr int O = decltype(out)::value, L = decltype(lay)::value;
                 constexpr uint32_t E = (uint32_t)decltype(epi)::value;
                 constexpr const TileCfg* T = I == TLG_F32 ? kTiledF32 : kTiled16;
@@ -575,7 +671,10 @@ int launch_tiled_in(const tlg_plan& p, const void* X, const void* W, const void*
                 default: set_error("bad tiled tile"); return (int)TLG_ERR_INVALID_ARG;
                 }
 #undef TLG_TILED_CASE
-            });
+            };
+            // the planner admits no bias or GELU with a transposed first operand
+            if constexpr (layout_a_transposed(decltype(lay)::value)) return by_epi(ic<0>{});
+            else return with_epi(p.epi, by_epi);
         });
     });
 }

@@ -60,10 +60,12 @@ static bool valid_pair(int in_dt, int out_dt) {
 
 // Rows of X and of the weight must start on 16-byte boundaries for the
 // vectorised kernels (every row start is then aligned when the base is).
+// X rows hold K elements, or M for the transposed-A layouts; weight rows K
+// (out×in) or N ([K][N]).
 static bool rows_aligned16(const tlg_plan& p) {
     const int64_t isz = dtype_size(p.in_dt);
-    if ((p.K * isz) % 16) return false;
-    if (p.layout == TLG_KN && (p.N * isz) % 16) return false;
+    if (((layout_a_transposed(p.layout) ? p.M : p.K) * isz) % 16) return false;
+    if (((layout_b_kn(p.layout) ? p.N : p.K) * isz) % 16) return false;
     return true;
 }
 
@@ -167,8 +169,8 @@ static int auto_stream(tlg_plan& p) {
 
 static int fill_tiled(tlg_plan& p, int tile, int split) {
     if (!rows_aligned16(p)) {
-        set_error("tiled kernel needs 16-byte aligned rows (K%s * elem_size %% 16 == 0)",
-                  p.layout == TLG_KN ? " and N" : "");
+        set_error("tiled kernel needs 16-byte aligned rows (%s and %s times elem_size a multiple of 16)",
+                  layout_a_transposed(p.layout) ? "M" : "K", layout_b_kn(p.layout) ? "N" : "K");
         return TLG_ERR_UNSUPPORTED;
     }
     if (tile < 0 || tile >= tiled_count(p.in_dt)) {
@@ -252,13 +254,17 @@ int gemm_plan_ex(tlg_plan_t* out, int64_t M, int64_t N, int64_t K, tlg_dtype in_
         set_error("gemm_plan: unknown dtype (%d, %d)", (int)in_dt, (int)out_dt);
         return TLG_ERR_INVALID_ARG;
     }
-    if (layout != TLG_NK && layout != TLG_KN) {
+    if ((int)layout < TLG_NK || (int)layout > TLG_AT_KN) {
         set_error("gemm_plan: unknown layout %d", (int)layout);
         return TLG_ERR_INVALID_ARG;
     }
-    if (epi_flags & ~(uint32_t)(TLG_EPI_BIAS | TLG_EPI_GELU_TANH)) {
+    if (epi_flags & ~(uint32_t)(TLG_EPI_BIAS | TLG_EPI_GELU_TANH | TLG_EPI_RESIDUAL)) {
         set_error("gemm_plan: unknown epilogue flags 0x%x", epi_flags);
         return TLG_ERR_INVALID_ARG;
+    }
+    if (layout_a_transposed(layout) && (epi_flags & (TLG_EPI_BIAS | TLG_EPI_GELU_TANH))) {
+        set_error("gemm_plan: the transposed-A layouts take no bias or GELU (only TLG_EPI_RESIDUAL)");
+        return TLG_ERR_UNSUPPORTED;
     }
     if (!valid_pair(in_dt, out_dt)) {
         set_error("gemm_plan: unsupported (in, out) dtype pair (%d, %d)", (int)in_dt, (int)out_dt);
@@ -284,7 +290,7 @@ int gemm_plan_ex(tlg_plan_t* out, int64_t M, int64_t N, int64_t K, tlg_dtype in_
     int rc;
     if (variant == TLG_VARIANT_AUTO) {
         const TableRow* row = (split == 0 && tile_sel == 0)
-                                  ? table_lookup(M, N, K, in_dt, out_dt, layout, epi_flags)
+                                  ? table_lookup(M, N, K, in_dt, out_dt, layout, epi_flags & kEpiKernel)
                                   : nullptr;
         if (row) {
             rc = row->variant == TLG_VARIANT_STREAM  ? fill_stream(p, row->tile, row->split)
@@ -361,14 +367,15 @@ int gemm_plan_describe(tlg_plan_t p, char* buf, size_t n) {
     }
     static const char* vname[] = {"generic", "stream", "tiled"};
     static const char* dname[] = {"f32", "f16", "bf16"};
+    static const char* lname[] = {"NK", "KN", "AT_NK", "AT_KN"};
     char tmp[320];
     int len = snprintf(tmp, sizeof tmp,
-                       "variant=%s M=%lld N=%lld K=%lld in=%s out=%s layout=%s epi=%s%s tile=%dx%dx%d "
+                       "variant=%s M=%lld N=%lld K=%lld in=%s out=%s layout=%s epi=%s%s%s tile=%dx%dx%d "
                        "split=%d threads=%d grid=%lldx%lldx%lld launches=%d ws=%zu",
                        vname[p->variant], (long long)p->M, (long long)p->N, (long long)p->K,
-                       dname[p->in_dt], dname[p->out_dt], p->layout == TLG_NK ? "NK" : "KN",
-                       (p->epi & TLG_EPI_BIAS) ? "bias" : "none",
-                       (p->epi & TLG_EPI_GELU_TANH) ? "+gelu" : "", p->bm, p->bn, p->bk, p->split,
+                       dname[p->in_dt], dname[p->out_dt], lname[p->layout],
+                       (p->epi & TLG_EPI_BIAS) ? "bias" : "none", (p->epi & TLG_EPI_GELU_TANH) ? "+gelu" : "",
+                       (p->epi & TLG_EPI_RESIDUAL) ? "+res" : "", p->bm, p->bn, p->bk, p->split,
                        p->threads, (long long)p->grid_x, (long long)p->grid_y, (long long)p->grid_z,
                        p->launches, p->ws_bytes);
     if (buf && n) {

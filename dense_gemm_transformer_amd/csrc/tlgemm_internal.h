@@ -17,6 +17,15 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 inline int dtype_size(int dt) { return dt == TLG_F32 ? 4 : 2; }
 
+// Layout bits: the weight is [K][N] (TLG_KN, TLG_AT_KN); the first operand is
+// stored transposed, [K][M] (TLG_AT_NK, TLG_AT_KN).
+constexpr bool layout_b_kn(int layout) { return (layout & 1) != 0; }
+constexpr bool layout_a_transposed(int layout) { return layout >= TLG_AT_NK; }
+
+// Epilogue flags that select a kernel at compile time; TLG_EPI_RESIDUAL is a
+// run-time argument of the same kernels (one read of Y per output element).
+constexpr uint32_t kEpiKernel = TLG_EPI_BIAS | TLG_EPI_GELU_TANH;
+
 // One entry of a variant's tile list.
 struct TileCfg {
     int bm, bn, bk;  // workgroup tile (rows of Y, columns of Y, K per pipeline stage)

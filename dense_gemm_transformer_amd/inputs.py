@@ -94,8 +94,10 @@ def uniform(seed: int, shape, lo: float, hi: float, dtype: str) -> np.ndarray:
 class LinearCase:
     """One linear layer's inputs in storage form.
 
-    ``W`` is out×in ``[N][K]`` for layout ``"NK"`` and ``[K][N]`` for ``"KN"``.
-    ``b`` is ``None`` when the layer has no bias.
+    ``X`` is ``[M][K]``, or ``[K][M]`` for the ``"AT_*"`` layouts.  ``W`` is
+    out×in ``[N][K]`` for ``"NK"``/``"AT_NK"`` and ``[K][N]`` for
+    ``"KN"``/``"AT_KN"``.  ``b`` is ``None`` when the layer has no bias; ``R``,
+    when given, is the residual ``[M][N]`` (output type) the result is added to.
     """
 
     name: str
@@ -110,6 +112,7 @@ class LinearCase:
     X: np.ndarray
     W: np.ndarray
     b: np.ndarray | None
+    R: np.ndarray | None = None
 
     @property
     def flops(self) -> int:
@@ -191,14 +194,19 @@ def workload_gpt2_stack(workload: int = 5, batch: int = 64, seq: int = 128, laye
     return out
 
 
+TENSOR_R = 4  # residual, in random_case
+
+
 def random_case(seed: int, M: int, N: int, K: int, in_dtype: str = "f32", out_dtype: str | None = None,
                 layout: str = "NK", bias: bool = False, gelu: bool = False,
-                x_scale: float = 1.0, w_scale: float = 0.05) -> LinearCase:
-    """A generic seeded case for parity tests of arbitrary shapes."""
+                x_scale: float = 1.0, w_scale: float = 0.05, residual: bool = False) -> LinearCase:
+    """A generic seeded case for parity tests of arbitrary shapes and all four layouts."""
     out_dtype = out_dtype or in_dtype
-    X = normal(seed * 16 + TENSOR_X, (M, K), x_scale, in_dtype)
-    wshape = (N, K) if layout == "NK" else (K, N)
+    xshape = (K, M) if layout.startswith("AT_") else (M, K)
+    X = normal(seed * 16 + TENSOR_X, xshape, x_scale, in_dtype)
+    wshape = (K, N) if layout.endswith("KN") else (N, K)
     W = normal(seed * 16 + TENSOR_W, wshape, w_scale, in_dtype)
     b = normal(seed * 16 + TENSOR_B, (N,), w_scale, in_dtype) if bias else None
-    return LinearCase(f"rand_{M}x{N}x{K}_{in_dtype}_{layout}", M, N, K, in_dtype, out_dtype,
-                      layout, bias, gelu, X, W, b)
+    R = normal(seed * 16 + TENSOR_R, (M, N), 1.0, out_dtype) if residual else None
+    return LinearCase(f"rand_{M}x{N}x{K}_{in_dtype}_{layout}{'_res' if residual else ''}", M, N, K, in_dtype,
+                      out_dtype, layout, bias, gelu, X, W, b, R)

@@ -24,8 +24,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libtlgemm.so")
 
 F32, F16, BF16 = 0, 1, 2
-NK, KN = 0, 1
-EPI_BIAS, EPI_GELU_TANH = 1, 2
+NK, KN, AT_NK, AT_KN = 0, 1, 2, 3
+EPI_BIAS, EPI_GELU_TANH, EPI_RESIDUAL = 1, 2, 4
 VARIANT_AUTO, VARIANT_GENERIC, VARIANT_STREAM, VARIANT_TILED = -1, 0, 1, 2
 VARIANT_NAMES = {VARIANT_GENERIC: "generic", VARIANT_STREAM: "stream", VARIANT_TILED: "tiled"}
 
@@ -33,7 +33,7 @@ OK = 0
 ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_WORKSPACE, ERR_NOMEM, ERR_LAUNCH = -1, -2, -3, -4, -5, -6
 
 DTYPE_CODES = {"f32": F32, "f16": F16, "bf16": BF16}
-LAYOUT_CODES = {"NK": NK, "KN": KN}
+LAYOUT_CODES = {"NK": NK, "KN": KN, "AT_NK": AT_NK, "AT_KN": AT_KN}
 
 # Every symbol include/tlgemm.h declares.
 EXPORTS = ("gemm_plan", "gemm_plan_ex", "gemm_workspace_size", "gemm_plan_info", "gemm_run",
@@ -173,9 +173,9 @@ class Plan:
 
     @classmethod
     def create(cls, M, N, K, in_dtype="f32", out_dtype=None, layout="NK", bias=False, gelu=False,
-               variant=VARIANT_AUTO, split_k=0, tile=0) -> "Plan":
+               variant=VARIANT_AUTO, split_k=0, tile=0, residual=False) -> "Plan":
         out_dtype = in_dtype if out_dtype is None else out_dtype
-        epi = (EPI_BIAS if bias else 0) | (EPI_GELU_TANH if gelu else 0)
+        epi = (EPI_BIAS if bias else 0) | (EPI_GELU_TANH if gelu else 0) | (EPI_RESIDUAL if residual else 0)
         h = gemm_plan_ex(M, N, K, in_dtype, out_dtype, layout, epi, variant, split_k, tile)
         return cls(h, M, N, K, in_dtype, out_dtype, layout, epi)
 
@@ -220,9 +220,14 @@ def torch_dtype(name: str):
 
 
 def run(plan: Plan, X, W, bias=None, Y=None, workspace=None, stream=None):
-    """Run ``plan`` on torch device tensors; allocates Y (and workspace) if not given."""
+    """Run ``plan`` on torch device tensors; allocates Y (and workspace) if not given.
+
+    With a residual plan Y is required: it holds the residual and receives the result.
+    """
     import torch
 
+    if plan.epi_flags & EPI_RESIDUAL and Y is None:
+        raise ValueError("a residual plan reads Y: pass the residual tensor as Y")
     if Y is None:
         Y = torch.empty((plan.M, plan.N), dtype=torch_dtype(plan.out_dtype), device=X.device)
     need = plan.workspace_size
@@ -238,13 +243,18 @@ def run(plan: Plan, X, W, bias=None, Y=None, workspace=None, stream=None):
 
 
 def linear(X, W, bias=None, *, gelu=False, layout="NK", out_dtype=None, variant=VARIANT_AUTO, split_k=0,
-           tile=0):
-    """Y = act(X·Wᵀ + bias) for torch device tensors (W out×in for ``layout="NK"``)."""
-    M, K = X.shape
-    N = W.shape[0] if layout == "NK" else W.shape[1]
+           tile=0, residual=None):
+    """Y = act(X·Wᵀ + bias) (+ residual) for torch device tensors.
+
+    W is out×in for ``layout="NK"``; the ``AT_*`` layouts take X stored [K][M].
+    ``residual`` ([M][N], the output dtype) is updated in place and returned.
+    """
+    M, K = (X.shape[1], X.shape[0]) if layout.startswith("AT_") else (X.shape[0], X.shape[1])
+    N = W.shape[1] if layout.endswith("KN") else W.shape[0]
     in_dt = _torch_dtype_name(X)
-    plan = Plan.create(M, N, K, in_dt, out_dtype or in_dt, layout, bias is not None, gelu, variant, split_k, tile)
+    plan = Plan.create(M, N, K, in_dt, out_dtype or in_dt, layout, bias is not None, gelu, variant, split_k, tile,
+                       residual is not None)
     try:
-        return run(plan, X, W, bias)
+        return run(plan, X, W, bias, Y=residual)
     finally:
         plan.close()

@@ -18,9 +18,20 @@
  * Act II and of the second page's section "One kernel was never going to be
  * enough".
  *
+ * The two transposed-input layouts complete the four transpose cases of
+ * "Writing a CUDA matmul that catches cuBLAS" (section "Putting it in the
+ * model, where it behaves differently") and with them the backward pass of
+ * the same layer (section "Then: a language model on top of it"): with the
+ * first operand stored [K][M], the weight gradient dW = dYᵀ·X is one call
+ * (A = dY stored [tokens][out], B = X stored [tokens][in]), and dX = dY·W is
+ * the TLG_KN layout.  The residual flag adds the layer's output onto what Y
+ * already holds, the fused residual of that page's section "The residual and
+ * GELU go the same way, and cost three detours".
+ *
  * Conventions for every entry point:
- *  - Every tensor is dense and row-major with no padding: X [M][K],
- *    W [N][K] (TLG_NK) or [K][N] (TLG_KN), bias [N], Y [M][N].
+ *  - Every tensor is dense and row-major with no padding: X [M][K] (or
+ *    [K][M] for the TLG_AT_* layouts), W [N][K] (TLG_NK, TLG_AT_NK) or
+ *    [K][N] (TLG_KN, TLG_AT_KN), bias [N], Y [M][N].
  *  - X, W and bias use the input element type; Y uses the output type.
  *    Products accumulate in fp32.  Half-precision outputs are rounded to
  *    nearest-even once, after the epilogue.
@@ -44,12 +55,19 @@ extern "C" {
 /* Element types (the arithmetic is always fp32-accumulate). */
 typedef enum { TLG_F32 = 0, TLG_F16 = 1, TLG_BF16 = 2 } tlg_dtype;
 
-/* Weight layouts. TLG_NK: W[N][K], Y = X·Wᵀ (PyTorch out×in).
- * TLG_KN: B[K][N], Y = X·B (row-major square GEMM). */
-typedef enum { TLG_NK = 0, TLG_KN = 1 } tlg_layout;
+/* Operand layouts.  TLG_NK: W[N][K], Y = X·Wᵀ (PyTorch out×in).
+ * TLG_KN: B[K][N], Y = X·B (row-major square GEMM).
+ * TLG_AT_NK, TLG_AT_KN: as TLG_NK and TLG_KN with the first operand stored
+ * transposed, A[K][M], so x(m,k) = A[k][m] (Y = Aᵀ·Wᵀ and Y = Aᵀ·B).  These
+ * two take no bias or GELU (TLG_ERR_UNSUPPORTED); TLG_EPI_RESIDUAL is allowed,
+ * for accumulating gradients. */
+typedef enum { TLG_NK = 0, TLG_KN = 1, TLG_AT_NK = 2, TLG_AT_KN = 3 } tlg_layout;
 
-/* Epilogue flags, applied in this order: bias, then GELU. */
-enum { TLG_EPI_BIAS = 1u, TLG_EPI_GELU_TANH = 2u };
+/* Epilogue flags, applied in this order: bias, then GELU, then the residual.
+ * TLG_EPI_RESIDUAL: Y is an input as well as the output; the result is
+ * act(X·Wᵀ + bias) + Y, each element of Y read once before it is written
+ * (summed in fp32, then rounded to the output type). */
+enum { TLG_EPI_BIAS = 1u, TLG_EPI_GELU_TANH = 2u, TLG_EPI_RESIDUAL = 4u };
 
 /* Status codes. */
 enum {
@@ -113,10 +131,10 @@ size_t gemm_workspace_size(tlg_plan_t p);
 int gemm_plan_info(tlg_plan_t p, tlg_plan_info* info);
 
 /*
- * gemm_run — enqueue Y = act(X·Wᵀ + bias) on `stream` (a hipStream_t; NULL
- * means the default stream) and return after the launch; errors inside a
- * kernel surface at the next synchronisation.  X, W, Y (and bias if
- * TLG_EPI_BIAS) must be non-NULL device pointers, 16-byte aligned; bias must
+ * gemm_run — enqueue Y = act(X·Wᵀ + bias) (+ Y with TLG_EPI_RESIDUAL) on
+ * `stream` (a hipStream_t; NULL means the default stream) and return after
+ * the launch; errors inside a kernel surface at the next synchronisation.
+ * X, W, Y (and bias if TLG_EPI_BIAS) must be non-NULL device pointers, 16-byte aligned; bias must
  * be NULL when TLG_EPI_BIAS is not set.  Y must not overlap X, W or bias.
  * workspace: device memory of at least gemm_workspace_size(p) bytes when
  * that is non-zero; it may be NULL when the size is 0.  It must be

@@ -13,6 +13,17 @@ Pins (checked by ``tests/test_oracle.py`` without a GPU): exact rational brute
 force on tiny shapes, the hand-worked examples in ``tests/golden``, identity,
 permutation and all-ones closed forms, numpy float64 matmul, linearity,
 layout equivalence, and the GELU identities plus its distance to the erf form.
+
+Two steps are done here rather than in C, each a plain one: the transposed
+first operand of the ``AT_*`` layouts ("Writing a CUDA matmul that catches
+cuBLAS", sections "Putting it in the model, where it behaves differently" and
+"Then: a language model on top of it": x(m,k) = A[k][m]) is transposed back
+to ``[M][K]`` with numpy before the C loop, and the residual of that page's
+section "The residual and GELU go the same way, and cost three detours" is
+added to the float64 result after bias and GELU, widened exactly from its
+stored type.  Pins: the ``AT_*`` result equals the plain layout on the
+transposed input and numpy's matmul; a zero weight with a residual returns
+the residual exactly; the residual adds linearly.
 """
 
 from __future__ import annotations
@@ -28,7 +39,7 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 _DT = {"f32": 0, "f16": 1, "bf16": 2}
-_LAYOUT = {"NK": 0, "KN": 1}
+_LAYOUT = {"NK": 0, "KN": 1}  # the C loop's weight layouts; "AT_*" transpose X first
 _STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
 
 _lib = None
@@ -67,10 +78,31 @@ def _load():
     return _lib
 
 
+def _dims(X, W, layout):
+    """(M, N, K) from the stored shapes: X [M][K] or [K][M] (AT_*), W [N][K] or [K][N]."""
+    if layout not in ("NK", "KN", "AT_NK", "AT_KN"):
+        raise ValueError(f"unknown layout {layout!r}")
+    K, M = np.shape(X) if layout.startswith("AT_") else np.shape(X)[::-1]
+    N = np.shape(W)[1] if layout.endswith("KN") else np.shape(W)[0]
+    return M, N, K
+
+
+def _widen(a, dtype):
+    a = np.ascontiguousarray(a, dtype=_STORAGE[dtype])
+    if dtype == "bf16":
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
 def _prep(X, W, b, dtype, layout, M, N, K):
     st = _STORAGE[dtype]
     X = np.ascontiguousarray(X, dtype=st)
     W = np.ascontiguousarray(W, dtype=st)
+    if layout.startswith("AT_"):
+        if X.shape != (K, M):
+            raise ValueError(f"X shape {X.shape} != {(K, M)} for layout {layout}")
+        X = np.ascontiguousarray(X.T)
+        layout = layout[3:]
     if X.shape != (M, K):
         raise ValueError(f"X shape {X.shape} != {(M, K)}")
     want = (N, K) if layout == "NK" else (K, N)
@@ -80,7 +112,7 @@ def _prep(X, W, b, dtype, layout, M, N, K):
         b = np.ascontiguousarray(b, dtype=st)
         if b.shape != (N,):
             raise ValueError(f"bias shape {b.shape} != {(N,)}")
-    return X, W, b
+    return X, W, b, layout
 
 
 def _ptr(a):
@@ -88,11 +120,10 @@ def _ptr(a):
 
 
 def linear_rows(X, W, b=None, *, dtype="f32", layout="NK", gelu=False, rows=None,
-                threads: int = 0) -> np.ndarray:
+                threads: int = 0, residual=None, out_dtype=None) -> np.ndarray:
     """Float64 reference for rows ``rows = (m0, m1)`` of the output (all by default)."""
-    M, K = np.shape(X)
-    N = np.shape(W)[0] if layout == "NK" else np.shape(W)[1]
-    X, W, b = _prep(X, W, b, dtype, layout, M, N, K)
+    M, N, K = _dims(X, W, layout)
+    X, W, b, layout = _prep(X, W, b, dtype, layout, M, N, K)
     m0, m1 = (0, M) if rows is None else rows
     out = np.empty((m1 - m0, N), dtype=np.float64)
     flags = (1 if b is not None else 0) | (2 if gelu else 0)
@@ -101,20 +132,25 @@ def linear_rows(X, W, b=None, *, dtype="f32", layout="NK", gelu=False, rows=None
                                     out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), threads)
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
+    if residual is not None:
+        if np.shape(residual) != (M, N):
+            raise ValueError(f"residual shape {np.shape(residual)} != {(M, N)}")
+        out += _widen(np.asarray(residual)[m0:m1], out_dtype or dtype)
     return out
 
 
-def linear(X, W, b=None, *, dtype="f32", layout="NK", gelu=False, threads: int = 0) -> np.ndarray:
+def linear(X, W, b=None, *, dtype="f32", layout="NK", gelu=False, threads: int = 0, residual=None,
+           out_dtype=None) -> np.ndarray:
     """Float64 reference of the whole output ``[M][N]``."""
-    return linear_rows(X, W, b, dtype=dtype, layout=layout, gelu=gelu, threads=threads)
+    return linear_rows(X, W, b, dtype=dtype, layout=layout, gelu=gelu, threads=threads, residual=residual,
+                       out_dtype=out_dtype)
 
 
 def linear_points(X, W, b=None, *, dtype="f32", layout="NK", gelu=False, mi, ni,
-                  threads: int = 0) -> np.ndarray:
+                  threads: int = 0, residual=None, out_dtype=None) -> np.ndarray:
     """Float64 reference of the elements ``(mi[i], ni[i])``."""
-    M, K = np.shape(X)
-    N = np.shape(W)[0] if layout == "NK" else np.shape(W)[1]
-    X, W, b = _prep(X, W, b, dtype, layout, M, N, K)
+    M, N, K = _dims(X, W, layout)
+    X, W, b, layout = _prep(X, W, b, dtype, layout, M, N, K)
     mi = np.ascontiguousarray(mi, dtype=np.int64)
     ni = np.ascontiguousarray(ni, dtype=np.int64)
     out = np.empty(mi.shape[0], dtype=np.float64)
@@ -126,13 +162,18 @@ def linear_points(X, W, b=None, *, dtype="f32", layout="NK", gelu=False, mi, ni,
                                       out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), threads)
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
+    if residual is not None:
+        if np.shape(residual) != (M, N):
+            raise ValueError(f"residual shape {np.shape(residual)} != {(M, N)}")
+        out += _widen(np.asarray(residual)[mi, ni], out_dtype or dtype)
     return out
 
 
 def linear_case(case, threads: int = 0, rows=None) -> np.ndarray:
-    """Reference for an ``inputs.LinearCase``."""
+    """Reference for an ``inputs.LinearCase`` (with its residual, if it has one)."""
     return linear_rows(case.X, case.W, case.b, dtype=case.in_dtype, layout=case.layout,
-                       gelu=case.gelu, rows=rows, threads=threads)
+                       gelu=case.gelu, rows=rows, threads=threads, residual=getattr(case, "R", None),
+                       out_dtype=case.out_dtype)
 
 
 def gelu_tanh(y: float) -> float:

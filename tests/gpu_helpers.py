@@ -35,11 +35,14 @@ def run_case(case: inputs.LinearCase, variant=tlgemm.VARIANT_AUTO, split_k=0, ti
     """Run one case through the C ABI; returns (Y tensor, plan description)."""
     X, W, b = dev if dev is not None else device_case(case)
     own = plan is None
+    R = getattr(case, "R", None)
     if own:
         plan = tlgemm.Plan.create(case.M, case.N, case.K, case.in_dtype, case.out_dtype, case.layout,
-                                  case.b is not None, case.gelu, variant, split_k, tile)
+                                  case.b is not None, case.gelu, variant, split_k, tile, R is not None)
     try:
-        Y = tlgemm.run(plan, X, W, b)
+        # with a residual, Y starts as the residual and is updated in place
+        Y = None if R is None else to_device(R, case.out_dtype, X.device)
+        Y = tlgemm.run(plan, X, W, b, Y=Y)
         torch.cuda.synchronize()
         return Y, plan.describe()
     finally:

@@ -179,11 +179,11 @@ def test_unsupported_pairs_and_flags():
     with pytest.raises(t.TlgError) as e:
         t.gemm_plan(4, 4, 4, "f16", "bf16")
     assert e.value.status == t.ERR_UNSUPPORTED
-    with pytest.raises(t.TlgError) as e:
-        t.gemm_plan(4, 4, 4, "f32", "f32", "NK", 4)
+    with pytest.raises(t.TlgError) as e:  # flags 1, 2, 4 are defined; 8 is not
+        t.gemm_plan(4, 4, 4, "f32", "f32", "NK", 8)
     assert e.value.status == t.ERR_INVALID_ARG
-    with pytest.raises(t.TlgError) as e:
-        t.gemm_plan(4, 4, 4, "f32", "f32", 2, 0)
+    with pytest.raises(t.TlgError) as e:  # layouts 0..3 are defined
+        t.gemm_plan(4, 4, 4, "f32", "f32", 4, 0)
     assert e.value.status == t.ERR_INVALID_ARG
 
 
@@ -221,3 +221,43 @@ def test_run_argument_errors_without_launch():
     assert lib.gemm_run(q.handle, big, 2 * big, None, 3 * big, None, 0, None) == t.ERR_WORKSPACE
     assert lib.gemm_run(q.handle, big, 2 * big, None, 3 * big, 8 * big, 16, None) == t.ERR_WORKSPACE
     assert "workspace" in t.gemm_last_error()
+
+
+# --- transposed first operand and the residual -------------------------------------
+
+def test_transposed_first_operand_layouts_plan():
+    for layout in ("AT_NK", "AT_KN"):
+        i = _plan(768, 3072, 8192, "bf16", "bf16", layout).info  # dW-shaped: M, N = out, in; K = tokens
+        assert i.variant == t.VARIANT_TILED
+        assert f"layout={layout} " in _plan(768, 3072, 8192, "f32", "f32", layout).describe()
+        # rows of the [K][M] operand must be 16-byte aligned for the tiled kernel
+        assert _plan(100, 64, 64, "f32", "f32", layout).info.variant == t.VARIANT_TILED
+        assert _plan(99, 64, 64, "f32", "f32", layout).info.variant == t.VARIANT_GENERIC
+        with pytest.raises(t.TlgError) as e:
+            _plan(16, 4096, 4096, "f16", "f16", layout, variant=t.VARIANT_STREAM)
+        assert e.value.status == t.ERR_UNSUPPORTED
+
+
+def test_transposed_first_operand_takes_no_bias_or_gelu():
+    for bias, gelu in ((True, False), (False, True), (True, True)):
+        with pytest.raises(t.TlgError) as e:
+            _plan(64, 64, 64, "f32", "f32", "AT_NK", bias, gelu)
+        assert e.value.status == t.ERR_UNSUPPORTED
+    assert "+res" in _plan(64, 64, 64, "f32", "f32", "AT_KN", residual=True).describe()
+
+
+def test_residual_flag_plans_like_its_base_epilogue():
+    # the residual is a run-time argument of the same kernels: the measured rows still apply
+    for args in ((16, 4096, 4096, "f16", "f16"), (8192, 3072, 768, "bf16", "bf16", "NK", True, True)):
+        base = _plan(*args).describe()
+        res = _plan(*args, residual=True).describe()
+        assert res.replace("+res", "") == base
+
+
+def test_bad_layout_and_flags_rejected():
+    h = ctypes.c_void_p()
+    lib = ctypes.CDLL(t.LIB_PATH)
+    assert lib.gemm_plan(ctypes.byref(h), 8, 8, 8, 0, 0, 4, 0) == t.ERR_INVALID_ARG
+    assert lib.gemm_plan(ctypes.byref(h), 8, 8, 8, 0, 0, 0, 8) == t.ERR_INVALID_ARG
+    assert lib.gemm_plan(ctypes.byref(h), 8, 8, 8, 0, 0, 2, 4) == t.OK
+    lib.gemm_destroy(h)

@@ -70,15 +70,19 @@ def _special_values(dtype):
     return np.array(v)
 
 
+LAYOUTS = ["NK", "KN", "AT_NK", "AT_KN"]
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("layout", ["NK", "KN"])
+@pytest.mark.parametrize("layout", LAYOUTS)
 def test_rational_bruteforce(oracle_lib, dtype, layout):
-    """Oracle vs exact Fraction sums for every M, N, K in 1..6 (plus bias).
+    """Oracle vs exact Fraction sums for every M, N, K in 1..6 (plus bias and a residual).
 
     Products of two stored values are exact in double, so the oracle's only
-    rounding is K additions: |oracle - exact| <= (K+1) * 2^-53 * sum|terms|
-    (a rigorous bound for recursive summation).  A dropped term, a wrong index
-    or a transposed operand is off by far more.
+    rounding is K additions plus the residual's: |oracle - exact| <=
+    (K+2) * 2^-53 * (sum|terms| + |r|) (a rigorous bound for recursive
+    summation).  A dropped term, a wrong index or a transposed operand is off
+    by far more.  x(m,k) is X[m][k], or X[k][m] for the transposed layouts.
     """
     rng = np.random.default_rng(7)
     specials = _special_values(dtype)
@@ -87,18 +91,20 @@ def test_rational_bruteforce(oracle_lib, dtype, layout):
         for N in range(1, 7):
             for K in range(1, 7):
                 pool = np.concatenate([rng.standard_normal(8) * 3, specials])
-                xv = rng.choice(pool, size=(M, K))
-                wv = rng.choice(pool, size=(N, K) if layout == "NK" else (K, N))
+                at, kn = layout.startswith("AT_"), layout.endswith("KN")
+                xv = rng.choice(pool, size=(K, M) if at else (M, K))
+                wv = rng.choice(pool, size=(K, N) if kn else (N, K))
                 bv = rng.choice(pool, size=(N,))
-                X, W, b = _store(xv, dtype), _store(wv, dtype), _store(bv, dtype)
-                ref = oracle_lib.linear(X, W, b, dtype=dtype, layout=layout)
-                Xe, We, be = _exact(X, dtype), _exact(W, dtype), _exact(b, dtype)
+                rv = rng.choice(pool, size=(M, N))
+                X, W, b, R = _store(xv, dtype), _store(wv, dtype), _store(bv, dtype), _store(rv, dtype)
+                ref = oracle_lib.linear(X, W, b, dtype=dtype, layout=layout, residual=R)
+                Xe, We, be, Re = _exact(X, dtype), _exact(W, dtype), _exact(b, dtype), _exact(R, dtype)
                 for m in range(M):
                     for n in range(N):
-                        terms = [Fraction(Xe[m, k]) * Fraction(We[n, k] if layout == "NK" else We[k, n])
-                                 for k in range(K)] + [Fraction(be[n])]
+                        terms = [Fraction(Xe[k, m] if at else Xe[m, k]) * Fraction(We[k, n] if kn else We[n, k])
+                                 for k in range(K)] + [Fraction(be[n]), Fraction(Re[m, n])]
                         exact = sum(terms, Fraction(0))
-                        bound = (K + 1) * u * float(sum(abs(t) for t in terms))
+                        bound = (K + 2) * u * float(sum(abs(t) for t in terms))
                         assert abs(Fraction(ref[m, n]) - exact) <= Fraction(bound), (M, N, K, m, n)
 
 
@@ -133,13 +139,36 @@ def test_ones_and_zero_weights(oracle_lib, dtype):
 # --- library special case and invariants ----------------------------------------------
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("layout", ["NK", "KN"])
+@pytest.mark.parametrize("layout", LAYOUTS)
 def test_matches_numpy_float64(oracle_lib, dtype, layout):
-    case = inputs.random_case(21, 33, 47, 129, dtype, layout=layout, bias=True)
+    case = inputs.random_case(21, 33, 47, 129, dtype, layout=layout, bias=True, residual=True)
     ref = oracle_lib.linear_case(case)
     Xe, We, be = _exact(case.X, dtype), _exact(case.W, dtype), _exact(case.b, dtype)
-    lib = Xe @ (We.T if layout == "NK" else We) + be
+    Re = _exact(case.R, dtype)
+    lib = (Xe.T if layout.startswith("AT_") else Xe) @ (We if layout.endswith("KN") else We.T) + be + Re
     assert np.max(np.abs(ref - lib)) <= 1e-13 * np.max(np.abs(lib))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_zero_weight_returns_residual(oracle_lib, dtype):
+    """W = 0 and no bias: every product is zero, GELU(0) = 0, so Y is the residual exactly."""
+    M, N, K = 7, 9, 33
+    X = inputs.normal(31, (M, K), 1.0, dtype)
+    R = inputs.normal(32, (M, N), 1.0, dtype)
+    W = _store(np.zeros((N, K)), dtype)
+    for gelu in (False, True):
+        out = oracle_lib.linear(X, W, dtype=dtype, gelu=gelu, residual=R)
+        assert np.array_equal(out, _exact(R, dtype))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_transposed_first_operand_identity(oracle_lib, dtype):
+    """AT_NK with W = I returns the stored [K][M] operand transposed, bitwise."""
+    K, M = 37, 5
+    A = inputs.normal(12, (K, M), 1.0, dtype)
+    eye = _store(np.eye(K), dtype)
+    assert np.array_equal(oracle_lib.linear(A, eye, dtype=dtype, layout="AT_NK"), _exact(A, dtype).T)
+    assert np.array_equal(oracle_lib.linear(A, eye, dtype=dtype, layout="AT_KN"), _exact(A, dtype).T)
 
 
 def test_linearity(oracle_lib):
