@@ -35,9 +35,9 @@ runs on one GPU.
 from __future__ import annotations
 
 import argparse
+import glob
 import json
 import os
-import subprocess
 import sys
 import time
 
@@ -91,15 +91,25 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def read_clocks():
-    """sclk/mclk as reported by rocm-smi (None if unavailable)."""
+def read_clocks(torch):
+    """Current sclk/mclk levels of this process's GPU, read from the amdgpu driver's sysfs tables
+    (the level marked '*'), matched to the device by PCI address; None if unavailable.  No
+    subprocess: a helper program started under a profiler would inherit its preloaded library."""
     try:
-        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
-        data = json.loads(out.stdout)
-        card = next(iter(data.values()))
-        return {k: v for k, v in card.items() if "sclk" in k.lower() or "mclk" in k.lower()}
+        pr = torch.cuda.get_device_properties(0)
+        bdf = f"{pr.pci_domain_id:04x}:{pr.pci_bus_id:02x}:{pr.pci_device_id:02x}."
+        for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+            if not os.path.basename(os.path.realpath(dev)).startswith(bdf):
+                continue
+            out = {}
+            for clk in ("sclk", "mclk"):
+                with open(os.path.join(dev, f"pp_dpm_{clk}")) as f:
+                    cur = [ln.strip() for ln in f if ln.rstrip().endswith("*")]
+                out[clk] = cur[0] if cur else None
+            return out
     except Exception:
         return None
+    return None
 
 
 def time_launches(fn, n: int, stream) -> float:
@@ -402,20 +412,20 @@ def bench_backward(torch, dev, stream, dtype: str, no_parity: bool, reps: int = 
     dW = dYᵀ·X accumulated onto an existing gradient (first operand stored transposed, residual flag)."""
     from dense_gemm_transformer_amd import inputs, tlgemm
 
-    T, w = 8192, 6
+    T = 8192
     peak = PEAK_F32_TFLOPS if dtype == "f32" else PEAK_BF16_TFLOPS
+    cases = inputs.workload_gpt2_backward(T=T, dtype=dtype)
+    nl = len(inputs.GPT2_LINEARS)
     jobs = []
     for g, (name, N, K, _) in enumerate(inputs.GPT2_LINEARS):
-        W, _b = inputs.gpt2_weights(w, 0, g, dtype)                             # [out][in]
-        dY = inputs.normal(inputs.seed_for(w, 1, 1, g), (T, N), 1.0, dtype)   # [tokens][out]
-        X = inputs.gpt2_activation(w, 0, g, T, dtype)                          # [tokens][in]
-        G = inputs.normal(inputs.seed_for(w, 1, 2, g), (N, K), 0.02, dtype)    # gradient so far
-        d = {k: dev_tensor(torch, a, dtype, dev) for k, a in (("W", W), ("dY", dY), ("X", X), ("G", G))}
-        dx = tlgemm.Plan.create(T, K, N, dtype, dtype, "KN")                 # [T][in] = [T][out]·[out][in]
-        dw = tlgemm.Plan.create(N, K, T, dtype, dtype, "AT_KN", residual=True)  # [out][in] += dYᵀ·X
+        cx, cw = cases[g], cases[nl + g]
+        d = {"W": dev_tensor(torch, cx.W, dtype, dev), "dY": dev_tensor(torch, cx.X, dtype, dev),
+             "X": dev_tensor(torch, cw.W, dtype, dev), "G": dev_tensor(torch, cw.R, dtype, dev)}
+        dx = tlgemm.Plan.create(cx.M, cx.N, cx.K, dtype, dtype, cx.layout)
+        dw = tlgemm.Plan.create(cw.M, cw.N, cw.K, dtype, dtype, cw.layout, residual=True)
         outs = {"dX": torch.empty((T, K), dtype=tlgemm.torch_dtype(dtype), device=dev), "dW": d["G"].clone()}
         wss = [torch.zeros(max(p.workspace_size, 1), dtype=torch.uint8, device=dev) for p in (dx, dw)]
-        jobs.append((name, dx, dw, d, outs, wss, (dY, W, X, G)))
+        jobs.append((name, dx, dw, d, outs, wss, (cx.X, cx.W, cw.W, cw.R)))
 
     def one_pass():
         for name, dx, dw, d, outs, wss, _ in jobs:
@@ -485,7 +495,7 @@ def main(argv=None) -> int:
         return 1
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
-    clocks_before = read_clocks()
+    clocks_before = read_clocks(torch)
 
     def to_dev(a, dt):
         if dt == "bf16":
@@ -570,7 +580,7 @@ def main(argv=None) -> int:
             log(f"GPT-2 backward GEMMs at 8192 tokens, {dt}")
             extra[f"gpt2_backward_t8192_{dt}"] = bench_backward(torch, dev, stream, dt, args.no_parity)
             torch.cuda.empty_cache()
-    clocks_after = read_clocks()
+    clocks_after = read_clocks(torch)
 
     cpu = None
     if not args.no_cpu_baseline:

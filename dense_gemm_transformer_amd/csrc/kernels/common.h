@@ -140,6 +140,20 @@ __device__ inline i32x4 buffer_rsrc(const void* p, int64_t bytes) {
     return r;
 }
 
+// ---- LDS transpose reads (ds_read_b64_tr_b16) ----------------------------------------
+// Every lane names 8 bytes (four 16-bit elements) of LDS; within each group of
+// 16 lanes, lane l receives element l % 4 of the 8 bytes named by lanes
+// 4j + l/4, j = 0..3 (layout measured on gfx950).  Pointed at four rows of a
+// row-major tile, four lanes per row and four elements apart, the group reads
+// a 4×16 block and each lane receives one column of it: four consecutive rows.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ inline u32x2 lds_read_tr16(const void* p) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(const_cast<void*>(p))));
+}
+
 // ---- MFMA wrappers -----------------------------------------------------------------
 // 16x16 output block, fp32 accumulate.
 __device__ inline f32x4 mfma16_f32(float a, float b, f32x4 c) {

@@ -18,9 +18,12 @@
 //    64-bit address per load, which keeps the loop free of register spills.
 //  * LDS rows are k-contiguous with a 16-byte pad (stride 80 B), so the
 //    16-byte operand reads of 16 consecutive rows hit 64 distinct banks.
-//    A row-major [K][N] fp32 operand stays n-contiguous (stride BN+8 floats,
-//    so the two half-waves read disjoint bank halves); a [K][N] 16-bit
-//    operand is transposed while it is written to LDS.
+//    A [K][N] weight or [K][M] first operand is stored to LDS as it lies in
+//    memory, n- or m-contiguous.  fp32 fragments are then gathered with
+//    scalar reads (stride BN+8 floats, so the two half-waves read disjoint
+//    bank halves); 16-bit fragments with two LDS transpose reads of four k
+//    rows each (stride BN+32 elements, 16 dwords mod 64 banks, so the four
+//    rows of one read fall in disjoint banks).
 //  * For fp32 one 16-byte read feeds four MFMAs; the k order inside a slice
 //    is permuted identically for both operands, which leaves each dot
 //    product unchanged.
@@ -40,19 +43,15 @@ namespace tlg {
 // Waves per SIMD the register allocation must allow: a wave tile of up to
 // 64×64 (64 accumulator registers) leaves room for two waves, up to 32×32 for
 // four, so LDS rather than registers limits how many workgroups share a CU.
-// With both 16-bit operands transposed in registers (transposed first operand
-// and [K][N] weight) the staging needs more room: one step less.
-template <int IN, int LAYOUT, int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN>
 constexpr int tiled_occupancy() {
     constexpr int acc = (BM / WM) * (BN / WN) / 64;
-    constexpr int occ = acc <= 16 ? 4 : acc <= 64 ? 2 : 1;
-    constexpr bool two_transposes = IN != TLG_F32 && layout_a_transposed(LAYOUT) && layout_b_kn(LAYOUT);
-    return two_transposes && occ > 1 ? occ / 2 : occ;
+    return acc <= 16 ? 4 : acc <= 64 ? 2 : 1;
 }
 
 template <int IN, int OUT, int LAYOUT, uint32_t EPI, int BM, int BN, int BK, int WM, int WN, bool EVEN,
           bool SPLIT>
-__global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<IN, LAYOUT, BM, BN, WM, WN>())) void tiled_kernel(const void* __restrict__ Xv,
+__global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) void tiled_kernel(const void* __restrict__ Xv,
                                                             const void* __restrict__ Wv,
                                                             const void* __restrict__ bias,
                                                             void* __restrict__ Y, float* __restrict__ ws,
@@ -66,27 +65,19 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<IN, LAYOUT, BM, BN, 
     constexpr int LDA = BK + EPV;         // padded LDS row (elements)
     constexpr bool KNB = layout_b_kn(LAYOUT);         // weight stored [K][N]
     constexpr bool AT = layout_a_transposed(LAYOUT);  // first operand stored [K][M]
-    constexpr bool B_NMAJOR = KNB && F32;             // fp32 [K][N] stays n-contiguous
-    constexpr int LDBN = BN + 8;                      // its padded row (floats)
-    constexpr bool A_MMAJOR = AT && F32;              // fp32 [K][M] stays m-contiguous
-    constexpr int LDAM = BM + 8;                      // its padded row (floats)
+    constexpr bool B_NMAJOR = KNB;                    // [K][N] stays n-contiguous in LDS
+    constexpr int LDBN = BN + (F32 ? 8 : 32);         // its padded row (elements)
+    constexpr bool A_MMAJOR = AT;                     // [K][M] stays m-contiguous in LDS
+    constexpr int LDAM = BM + (F32 ? 8 : 32);         // its padded row (elements)
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int TM = WTM / 32, TN = WTN / 32;
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile is a multiple of 32×32");
-    // A 16-bit [K][N] weight (or [K][M] first operand) is moved as 8×8 blocks
-    // (8 rows of k, 8 columns of n or m), transposed in registers so LDS
-    // receives 16-byte runs of k.
-    constexpr bool B_T16 = KNB && !F32;
-    constexpr bool A_T16 = AT && !F32;
-    constexpr int NBK = BK / 8;
-    constexpr int TBLK = NBK * (BN / 8), BPT = (TBLK + THREADS - 1) / THREADS;    // weight blocks, per thread
-    constexpr int TBLKA = NBK * (BM / 8), APT = (TBLKA + THREADS - 1) / THREADS;  // A blocks, per thread
     constexpr int MV = BM / EPV, NV = BN / EPV;  // 16-byte vectors per [K][M] / [K][N] row of the tile
-    constexpr int AV = A_T16 ? 8 * APT : A_MMAJOR ? BK * MV / THREADS : BM * VPR / THREADS;
-    constexpr int BV = B_T16 ? 8 * BPT : !KNB ? BN * VPR / THREADS : BK * NV / THREADS;
+    constexpr int AV = A_MMAJOR ? BK * MV / THREADS : BM * VPR / THREADS;
+    constexpr int BV = !KNB ? BN * VPR / THREADS : BK * NV / THREADS;
     static_assert(AV >= 1 && BV >= 1, "every thread loads");
-    static_assert(A_T16 || AV * THREADS == (A_MMAJOR ? BK * MV : BM * VPR), "A loads divide evenly");
-    static_assert(B_T16 || BV * THREADS == (KNB ? BK * NV : BN * VPR), "weight loads divide evenly");
+    static_assert(AV * THREADS == (A_MMAJOR ? BK * MV : BM * VPR), "A loads divide evenly");
+    static_assert(BV * THREADS == (KNB ? BK * NV : BN * VPR), "weight loads divide evenly");
     constexpr int A_ELEMS = A_MMAJOR ? BK * LDAM : BM * LDA;
     constexpr int B_ELEMS = B_NMAJOR ? BK * LDBN : BN * LDA;
 
@@ -125,23 +116,14 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<IN, LAYOUT, BM, BN, 
 
     // EVEN (exact-fit tiles, every operand region below 2 GiB, checked by the
     // host) loads through buffer descriptors: a uniform base per operand tile
-    // plus one 32-bit lane offset, the per-load offsets uniform.  Threads past
-    // the last 8×8 block of a transposed operand load the tile's first block
-    // (and drop it): the scalar offset is not range-checked, so an unused lane
-    // must still point inside the operand.
+    // plus one 32-bit lane offset, the per-load offsets uniform.
     constexpr int ES = (int)sizeof(S);
-    static_assert(THREADS % VPR == 0 && (!(A_T16 || B_T16) || THREADS % NBK == 0) &&
-                      (!B_NMAJOR || THREADS % NV == 0) && (!A_MMAJOR || THREADS % MV == 0),
+    static_assert(THREADS % VPR == 0 && (!B_NMAJOR || THREADS % NV == 0) && (!A_MMAJOR || THREADS % MV == 0),
                   "each thread's loads share one lane offset");
-    static_assert(!EVEN || ((!A_T16 || APT == 1) && (!B_T16 || BPT == 1)), "one 8×8 block per thread");
-    const int ta = (TBLKA % THREADS == 0 || t < TBLKA) ? t : 0;
-    const int tb = (TBLK % THREADS == 0 || t < TBLK) ? t : 0;
-    const uint32_t a_lane = A_T16      ? (uint32_t)(((ta % NBK) * 8 * M + (ta / NBK) * 8) * ES)
-                            : A_MMAJOR ? (uint32_t)(((t / MV) * M + (t % MV) * EPV) * ES)
-                                       : (uint32_t)(((t / VPR) * K + (t % VPR) * EPV) * ES);
-    const uint32_t b_lane = !KNB  ? (uint32_t)(((t / VPR) * K + (t % VPR) * EPV) * ES)
-                            : B_T16 ? (uint32_t)(((tb % NBK) * 8 * N + (tb / NBK) * 8) * ES)
-                                    : (uint32_t)(((t / NV) * N + (t % NV) * EPV) * ES);
+    const uint32_t a_lane = A_MMAJOR ? (uint32_t)(((t / MV) * M + (t % MV) * EPV) * ES)
+                                     : (uint32_t)(((t / VPR) * K + (t % VPR) * EPV) * ES);
+    const uint32_t b_lane = !KNB ? (uint32_t)(((t / VPR) * K + (t % VPR) * EPV) * ES)
+                                 : (uint32_t)(((t / NV) * N + (t % NV) * EPV) * ES);
     i32x4 rsrc_a = {0, 0, 0, 0}, rsrc_b = {0, 0, 0, 0};
     if constexpr (EVEN) {
         rsrc_a = AT ? buffer_rsrc(X + m0, ((int64_t)K * M - m0) * ES) : buffer_rsrc(X + (int64_t)m0 * K, (int64_t)BM * K * ES);
@@ -152,9 +134,7 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<IN, LAYOUT, BM, BN, 
         if constexpr (EVEN) {
 #pragma unroll
             for (int i = 0; i < AV; ++i) {
-                if constexpr (A_T16)  // row i of the thread's 8×8 block
-                    ra[i] = buffer_load16(rsrc_a, a_lane, (k0 + i) * M * ES, 0);
-                else if constexpr (A_MMAJOR)
+                if constexpr (A_MMAJOR)
                     ra[i] = buffer_load16(rsrc_a, a_lane, (k0 + i * (THREADS / MV)) * M * ES, 0);
                 else
                     ra[i] = buffer_load16(rsrc_a, a_lane, (k0 + i * (THREADS / VPR) * K) * ES, 0);
@@ -163,8 +143,6 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<IN, LAYOUT, BM, BN, 
             for (int i = 0; i < BV; ++i) {
                 if constexpr (!KNB)
                     rbv[i] = buffer_load16(rsrc_b, b_lane, (k0 + i * (THREADS / VPR) * K) * ES, 0);
-                else if constexpr (B_T16)  // block row i % 8 of block column group i / 8
-                    rbv[i] = buffer_load16(rsrc_b, b_lane, ((k0 + i % 8) * N + (i / 8) * (THREADS / NBK) * 8) * ES, 0);
                 else
                     rbv[i] = buffer_load16(rsrc_b, b_lane, (k0 + i * (THREADS / NV)) * N * ES, 0);
             }
@@ -175,17 +153,7 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<IN, LAYOUT, BM, BN, 
 #pragma unroll
         for (int i = 0; i < AV; ++i) {
             const int v = t + THREADS * i;
-            if constexpr (A_T16) {
-                // block q = t + THREADS*(i/8), row i%8 of it: k = kc*8 + i%8, m = mb*8..+7
-                const int q = t + THREADS * (i / 8);
-                const int kc = q % NBK, mb = q / NBK;
-                const int k = k0 + kc * 8 + (i % 8);
-                const int m = min(m0 + mb * 8, M - 8);
-                if ((TBLKA % THREADS == 0 || q < TBLKA) && k < kend)
-                    ra[i] = ldg16(X + (int64_t)k * M + m);
-                else
-                    ra[i] = u32x4{0u, 0u, 0u, 0u};
-            } else if constexpr (A_MMAJOR) {
+            if constexpr (A_MMAJOR) {
                 const int kr = v / MV, mv = v % MV;
                 const int k = k0 + kr;
                 const int m = min(m0 + mv * EPV, M - EPV);
@@ -212,16 +180,6 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<IN, LAYOUT, BM, BN, 
                     rbv[i] = ldg16(W + (int64_t)n * K + k);
                 else
                     rbv[i] = u32x4{0u, 0u, 0u, 0u};
-            } else if constexpr (B_T16) {
-                // block q = t + THREADS*(i/8), row i%8 of it: k = kc*8 + i%8, n = nb*8..+7
-                const int q = t + THREADS * (i / 8);
-                const int kc = q % NBK, nb = q / NBK;
-                const int k = k0 + kc * 8 + (i % 8);
-                const int n = EVEN ? n0 + nb * 8 : min(n0 + nb * 8, N - 8);
-                if ((TBLK % THREADS == 0 || q < TBLK) && (EVEN || k < kend))
-                    rbv[i] = ldg16(W + (int64_t)k * N + n);
-                else
-                    rbv[i] = u32x4{0u, 0u, 0u, 0u};
             } else {
                 const int kr = v / NV, nv = v % NV;
                 const int k = k0 + kr;
@@ -233,36 +191,13 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<IN, LAYOUT, BM, BN, 
             }
         }
     };
-    // Transpose one 8×8 block (rows i0..i0+7 of `rows`: 8 values of k each
-    // along m or n) into LDS rows that run along k: column c gathers half c of
-    // rows 0..7, packed two rows per dword (v_perm), then one 16-byte store per
-    // column.  Eight consecutive lanes write one row's eight 16-byte runs; the
-    // next eight lanes write a row 8 below (288 dwords on: the other 32 banks),
-    // so the stores are conflict-free.
-    auto store_t8 = [&](S* dst, const auto& rows, int i0, int q) {
-        const int kc = q % NBK, cb = q / NBK;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-            u32x4 col;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                col[j] = __builtin_amdgcn_perm(rows[i0 + 2 * j + 1][c >> 1], rows[i0 + 2 * j][c >> 1], sel);
-            *reinterpret_cast<u32x4*>(dst + (cb * 8 + c) * LDA + kc * 8) = col;
-        }
-    };
     auto lstore = [&](int buf, const u32x4 (&ra)[AV], const u32x4 (&rbv)[BV]) {
         S* As = buf ? lds_a1 : lds_a0;
         S* Bs = buf ? lds_b1 : lds_b0;
 #pragma unroll
         for (int i = 0; i < AV; ++i) {
             const int v = t + THREADS * i;
-            if constexpr (A_T16) {
-                if (i % 8 != 0) continue;
-                const int q = t + THREADS * (i / 8);
-                if (TBLKA % THREADS != 0 && q >= TBLKA) continue;
-                store_t8(As, ra, i, q);
-            } else if constexpr (A_MMAJOR) {
+            if constexpr (A_MMAJOR) {
                 *reinterpret_cast<u32x4*>(As + (v / MV) * LDAM + (v % MV) * EPV) = ra[i];
             } else {
                 *reinterpret_cast<u32x4*>(As + (v / VPR) * LDA + (v % VPR) * EPV) = ra[i];
@@ -273,13 +208,8 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<IN, LAYOUT, BM, BN, 
             const int v = t + THREADS * i;
             if constexpr (!KNB) {
                 *reinterpret_cast<u32x4*>(Bs + (v / VPR) * LDA + (v % VPR) * EPV) = rbv[i];
-            } else if constexpr (B_NMAJOR) {
-                *reinterpret_cast<u32x4*>(Bs + (v / NV) * LDBN + (v % NV) * EPV) = rbv[i];
             } else {
-                if (i % 8 != 0) continue;
-                const int q = t + THREADS * (i / 8);
-                if (TBLK % THREADS != 0 && q >= TBLK) continue;
-                store_t8(Bs, rbv, i, q);
+                *reinterpret_cast<u32x4*>(Bs + (v / NV) * LDBN + (v % NV) * EPV) = rbv[i];
             }
         }
     };
@@ -330,16 +260,34 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<IN, LAYOUT, BM, BN, 
             }
         } else {
             // Operand fragments for k-step kq+1 are read from LDS while the
-            // MFMAs of k-step kq issue, so LDS latency overlaps the math.
+            // MFMAs of k-step kq issue, so LDS latency overlaps the math.  A
+            // fragment of an m- or n-contiguous tile (lane: row r, k = 8g..8g+7)
+            // is two transpose reads: lane L names row 8g + (L%16)/4 (+4 for
+            // the second read) and column 16·((L/16)%2) + 4·(L%4) of the
+            // 32-wide block, and receives column r of k rows 8g..8g+3 (+4).
             constexpr int KQ = BK / 16;
             u32x4 a[2][TM], b[2][TN];
+            const int tr_row = 8 * g + ((lane & 15) >> 2), tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+            auto tr_frag = [&](const S* p, int ld) {
+                const u32x2 lo = lds_read_tr16(p + tr_row * ld + tr_col);
+                const u32x2 hi = lds_read_tr16(p + (tr_row + 4) * ld + tr_col);
+                return u32x4{lo[0], lo[1], hi[0], hi[1]};
+            };
             auto frag = [&](int kq, u32x4(&fa)[TM], u32x4(&fb)[TN]) {
 #pragma unroll
-                for (int i = 0; i < TM; ++i)
-                    fa[i] = *reinterpret_cast<const u32x4*>(As + (wm0 + i * 32 + r) * LDA + kq * 16 + 8 * g);
+                for (int i = 0; i < TM; ++i) {
+                    if constexpr (A_MMAJOR)
+                        fa[i] = tr_frag(As + kq * 16 * LDAM + wm0 + i * 32, LDAM);
+                    else
+                        fa[i] = *reinterpret_cast<const u32x4*>(As + (wm0 + i * 32 + r) * LDA + kq * 16 + 8 * g);
+                }
 #pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    fb[j] = *reinterpret_cast<const u32x4*>(Bs + (wn0 + j * 32 + r) * LDA + kq * 16 + 8 * g);
+                for (int j = 0; j < TN; ++j) {
+                    if constexpr (B_NMAJOR)
+                        fb[j] = tr_frag(Bs + kq * 16 * LDBN + wn0 + j * 32, LDBN);
+                    else
+                        fb[j] = *reinterpret_cast<const u32x4*>(Bs + (wn0 + j * 32 + r) * LDA + kq * 16 + 8 * g);
+                }
             };
             frag(0, a[0], b[0]);
 #pragma unroll
@@ -359,13 +307,12 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<IN, LAYOUT, BM, BN, 
     // is stored to the other buffer and the one after is loaded): the first
     // k-step's operand reads, then every MFMA followed by its share of the
     // other work — the global loads over the first half of the MFMAs, the next
-    // k-step's operand reads inside each k-step, and the LDS stores (16-bit
-    // [K][N] operands: four transposing permutes before each) over the second
-    // half.  Whole phase as one scheduling region for 16-bit inputs; fp32
+    // k-step's operand reads inside each k-step, and the LDS stores over the
+    // second half.  Whole phase as one scheduling region for 16-bit inputs; fp32
     // splits it at the middle k-step (measured: 2803 vs 3809 cycles per
     // 256×256×64 bf16 slice, 8481 vs 8564 per 256×256×16 fp32 slice).
     constexpr int NKQ = F32 ? BK / 8 : BK / 16;
-    constexpr int FR = F32 ? (A_MMAJOR ? 4 : 1) * TM + (B_NMAJOR ? 4 : 1) * TN : TM + TN;
+    constexpr int FR = (A_MMAJOR ? (F32 ? 4 : 2) : 1) * TM + (B_NMAJOR ? (F32 ? 4 : 2) : 1) * TN;
     constexpr int NMF = F32 ? NKQ * 4 * TM * TN : NKQ * TM * TN;
     constexpr int MPK = NMF / NKQ, HALF = NMF / 2;
     constexpr int NVM = AV + BV, NDW = AV + BV;
@@ -377,11 +324,8 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<IN, LAYOUT, BM, BN, 
         if (loads && m % SV == 0 && m / SV < NVM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         if (m / MPK < NKQ - 1 && (m % MPK) % SR == 0 && (m % MPK) / SR < FR)
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // next k-step's operand read
-        if (stores && m >= HALF && (m - HALF) % SW == 0 && (m - HALF) / SW < NDW) {
-            const int w = (m - HALF) / SW;  // LDS stores: A's first, then the weight's
-            if ((A_T16 && w < AV) || (B_T16 && w >= AV)) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-        }
+        if (stores && m >= HALF && (m - HALF) % SW == 0 && (m - HALF) / SW < NDW)
+            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS stores: A's first, then the weight's
     };
     auto whole_phase = [&]() {
         __builtin_amdgcn_sched_group_barrier(0x100, FR, 0);

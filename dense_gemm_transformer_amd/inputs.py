@@ -10,7 +10,7 @@ Recipe (one source of truth for tests and the benchmark):
   a seeded generator but never say which one ("Optimizing a GPT-2-class
   transformer on a GPU", Results), so the draws differ from theirs.
 * Seeds: ``1000 * workload + 10 * layer + tensor`` with tensor X = 1, W = 2,
-  b = 3, plus ``100000 * g`` for the g-th linear of a GPT-2 layer (qkv 0,
+  b = 3 (backward: dY = 5, accumulated weight gradient = 6), plus ``100000 * g`` for the g-th linear of a GPT-2 layer (qkv 0,
   attn-out 1, fc 2, proj 3), so that no two tensors of a stack share a seed.
 * Values are drawn in float64, rounded to float32 with round-to-nearest-even,
   then (for half formats) rounded again to float16 / bfloat16 with
@@ -192,6 +192,32 @@ def workload_gpt2_stack(workload: int = 5, batch: int = 64, seq: int = 128, laye
     for layer in range(layers):
         out.extend(workload_gpt2_layer(workload, M, dtype, layer))
     return out
+
+
+TENSOR_DY, TENSOR_G = 5, 6  # output gradient and the weight gradient accumulated so far
+
+
+def workload_gpt2_backward(workload: int = 6, T: int = 8192, dtype: str = "f32", layer: int = 0):
+    """Backward GEMMs of the four GPT-2-small linears of one layer over T tokens.
+
+    For each linear Y = X·Wᵀ (X [T][K], W [N][K]) and an output gradient dY
+    [T][N] ~ N(0, 1): the input gradient dX = dY·W, layout ``"KN"`` with the
+    weight read as stored, and the weight gradient dW = dYᵀ·X added onto the
+    gradient G [N][K] ~ N(0, 0.02) accumulated so far, layout ``"AT_KN"`` with
+    dY as the transposed first operand and residual G.  Returns the dX cases,
+    then the dW cases, in the order of the linears.
+    """
+    dx, dw = [], []
+    for g, (name, N, K, _) in enumerate(GPT2_LINEARS):
+        W, _b = gpt2_weights(workload, layer, g, dtype)
+        X = gpt2_activation(workload, layer, g, T, dtype)
+        dY = normal(seed_for(workload, layer, TENSOR_DY, g), (T, N), 1.0, dtype)
+        G = normal(seed_for(workload, layer, TENSOR_G, g), (N, K), 0.02, dtype)
+        dx.append(LinearCase(f"{name}_dX_{T}x{K}x{N}_{dtype}", T, K, N, dtype, dtype, "KN", False, False,
+                             dY, W, None))
+        dw.append(LinearCase(f"{name}_dW_{N}x{K}x{T}_{dtype}", N, K, T, dtype, dtype, "AT_KN", False, False,
+                             dY, X, None, G))
+    return dx + dw
 
 
 TENSOR_R = 4  # residual, in random_case

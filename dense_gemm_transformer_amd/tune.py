@@ -2,7 +2,8 @@
 
     python -m dense_gemm_transformer_amd.tune [--out csrc/dispatch_table.inc] [--rounds 5]
 
-For every workload shape (the five linear-layer workloads) each candidate
+For every workload shape (the five linear-layer workloads and the backward
+GEMMs of a GPT-2-small layer) each candidate
 plan — stream and tiled configurations, with and without split-K — runs in
 paired rounds: one timing of every candidate per round, the round order
 rotating, the median over rounds kept ("compare only within one window", the
@@ -10,7 +11,10 @@ paired measurements of "Optimizing a GPT-2-class transformer on a GPU", Act V).
 Each timing replays a CUDA graph of back-to-back launches, so host launch
 overhead does not hide microsecond kernels.  A candidate whose output differs
 from the planner's default plan by more than the parity tolerance is dropped.
-The winner of each shape becomes one row of ``csrc/dispatch_table.inc``.
+The winner of each shape becomes one row of ``csrc/dispatch_table.inc``; with
+``--only`` the rows of the shapes not measured are kept from the existing table.
+The table keys on the kernel epilogue (bias, GELU) only, so a residual case is
+timed without its residual: the flag adds one read of Y to the same kernel.
 """
 
 from __future__ import annotations
@@ -34,7 +38,33 @@ def workload_cases():
     cases += inputs.workload_gpt2_layer(M=128, dtype="f32")
     cases += [inputs.workload_square(dtype="f32"), inputs.workload_square(dtype="bf16")]
     cases += inputs.workload_gpt2_layer(M=8192, dtype="f32") + inputs.workload_gpt2_layer(M=8192, dtype="bf16")
+    cases += inputs.workload_gpt2_backward(dtype="f32") + inputs.workload_gpt2_backward(dtype="bf16")
     return cases
+
+
+_DT = {"f32": 0, "f16": 1, "bf16": 2}
+_LAY = {"NK": 0, "KN": 1, "AT_NK": 2, "AT_KN": 3}
+
+
+def table_row(M, N, K, in_dtype, out_dtype, layout, epi, v, tile, split, comment) -> str:
+    return (f"{{{M}, {N}, {K}, {_DT[in_dtype]}, {_DT[out_dtype]}, {_LAY[layout]}, {epi}u, {v}, {tile}, "
+            f"{split}}},  // {comment}")
+
+
+def existing_rows(path):
+    """Rows of a table file as {shape key: line}; the sentinel and comments are skipped."""
+    rows = {}
+    if not os.path.exists(path):
+        return rows
+    for line in open(path):
+        line = line.strip()
+        if not line.startswith("{"):
+            continue
+        fields = [f.strip().rstrip("u") for f in line[1:line.index("}")].split(",")]
+        key = tuple(int(f) for f in fields[:7])
+        if key[0] >= 1:
+            rows[key] = line
+    return rows
 
 
 def candidates(case, tlgemm):
@@ -66,7 +96,7 @@ def main(argv=None) -> int:
     ap.add_argument("--out", default=TABLE)
     ap.add_argument("--rounds", type=int, default=5)
     ap.add_argument("--launches", type=int, default=20, help="launches per captured graph")
-    ap.add_argument("--only", default="", help="substring filter on workload names")
+    ap.add_argument("--only", default="", help="comma-separated substrings: tune only workloads naming one")
     ap.add_argument("--jsonl", default="", help="append every measurement here")
     args = ap.parse_args(argv)
 
@@ -84,7 +114,7 @@ def main(argv=None) -> int:
     rows = []
     log = open(args.jsonl, "a") if args.jsonl else None
     for case in workload_cases():
-        if args.only and args.only not in case.name:
+        if args.only and not any(o in case.name for o in args.only.split(",")):
             continue
         X, W = put(case.X, case.in_dtype), put(case.W, case.in_dtype)
         b = None if case.b is None else put(case.b, case.in_dtype)
@@ -143,17 +173,19 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
 
     if rows and args.out:
-        dt = {"f32": 0, "f16": 1, "bf16": 2}
-        lay = {"NK": 0, "KN": 1}
+        merged = existing_rows(args.out) if args.only else {}
+        for case, v, tile, split, epi, us, desc in rows:
+            key = (case.M, case.N, case.K, _DT[case.in_dtype], _DT[case.out_dtype], _LAY[case.layout], epi)
+            merged[key] = table_row(case.M, case.N, case.K, case.in_dtype, case.out_dtype, case.layout, epi,
+                                    v, tile, split, f"{case.name}: {us:.2f} us")
         with open(args.out, "w") as f:
             f.write("// Measured per-shape routing: {M, N, K, in_dt, out_dt, layout, epi, variant, tile, split}.\n")
             f.write("// Written by `python -m dense_gemm_transformer_amd.tune` on one MI355X: the fastest\n")
             f.write("// candidate of paired rounds, each timing a graph replay of back-to-back launches.\n")
             f.write("{0, 0, 0, 0, 0, 0, 0u, 0, 0, 0},  // sentinel (matches no shape: M >= 1 is enforced)\n")
-            for case, v, tile, split, epi, us, desc in rows:
-                f.write(f"{{{case.M}, {case.N}, {case.K}, {dt[case.in_dtype]}, {dt[case.out_dtype]}, "
-                        f"{lay[case.layout]}, {epi}u, {v}, {tile}, {split}}},  // {case.name}: {us:.2f} us\n")
-        print(f"# wrote {len(rows)} rows to {args.out}", file=sys.stderr)
+            for line in merged.values():
+                f.write(line + "\n")
+        print(f"# wrote {len(merged)} rows ({len(rows)} measured) to {args.out}", file=sys.stderr)
     return 0
 
 
