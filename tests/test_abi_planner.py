@@ -83,8 +83,9 @@ def _table_rows():
 def test_dispatch_table_rows_drive_the_planner():
     """Every measured row is what the default plan of its exact shape becomes."""
     rows = _table_rows()
-    assert len(rows) == 16
-    dt, lay = {0: "f32", 1: "f16", 2: "bf16"}, {0: "NK", 1: "KN"}
+    assert len(rows) == 31  # 15 forward shapes, 16 backward (dX and dW of four linears, fp32 and bf16)
+    assert sum(r[5] == 3 for r in rows) == 8  # the weight gradients: transposed first operand
+    dt, lay = {0: "f32", 1: "f16", 2: "bf16"}, {0: "NK", 1: "KN", 2: "AT_NK", 3: "AT_KN"}
     for M, N, K, i, o, l, epi, variant, tile, split in rows:
         args = (M, N, K, dt[i], dt[o], lay[l], bool(epi & 1), bool(epi & 2))
         want = _plan(*args, variant=variant, tile=tile + 1, split_k=split).describe()
