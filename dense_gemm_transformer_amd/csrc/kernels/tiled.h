@@ -49,6 +49,17 @@ constexpr int tiled_occupancy() {
     return acc <= 16 ? 4 : acc <= 64 ? 2 : 1;
 }
 
+// Static LDS of one workgroup: two buffers of each operand tile (the arrays
+// the kernel declares; the padded row lengths are the kernel's).
+template <int IN, int LAYOUT, int BM, int BN, int BK>
+constexpr int tiled_lds_bytes() {
+    constexpr bool f32 = IN == TLG_F32;
+    constexpr int es = f32 ? 4 : 2, epv = 16 / es;
+    constexpr int a = layout_a_transposed(LAYOUT) ? BK * (BM + (f32 ? 8 : 32)) : BM * (BK + epv);
+    constexpr int b = layout_b_kn(LAYOUT) ? BK * (BN + (f32 ? 8 : 32)) : BN * (BK + epv);
+    return 2 * (a + b) * es;
+}
+
 template <int IN, int OUT, int LAYOUT, uint32_t EPI, int BM, int BN, int BK, int WM, int WN, bool EVEN,
           bool SPLIT>
 __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) void tiled_kernel(const void* __restrict__ Xv,
@@ -80,6 +91,8 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) 
     static_assert(BV * THREADS == (KNB ? BK * NV : BN * VPR), "weight loads divide evenly");
     constexpr int A_ELEMS = A_MMAJOR ? BK * LDAM : BM * LDA;
     constexpr int B_ELEMS = B_NMAJOR ? BK * LDBN : BN * LDA;
+    static_assert(2 * (A_ELEMS + B_ELEMS) * (int)sizeof(S) == tiled_lds_bytes<IN, LAYOUT, BM, BN, BK>(),
+                  "the launcher's LDS figure matches the arrays");
 
     // Four LDS arrays (A and B operand, two buffers each): separate objects,
     // so the compiler sees that stores into one buffer never alias operand
@@ -368,42 +381,26 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) 
     // follows its last read.
     // Every compute and load in the loop is unconditional, which keeps the
     // accumulators in place across iterations and lets each wait cover only
-    // the slice about to be stored.
+    // the slice about to be stored.  The loop runs over every pair of slices;
+    // prefetches past the last slice re-read the last one (an L2 hit; the
+    // copy lands in a buffer nothing reads), so no tail code with its own
+    // register allocation follows the loop: an odd count leaves one multiply.
     if (nslices > 0) {
         u32x4 ra0[AV], rb0[BV], ra1[AV], rb1[BV];
+        const int last = nslices - 1;
         gload(0, ra0, rb0);
-        if (nslices > 1) gload(1, ra1, rb1);
+        gload(min(1, last), ra1, rb1);
         lstore(0, ra0, rb0);
         __syncthreads();
-        // Steady state: pairs whose two prefetches are in range, so the loads
-        // are unconditional and the wait before each LDS store covers only
-        // the older slice.
+        // At the top of each pair: buffer 0 holds slice s, ra1 slice s+1.
         int s = 0;
-        for (; s + 3 < nslices; s += 2) {
-            phase(0, s + 2, ra0, rb0, ra1, rb1);  // multiply s, store s+1, load s+2
+        for (; s + 1 < nslices; s += 2) {
+            phase(0, min(s + 2, last), ra0, rb0, ra1, rb1);  // multiply s, store s+1, load s+2
             __syncthreads();
-            phase(1, s + 3, ra1, rb1, ra0, rb0);  // multiply s+1, store s+2, load s+3
+            phase(1, min(s + 3, last), ra1, rb1, ra0, rb0);  // multiply s+1, store s+2, load s+3
             __syncthreads();
         }
-        // Tail: slice s is in buffer 0, slice s+1 (if any) in ra1.
-        const int rem = nslices - s;  // 1, 2 or 3
-        if (rem == 3) {
-            gload(s + 2, ra0, rb0);
-            compute(0, nothing);
-            lstore(1, ra1, rb1);
-            __syncthreads();
-            compute(1, nothing);
-            lstore(0, ra0, rb0);
-            __syncthreads();
-            compute(0, nothing);
-        } else if (rem == 2) {
-            compute(0, nothing);
-            lstore(1, ra1, rb1);
-            __syncthreads();
-            compute(1, nothing);
-        } else {
-            compute(0, nothing);
-        }
+        if (s < nslices) compute(0, nothing);  // odd count: the last slice is in buffer 0
     }
 
     // ---- epilogue: a 32×32 accumulator holds column (lane % 32) and rows
@@ -548,9 +545,14 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     }
 }
 
-template <int I, int O, int L, uint32_t E, int BM, int BN, int BK, int WM, int WN>
+template <int I, int O, int L, uint32_t E, int BM, int BN, int BK, int WM, int WN, int CAP>
 static int launch_tiled_cfg(const tlg_plan& p, const void* X, const void* W, const void* bias, void* Y,
                             float* ws, hipStream_t stream) {
+    // A workgroups-per-CU cap is enforced by asking for unused dynamic LDS:
+    // just past 1/(CAP+1) of the CU's 160 KiB per workgroup.
+    constexpr int kLdsPerCu = 160 * 1024, st = tiled_lds_bytes<I, L, BM, BN, BK>();
+    constexpr int dyn = CAP > 0 && st < kLdsPerCu / (CAP + 1) + 1024 ? kLdsPerCu / (CAP + 1) + 1024 - st : 0;
+    static_assert(CAP == 0 || (st + dyn) * CAP <= kLdsPerCu, "the cap still fits CAP workgroups");
     const int S = p.split;
     const int kper = (int)(ceil_div(ceil_div(p.K, S), BK) * BK);
     const int64_t es = I == TLG_F32 ? 4 : 2;
@@ -562,12 +564,12 @@ static int launch_tiled_cfg(const tlg_plan& p, const void* X, const void* W, con
     const dim3 grid((unsigned)(p.grid_x * p.grid_y), (unsigned)S), block(64 * WM * WN);
     auto go = [&](auto ev, auto sp) {
         hipLaunchKernelGGL((tiled_kernel<I, O, L, E, BM, BN, BK, WM, WN, decltype(ev)::value, decltype(sp)::value>),
-                           grid, block, 0, stream, X, W, bias, Y, ws, (int)p.M, (int)p.N, (int)p.K, kper, resid);
+                           grid, block, dyn, stream, X, W, bias, Y, ws, (int)p.M, (int)p.N, (int)p.K, kper, resid);
         return check_launch("tiled_kernel");
     };
     auto go_split = [&](auto ev) {
         hipLaunchKernelGGL((tiled_kernel<I, TLG_F32, L, 0u, BM, BN, BK, WM, WN, decltype(ev)::value, true>), grid,
-                           block, 0, stream, X, W, nullptr, nullptr, ws, (int)p.M, (int)p.N, (int)p.K, kper, 0);
+                           block, dyn, stream, X, W, nullptr, nullptr, ws, (int)p.M, (int)p.N, (int)p.K, kper, 0);
         return check_launch("tiled_kernel");
     };
     int rc;
@@ -604,7 +606,7 @@ int launch_tiled_in(const tlg_plan& p, const void* X, const void* W, const void*
 #define TLG_TILED_CASE(i)                                                                                 \
     case i: {                                                                                             \
         constexpr TileCfg c = T[i];                                                                       \
-        return launch_tiled_cfg<I, O, L, E, c.bm, c.bn, c.bk, c.wm, c.wn>(p, X, W, bias, Y, wsf, stream); \
+        return launch_tiled_cfg<I, O, L, E, c.bm, c.bn, c.bk, c.wm, c.wn, c.cap>(p, X, W, bias, Y, wsf, stream); \
     }
                 switch (p.tile) {
                     TLG_TILED_CASE(0)

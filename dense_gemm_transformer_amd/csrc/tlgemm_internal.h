@@ -30,13 +30,14 @@ constexpr uint32_t kEpiKernel = TLG_EPI_BIAS | TLG_EPI_GELU_TANH;
 struct TileCfg {
     int bm, bn, bk;  // workgroup tile (rows of Y, columns of Y, K per pipeline stage)
     int wm, wn;      // waves along M and N
+    int cap = 0;     // workgroups per CU at most (enforced with unused LDS); 0: as registers and LDS allow
 };
 
 // Tiles of the LDS-tiled MFMA kernel, per input class.  The index is what
 // tlg_plan_opts::tile selects (entry k-1).
 // fp32 operands: v_mfma_f32_32x32x2_f32, wave tile (bm/wm)×(bn/wn).
 constexpr TileCfg kTiledF32[] = {
-    {128, 128, 16, 2, 2},  // 0: square and wide shapes
+    {128, 128, 16, 2, 2, 2},  // 0: square and wide shapes; two per CU (a third leaves a one-per-CU tail)
     {64, 64, 16, 2, 2},    // 1: narrow grids, pairs with split-K
     {256, 128, 16, 2, 2},  // 2: 128×64 wave tiles
     {128, 128, 32, 2, 2},  // 3: deeper K slice
