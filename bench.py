@@ -196,6 +196,7 @@ def graph_span_ms(torch, launch, reps: int, outputs):
     kernels are deterministic, so a replay must reproduce them exactly).
     """
     side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())  # the buffers were written on the current stream
     with torch.cuda.stream(side):
         launch(side.cuda_stream)
     side.synchronize()

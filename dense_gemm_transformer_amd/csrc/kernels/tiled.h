@@ -410,24 +410,25 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) 
     // on disjoint banks), then every lane takes whole 16-byte runs of one row,
     // applies bias, GELU and the residual, converts and stores them: full-line
     // writes and one store per 16 bytes instead of one per element.  The
-    // operand buffers are free once every wave is past its last multiply: two
-    // waves share each A array where it is large enough, else each wave takes
-    // one of the four arrays; where neither fits, the per-element path below.
+    // operand buffers are free once every wave is past its last multiply:
+    // each wave takes a strip of its own from them; where the four arrays
+    // hold fewer strips than there are waves, the per-element path below.
     constexpr int SROW = WTN + 8;  // staged row stride (floats)
     constexpr int STG = 16 * SROW;
-    constexpr int STAGE = 2 * STG * 4 <= A_ELEMS * (int)sizeof(S) ? 2
-                          : (WM * WN == 4 && STG * 4 <= A_ELEMS * (int)sizeof(S) &&
-                             STG * 4 <= B_ELEMS * (int)sizeof(S))
-                              ? 1
-                              : 0;
-    if constexpr (EVEN && STAGE > 0) {
+    // Strips of STG floats that fit in each operand array; wave w takes strip
+    // w of a0, a1, b0, b1 in turn.
+    constexpr int SA = A_ELEMS * (int)sizeof(S) / (STG * 4), SB = B_ELEMS * (int)sizeof(S) / (STG * 4);
+    constexpr bool STAGED = 2 * SA + 2 * SB >= WM * WN;
+    if constexpr (EVEN && STAGED) {
         constexpr int OB = SPLIT ? 4 : (OUT == TLG_F32 ? 4 : 2);  // bytes per written element
         constexpr int EPC = 16 / OB;                               // elements per 16-byte store
         constexpr int CPR = WTN / EPC;                             // 16-byte runs per staged row
         static_assert(64 % CPR == 0 && (16 * CPR) % 64 == 0, "runs divide evenly over the lanes");
         __syncthreads();
-        float* stg = STAGE == 2 ? reinterpret_cast<float*>((wave >> 1) ? lds_a1 : lds_a0) + (wave & 1) * STG
-                     : reinterpret_cast<float*>(wave == 0 ? lds_a0 : wave == 1 ? lds_a1 : wave == 2 ? lds_b0 : lds_b1);
+        float* stg = wave < SA           ? reinterpret_cast<float*>(lds_a0) + wave * STG
+                     : wave < 2 * SA       ? reinterpret_cast<float*>(lds_a1) + (wave - SA) * STG
+                     : wave < 2 * SA + SB  ? reinterpret_cast<float*>(lds_b0) + (wave - 2 * SA) * STG
+                                           : reinterpret_cast<float*>(lds_b1) + (wave - 2 * SA - SB) * STG;
         // Opaque copy of the lane index: everything the epilogue derives from
         // it is computed here, after the loop, instead of being hoisted in
         // front of it and held in registers through it (which spilled the
@@ -602,7 +603,7 @@ int launch_tiled_in(const tlg_plan& p, const void* X, const void* W, const void*
                 constexpr int O = decltype(out)::value, L = decltype(lay)::value;
                 constexpr uint32_t E = (uint32_t)decltype(epi)::value;
                 constexpr const TileCfg* T = I == TLG_F32 ? kTiledF32 : kTiled16;
-                static_assert(kNumTiledF32 == 5 && kNumTiled16 == 5, "tile lists changed");
+                static_assert(kNumTiledF32 == 6 && kNumTiled16 == 6, "tile lists changed");
 #define TLG_TILED_CASE(i)                                                                                 \
     case i: {                                                                                             \
         constexpr TileCfg c = T[i];                                                                       \
@@ -614,6 +615,7 @@ int launch_tiled_in(const tlg_plan& p, const void* X, const void* W, const void*
                     TLG_TILED_CASE(2)
                     TLG_TILED_CASE(3)
                     TLG_TILED_CASE(4)
+                    TLG_TILED_CASE(5)
                 default: set_error("bad tiled tile"); return (int)TLG_ERR_INVALID_ARG;
                 }
 #undef TLG_TILED_CASE

@@ -42,6 +42,7 @@ constexpr TileCfg kTiledF32[] = {
     {256, 128, 16, 2, 2},  // 2: 128×64 wave tiles
     {128, 128, 32, 2, 2},  // 3: deeper K slice
     {256, 256, 16, 2, 2},  // 4: 128×128 wave tiles
+    {256, 256, 16, 2, 4},  // 5: eight waves, two per SIMD, 128×64 wave tiles
 };
 // 16-bit operands: v_mfma_f32_32x32x16_{f16,bf16}.  A slice of 32 elements
 // is only 256 MFMA cycles per wave, too short to hide one slice of load
@@ -52,6 +53,7 @@ constexpr TileCfg kTiled16[] = {
     {256, 128, 64, 2, 2},   // 2
     {128, 128, 128, 2, 2},  // 3
     {256, 256, 64, 2, 2},   // 4
+    {256, 256, 64, 2, 4},   // 5: eight waves, two per SIMD: one's stalls are the other's MFMA time
 };
 constexpr int kNumTiledF32 = sizeof(kTiledF32) / sizeof(kTiledF32[0]);
 constexpr int kNumTiled16 = sizeof(kTiled16) / sizeof(kTiled16[0]);

@@ -233,7 +233,10 @@ def run(plan: Plan, X, W, bias=None, Y=None, workspace=None, stream=None):
     need = plan.workspace_size
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.zeros(need, dtype=torch.uint8, device=X.device)  # zero before first use
-    s = stream if stream is not None else torch.cuda.current_stream(X.device)
+    cur = torch.cuda.current_stream(X.device)
+    s = stream if stream is not None else cur
+    if s != cur:  # Y and the workspace were allocated (and the workspace zeroed) on the current stream
+        s.wait_stream(cur)
     for name, t in (("X", X), ("W", W), ("Y", Y), ("bias", bias)):
         if t is not None and not (t.is_cuda and t.is_contiguous()):
             raise ValueError(f"{name} must be a contiguous device tensor")

@@ -87,7 +87,7 @@ def candidates(case, tlgemm):
     if case.layout == "NK" and case.M <= 256:
         for tile in range(1, 6):
             opts += [(tlgemm.VARIANT_STREAM, tile, 0), (tlgemm.VARIANT_STREAM, tile, 1)]
-    for tile in range(1, 6):
+    for tile in range(1, 7):
         for split in (1, 2, 4, 8):
             opts.append((tlgemm.VARIANT_TILED, tile, split))
     for v, tile, split in opts:
@@ -173,6 +173,7 @@ def main(argv=None) -> int:
             args_ = (X.data_ptr(), W.data_ptr(), 0 if b is None else b.data_ptr(), Y.data_ptr(),
                      ws.data_ptr() if p.workspace_size else 0, p.workspace_size)
             s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())  # Y, ws and the inputs come from the default stream
             with torch.cuda.stream(s):
                 p.run_ptrs(*args_, s.cuda_stream)
             s.synchronize()
@@ -284,7 +285,7 @@ def table_tile(plan) -> int:
     from . import tlgemm
 
     i = plan.info
-    for t in range(1, 6):
+    for t in range(1, 7):
         try:
             q = tlgemm.Plan.create(plan.M, plan.N, plan.K, plan.in_dtype, plan.out_dtype, plan.layout,
                                    bool(plan.epi_flags & 1), bool(plan.epi_flags & 2), i.variant, max(i.split_k, 1)

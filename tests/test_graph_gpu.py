@@ -49,6 +49,7 @@ def test_captured_sequence_replays_bitwise():
         _setup(inputs.workload_fp16_narrow()),                                         # the narrow layer
     ]
     s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())  # inputs, outputs and zeroed workspaces come from the default stream
     with torch.cuda.stream(s):
         for g in gemms:
             _launch(g, s)

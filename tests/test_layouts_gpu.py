@@ -45,7 +45,7 @@ def test_transposed_first_operand(pair, layout, residual):
         c = inputs.random_case(61, M, N, K, pair[0], pair[1], layout, residual=residual)
         _, desc = _check(c)
         assert "variant=generic" in desc
-    for tile in (1, 2, 3, 4, 5):
+    for tile in (1, 2, 3, 4, 5, 6):
         for (M, N, K), split in [((136, 136, 72), 1), ((256, 256, 256), 1), ((64, 64, 64), 1),
                                  ((200, 264, 400), 3), ((512, 512, 1024), 4)]:
             c = inputs.random_case(62, M, N, K, pair[0], pair[1], layout, residual=residual)

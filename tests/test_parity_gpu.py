@@ -89,7 +89,7 @@ def test_stream_forced_split(pair, split):
 @pytest.mark.parametrize("layout", ["NK", "KN"])
 @pytest.mark.parametrize("epi", EPIS, ids=["none", "bias", "gelu", "bias+gelu"])
 def test_tiled(pair, layout, epi):
-    for tile in (1, 2, 3):
+    for tile in (1, 2, 3, 4, 5, 6):
         for (M, N, K), split in [((130, 136, 72), 1), ((256, 256, 256), 1), ((64, 64, 32), 1),
                                  ((200, 264, 400), 3), ((33, 520, 1024), 4)]:
             c = _case(3, M, N, K, pair, layout, epi)
