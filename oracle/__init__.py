@@ -1,4 +1,4 @@
-"""CPU oracle for Y = X·Wᵀ (+ b, optional tanh-GELU).  TEST INFRASTRUCTURE.
+"""CPU oracle for Y = X·Wᵀ (+ b, optional tanh-GELU) and the layer around it.  TEST INFRASTRUCTURE.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  The product library never does, and
@@ -13,6 +13,16 @@ Pins (checked by ``tests/test_oracle.py`` without a GPU): exact rational brute
 force on tiny shapes, the hand-worked examples in ``tests/golden``, identity,
 permutation and all-ones closed forms, numpy float64 matmul, linearity,
 layout equivalence, and the GELU identities plus its distance to the erf form.
+
+The two operations around the GEMMs in a GPT-2 layer are written out in C
+the same way: ``layernorm`` (biased variance over the row, eps inside the
+square root) and ``attention`` (softmax of q·k/sqrt(HS) over the keys up to
+the query's position, applied to v, with the log-sum-exp).  Pins
+(``tests/test_oracle_layer.py``): torch's float64 layer_norm and
+scaled_dot_product_attention on the CPU, a hand-worked normalisation, a
+constant row, shift/scale invariance and the unit moments of the output; one
+position returns its value row, identical keys average the values, later
+positions do not touch earlier outputs, and the probabilities sum to one.
 
 Two steps are done here rather than in C, each a plain one: the transposed
 first operand of the ``AT_*`` layouts ("Writing a CUDA matmul that catches
@@ -74,6 +84,10 @@ def _load():
         lib.oracle_decode.argtypes = [vp, i64, ci]
         lib.oracle_decode.restype = ctypes.c_double
         lib.oracle_max_threads.restype = ci
+        lib.oracle_layernorm.argtypes = [i64, i64, ci, vp, vp, vp, ctypes.c_double, dp, dp, dp, ci]
+        lib.oracle_layernorm.restype = ci
+        lib.oracle_attention.argtypes = [i64, i64, i64, i64, ci, vp, ci, dp, dp, ci]
+        lib.oracle_attention.restype = ci
         _lib = lib
     return _lib
 
@@ -174,6 +188,44 @@ def linear_case(case, threads: int = 0, rows=None) -> np.ndarray:
     return linear_rows(case.X, case.W, case.b, dtype=case.in_dtype, layout=case.layout,
                        gelu=case.gelu, rows=rows, threads=threads, residual=getattr(case, "R", None),
                        out_dtype=case.out_dtype)
+
+
+def layernorm(X, gamma, beta, *, dtype="f32", eps: float = 1e-5, threads: int = 0):
+    """Float64 (Y [rows][C], mean [rows], rstd [rows]) of the row-wise layer normalisation of X."""
+    st = _STORAGE[dtype]
+    X = np.ascontiguousarray(X, dtype=st)
+    gamma = np.ascontiguousarray(gamma, dtype=st)
+    beta = np.ascontiguousarray(beta, dtype=st)
+    rows, C = X.shape
+    if gamma.shape != (C,) or beta.shape != (C,):
+        raise ValueError("gamma and beta must have C elements")
+    Y = np.empty((rows, C), dtype=np.float64)
+    mean = np.empty(rows, dtype=np.float64)
+    rstd = np.empty(rows, dtype=np.float64)
+    dp = ctypes.POINTER(ctypes.c_double)
+    rc = _load().oracle_layernorm(rows, C, _DT[dtype], _ptr(X), _ptr(gamma), _ptr(beta), float(eps),
+                                  Y.ctypes.data_as(dp), mean.ctypes.data_as(dp), rstd.ctypes.data_as(dp), threads)
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return Y, mean, rstd
+
+
+def attention(qkv, n_head: int, *, dtype="f32", causal: bool = True, threads: int = 0):
+    """Float64 (out [B][T][C], lse [B][NH][T]) of scaled dot-product attention over qkv [B][T][3C]."""
+    qkv = np.ascontiguousarray(qkv, dtype=_STORAGE[dtype])
+    B, T, C3 = qkv.shape
+    if C3 % (3 * n_head):
+        raise ValueError("3C must split into three blocks of n_head heads")
+    C = C3 // 3
+    HS = C // n_head
+    out = np.empty((B, T, C), dtype=np.float64)
+    lse = np.empty((B, n_head, T), dtype=np.float64)
+    dp = ctypes.POINTER(ctypes.c_double)
+    rc = _load().oracle_attention(B, T, n_head, HS, _DT[dtype], _ptr(qkv), int(bool(causal)),
+                                  out.ctypes.data_as(dp), lse.ctypes.data_as(dp), threads)
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return out, lse
 
 
 def gelu_tanh(y: float) -> float:

@@ -32,6 +32,10 @@
  *
  * Element formats: 0 = IEEE binary32, 1 = IEEE binary16, 2 = bfloat16 (the
  * upper 16 bits of a binary32).  All are decoded exactly into double here.
+ *
+ * The end of the file holds the two operations that complete a GPT-2 layer
+ * around the GEMMs, written out the same way: layer normalisation and causal
+ * scaled dot-product attention.
  */
 #include <math.h>
 #include <stdint.h>
@@ -155,4 +159,87 @@ int oracle_max_threads(void) {
 #else
     return 1;
 #endif
+}
+
+/* ---- the operations around the GEMMs in a GPT-2 layer ----------------------------
+ *
+ * Layer normalisation of each row of X [rows][C] ("mage-003: What the kernels
+ * were short of", the layer-normalisation section): mean and biased variance
+ * over the row, in double, k ascending; y = (x - mean) / sqrt(var + eps) *
+ * gamma + beta.  Y, mean and rstd = 1/sqrt(var + eps) stay double.
+ */
+int oracle_layernorm(int64_t rows, int64_t C, int dtype, const void* X, const void* gamma, const void* beta,
+                     double eps, double* Y, double* mean, double* rstd, int nthreads) {
+    if (rows < 1 || C < 1 || !X || !gamma || !beta || !Y || (dtype != OR_F32 && dtype != OR_F16 && dtype != OR_BF16))
+        return -1;
+    set_threads(nthreads);
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        double s = 0.0;
+        for (int64_t c = 0; c < C; ++c) s += load(X, r * C + c, dtype);
+        const double mu = s / (double)C;
+        double v = 0.0;
+        for (int64_t c = 0; c < C; ++c) {
+            const double d = load(X, r * C + c, dtype) - mu;
+            v += d * d;
+        }
+        const double rs = 1.0 / sqrt(v / (double)C + eps);
+        for (int64_t c = 0; c < C; ++c)
+            Y[r * C + c] = (load(X, r * C + c, dtype) - mu) * rs * load(gamma, c, dtype) + load(beta, c, dtype);
+        if (mean) mean[r] = mu;
+        if (rstd) rstd[r] = rs;
+    }
+    return 0;
+}
+
+/*
+ * Scaled dot-product attention over the output of the qkv projection
+ * ("Optimizing a GPT-2-class transformer on a GPU", section "Fusing attention:
+ * the score matrix never exists"): qkv is [B][T][3C] with C = NH * HS, the
+ * query of head h at columns h*HS .. h*HS+HS-1, its key C further and its
+ * value 2C further.  For each (b, h, i):
+ *   s_j = scale * sum_d q[i][d] k[j][d]   for j <= i (causal) or every j,
+ *   m = max_j s_j,  l = sum_j exp(s_j - m),  lse = m + log(l),
+ *   out[b][i][h*HS + d] = sum_j exp(s_j - m) / l * v[j][d],
+ * with scale = 1/sqrt(HS) (the pages print no scale; the usual one is the
+ * reading taken).  Sums in double, j ascending.  out is [B][T][C], lse [B][NH][T].
+ */
+int oracle_attention(int64_t B, int64_t T, int64_t NH, int64_t HS, int dtype, const void* qkv, int causal,
+                     double* out, double* lse, int nthreads) {
+    if (B < 1 || T < 1 || NH < 1 || HS < 1 || !qkv || !out || (dtype != OR_F32 && dtype != OR_F16 && dtype != OR_BF16))
+        return -1;
+    const int64_t C = NH * HS, C3 = 3 * C;
+    const double scale = 1.0 / sqrt((double)HS);
+    set_threads(nthreads);
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t h = 0; h < NH; ++h) {
+            for (int64_t i = 0; i < T; ++i) {
+                const int64_t jend = causal ? i + 1 : T;
+                const int64_t qrow = (b * T + i) * C3 + h * HS;
+                double m = -INFINITY;
+                for (int64_t j = 0; j < jend; ++j) {
+                    const int64_t krow = (b * T + j) * C3 + C + h * HS;
+                    double d = 0.0;
+                    for (int64_t e = 0; e < HS; ++e) d += load(qkv, qrow + e, dtype) * load(qkv, krow + e, dtype);
+                    d *= scale;
+                    if (d > m) m = d;
+                }
+                double l = 0.0;
+                double* o = out + (b * T + i) * C + h * HS;
+                for (int64_t e = 0; e < HS; ++e) o[e] = 0.0;
+                for (int64_t j = 0; j < jend; ++j) {
+                    const int64_t krow = (b * T + j) * C3 + C + h * HS, vrow = (b * T + j) * C3 + 2 * C + h * HS;
+                    double d = 0.0;
+                    for (int64_t e = 0; e < HS; ++e) d += load(qkv, qrow + e, dtype) * load(qkv, krow + e, dtype);
+                    const double p = exp(d * scale - m);
+                    l += p;
+                    for (int64_t e = 0; e < HS; ++e) o[e] += p * load(qkv, vrow + e, dtype);
+                }
+                for (int64_t e = 0; e < HS; ++e) o[e] /= l;
+                if (lse) lse[(b * NH + h) * T + i] = m + log(l);
+            }
+        }
+    }
+    return 0;
 }
