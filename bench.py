@@ -470,6 +470,54 @@ def bench_backward(torch, dev, stream, dtype: str, no_parity: bool, reps: int = 
                       "dW accumulates onto itself from pass to pass"}
 
 
+def bench_layer_ops(torch, dev, stream, dtype: str, no_parity: bool, reps: int = 50):
+    """LayerNorm over the GPT-2-small stack's 8192 x 768 activations and fused causal attention over its
+    64 x 128 x 12-head qkv projection: HBM-bound, so bytes per launch against 8 TB/s."""
+    from dense_gemm_transformer_amd import inputs, layer
+
+    es = 4 if dtype == "f32" else 2
+    X, g, b = inputs.workload_gpt2_layernorm(dtype=dtype)
+    rows, C = X.shape
+    dX, dg, db = (dev_tensor(torch, a, dtype, dev) for a in (X, g, b))
+    dY = torch.empty_like(dX)
+    ln = lambda: layer.tlg_layernorm(dX.data_ptr(), dg.data_ptr(), db.data_ptr(), dY.data_ptr(), 0, 0, rows, C,
+                                     1e-5, dtype, stream.cuda_stream)
+    B, T, NH, HS = 64, 128, 12, 64
+    qkv = inputs.workload_gpt2_attention(B=B, T=T, n_head=NH, head_size=HS, dtype=dtype)
+    dqkv = dev_tensor(torch, qkv, dtype, dev)
+    dout = torch.empty((B, T, NH * HS), dtype=dqkv.dtype, device=dev)
+    att = lambda: layer.tlg_attention(dqkv.data_ptr(), dout.data_ptr(), 0, B, T, NH, HS, dtype, True,
+                                      stream.cuda_stream)
+    res = {}
+    for name, fn, nbytes, flops in (
+            ("layernorm_8192x768", ln, rows * C * 2 * es + 2 * C * es, None),
+            ("attention_b64_t128_h12", att, B * T * 4 * NH * HS * es, 4 * B * NH * HS * T * (T + 1) // 2)):
+        fn()
+        torch.cuda.synchronize()
+        us = time_launches(lambda i: fn(), reps, stream) * 1e3
+        r = {"us": round(us, 3), "GB/s": round(nbytes / us / 1e3, 1),
+             "roofline": {"bound": "hbm", "achieved": round(nbytes / us / 1e3, 1), "peak": PEAK_HBM_GBS,
+                          "unit": "GB/s", "frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4),
+                          "algorithmic_bytes_per_launch": nbytes}}
+        if flops:
+            r["TFLOP/s"] = round(flops / us / 1e6, 2)
+        res[name] = r
+    if not no_parity:
+        import oracle
+
+        ref, _, _ = oracle.layernorm(X, g, b, dtype=dtype)
+        res["layernorm_8192x768"]["parity_err"] = oracle.normalized_error(host_f64(torch, dY), ref)
+        ref, _ = oracle.attention(qkv[:4], NH, dtype=dtype)  # the first 4 sequences
+        res["attention_b64_t128_h12"]["parity_err"] = oracle.normalized_error(host_f64(torch, dout)[:4], ref)
+        tol = 1e-5 if dtype == "f32" else 1e-2
+        for k in res:
+            res[k]["parity_pass"] = res[k]["parity_err"] <= tol
+    res["timing"] = f"HIP events over {reps} back-to-back launches on one stream (includes launch gaps)"
+    res["workload"] = (f"GPT-2-small layer ops, {dtype}: LayerNorm of X [{rows}][{C}] (gamma, beta), fused causal "
+                       f"attention over qkv [{B}][{T}][{3 * NH * HS}] ({NH} heads of {HS}), no lse")
+    return res
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -577,6 +625,9 @@ def main(argv=None) -> int:
             log(f"GPT-2 stack at M=8192, {dt}")
             extra[f"gpt2_stack_m8192_{dt}"] = bench_c5(torch, dev, stream, dt, args.no_parity)
             torch.cuda.empty_cache()
+        for dt in ("f32", "bf16"):
+            log(f"GPT-2 layer ops (LayerNorm, attention), {dt}")
+            extra[f"gpt2_layer_ops_{dt}"] = bench_layer_ops(torch, dev, stream, dt, args.no_parity)
         for dt in ("f32", "bf16"):
             log(f"GPT-2 backward GEMMs at 8192 tokens, {dt}")
             extra[f"gpt2_backward_t8192_{dt}"] = bench_backward(torch, dev, stream, dt, args.no_parity)

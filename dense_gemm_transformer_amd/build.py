@@ -37,6 +37,7 @@ SOURCES = [
     "kernels/tiled_f32.hip",
     "kernels/tiled_f16.hip",
     "kernels/tiled_bf16.hip",
+    "layer.hip",
 ]
 HEADERS = ["tlgemm_internal.h", "dispatch_table.inc", "kernels/common.h", "kernels/stream.h",
            "kernels/tiled.h"]
@@ -54,7 +55,8 @@ def hipcc() -> str:
 
 
 def _deps_mtime() -> float:
-    paths = [os.path.join(CSRC, h) for h in HEADERS] + [os.path.join(INCLUDE, "tlgemm.h"), __file__]
+    paths = [os.path.join(CSRC, h) for h in HEADERS] + [os.path.join(INCLUDE, h) for h in ("tlgemm.h", "tlglayer.h")]
+    paths.append(__file__)
     return max(os.path.getmtime(p) for p in paths)
 
 

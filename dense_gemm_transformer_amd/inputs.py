@@ -10,7 +10,8 @@ Recipe (one source of truth for tests and the benchmark):
   a seeded generator but never say which one ("Optimizing a GPT-2-class
   transformer on a GPU", Results), so the draws differ from theirs.
 * Seeds: ``1000 * workload + 10 * layer + tensor`` with tensor X = 1, W = 2,
-  b = 3 (backward: dY = 5, accumulated weight gradient = 6), plus ``100000 * g`` for the g-th linear of a GPT-2 layer (qkv 0,
+  b = 3 (backward: dY = 5, accumulated weight gradient = 6; LayerNorm: X, gamma,
+  beta = 1, 2, 3 of workload 7; attention: qkv = 1 of workload 8), plus ``100000 * g`` for the g-th linear of a GPT-2 layer (qkv 0,
   attn-out 1, fc 2, proj 3), so that no two tensors of a stack share a seed.
 * Values are drawn in float64, rounded to float32 with round-to-nearest-even,
   then (for half formats) rounded again to float16 / bfloat16 with
@@ -192,6 +193,25 @@ def workload_gpt2_stack(workload: int = 5, batch: int = 64, seq: int = 128, laye
     for layer in range(layers):
         out.extend(workload_gpt2_layer(workload, M, dtype, layer))
     return out
+
+
+def normal_around(seed: int, shape, mean: float, std: float, dtype: str) -> np.ndarray:
+    """``mean + N(0, std)`` drawn in float64 and stored like ``normal``."""
+    return store(mean + _rng(seed).standard_normal(shape) * std, dtype)
+
+
+def workload_gpt2_layernorm(workload: int = 7, rows: int = 8192, C: int = 768, dtype: str = "f32"):
+    """LayerNorm input of the GPT-2-small stack: X [rows][C] ~ N(0, 1), gamma ~ 1 + N(0, 0.1), beta ~ N(0, 0.1)."""
+    X = normal(seed_for(workload, 0, TENSOR_X), (rows, C), 1.0, dtype)
+    gamma = normal_around(seed_for(workload, 0, TENSOR_W), (C,), 1.0, 0.1, dtype)
+    beta = normal(seed_for(workload, 0, TENSOR_B), (C,), 0.1, dtype)
+    return X, gamma, beta
+
+
+def workload_gpt2_attention(workload: int = 8, B: int = 64, T: int = 128, n_head: int = 12, head_size: int = 64,
+                            dtype: str = "f32"):
+    """The qkv projection output [B][T][3C] ~ N(0, 1) that GPT-2-small attention reads (C = n_head * head_size)."""
+    return normal(seed_for(workload, 0, TENSOR_X), (B, T, 3 * n_head * head_size), 1.0, dtype)
 
 
 TENSOR_DY, TENSOR_G = 5, 6  # output gradient and the weight gradient accumulated so far
