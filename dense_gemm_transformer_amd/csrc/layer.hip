@@ -57,196 +57,234 @@ __device__ inline float wave_sum(float x) {
 }
 
 // ---- layer normalisation ------------------------------------------------------------
-// 256 threads = 4 waves = 2 rows; waves 2r and 2r+1 hold the two halves of
-// row r.  A lane holds vectors lane, lane+64, ... of its half, so every load
-// instruction of a wave covers 64 consecutive vectors.  Each wave reduces its
-// half's mean and squared deviations from registers; the halves are combined
-// once through LDS with the pairwise update of means and squared deviations
-// (Chan, Golub and LeVeque), which needs no second read of the row.
-constexpr int kLnMaxPerLane = 64;  // values a lane holds: C <= 2 * 64 * 64
+// The pages split a row over two warps so that enough threads are resident to
+// keep loads in flight.  On gfx950 the measure is bytes in flight per CU, so a
+// wave owns whole rows instead, and R rows at a time: a lane holds vectors
+// lane, lane+64, ... of each of its rows (every load instruction of the wave
+// covers 64 consecutive vectors) and issues all of them before the first
+// reduction.  Mean and squared deviations come from registers (two passes
+// over the values, one read of the row); no LDS, no barrier.
+constexpr int kLnMaxPerLane = 64;  // values a lane holds: C <= 64 * 64
 
-template <int DT, int VE>
+template <int DT, int VE, int R>
 __global__ __launch_bounds__(256) void layernorm_kernel(const void* __restrict__ X, const void* __restrict__ gamma,
                                                         const void* __restrict__ beta, void* __restrict__ Y,
                                                         float* __restrict__ mean_out, float* __restrict__ rstd_out,
                                                         int64_t rows, int C, float eps) {
-    constexpr int NVMAX = kLnMaxPerLane / VE;
-    __shared__ float part[2][2][2];  // [row in workgroup][half][mean, squared deviations]
+    constexpr int NVMAX = kLnMaxPerLane / (VE * R);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int rw = wave >> 1, half = wave & 1;
-    const int64_t row = (int64_t)blockIdx.x * 2 + rw;
-    const bool live = row < rows;
-    const int h0 = (C + 1) / 2;  // the first half's length; VE > 1 needs C % (2 VE) == 0
-    const int hstart = half ? h0 : 0, hlen = half ? C - h0 : h0;
-    const int64_t base = row * C + hstart;
-
-    float v[NVMAX][VE];
-    float s = 0.0f;
+    const int64_t row0 = ((int64_t)blockIdx.x * 4 + wave) * R;
+    float v[R][NVMAX][VE];
 #pragma unroll
-    for (int j = 0; j < NVMAX; ++j) {
-        const int e = (lane + 64 * j) * VE;
-        if (live && e < hlen) {
-            load_vec<DT, VE>(X, base + e, v[j]);
+    for (int r = 0; r < R; ++r)
 #pragma unroll
-            for (int u = 0; u < VE; ++u) s += v[j][u];
+        for (int j = 0; j < NVMAX; ++j) {
+            const int e = (lane + 64 * j) * VE;
+            if (row0 + r < rows && e < C) load_vec<DT, VE>(X, (row0 + r) * C + e, v[r][j]);
         }
-    }
-    const float nw = (float)hlen;
-    const float mw = hlen > 0 ? wave_sum(s) / nw : 0.0f;
-    float q = 0.0f;
+    const float inv_c = 1.0f / (float)C;
 #pragma unroll
-    for (int j = 0; j < NVMAX; ++j) {
-        const int e = (lane + 64 * j) * VE;
-        if (live && e < hlen) {
+    for (int r = 0; r < R; ++r) {
+        const int64_t row = row0 + r;
+        if (row >= rows) break;  // wave-uniform
+        float s = 0.0f;
 #pragma unroll
-            for (int u = 0; u < VE; ++u) {
-                const float d = v[j][u] - mw;
-                q += d * d;
+        for (int j = 0; j < NVMAX; ++j)
+            if ((lane + 64 * j) * VE < C)
+#pragma unroll
+                for (int u = 0; u < VE; ++u) s += v[r][j][u];
+        const float mu = wave_sum(s) * inv_c;
+        float q = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NVMAX; ++j)
+            if ((lane + 64 * j) * VE < C)
+#pragma unroll
+                for (int u = 0; u < VE; ++u) {
+                    const float d = v[r][j][u] - mu;
+                    q += d * d;
+                }
+        const float rs = 1.0f / sqrtf(wave_sum(q) * inv_c + eps);
+#pragma unroll
+        for (int j = 0; j < NVMAX; ++j) {
+            const int e = (lane + 64 * j) * VE;
+            if (e < C) {
+                float g[VE], b[VE], y[VE];
+                load_vec<DT, VE>(gamma, e, g);
+                load_vec<DT, VE>(beta, e, b);
+#pragma unroll
+                for (int u = 0; u < VE; ++u) y[u] = (v[r][j][u] - mu) * rs * g[u] + b[u];
+                store_vec<DT, VE>(Y, row * C + e, y);
             }
         }
-    }
-    const float m2w = wave_sum(q);
-    if (lane == 0) {
-        part[rw][half][0] = mw;
-        part[rw][half][1] = m2w;
-    }
-    __syncthreads();
-    // Both waves combine the halves in the same order, so they agree exactly.
-    const float n0 = (float)h0, n1 = (float)(C - h0), n = (float)C;
-    const float mu0 = part[rw][0][0], mu1 = part[rw][1][0];
-    const float delta = mu1 - mu0;
-    const float mu = mu0 + delta * (n1 / n);
-    const float m2 = part[rw][0][1] + part[rw][1][1] + delta * delta * (n0 * n1 / n);
-    const float rs = 1.0f / sqrtf(m2 / n + eps);
-    if (!live) return;
-#pragma unroll
-    for (int j = 0; j < NVMAX; ++j) {
-        const int e = (lane + 64 * j) * VE;
-        if (e < hlen) {
-            float g[VE], b[VE], y[VE];
-            load_vec<DT, VE>(gamma, hstart + e, g);
-            load_vec<DT, VE>(beta, hstart + e, b);
-#pragma unroll
-            for (int u = 0; u < VE; ++u) y[u] = (v[j][u] - mu) * rs * g[u] + b[u];
-            store_vec<DT, VE>(Y, base + e, y);
+        if (lane == 0) {
+            if (mean_out) mean_out[row] = mu;
+            if (rstd_out) rstd_out[row] = rs;
         }
-    }
-    if (half == 0 && lane == 0) {
-        if (mean_out) mean_out[row] = mu;
-        if (rstd_out) rstd_out[row] = rs;
     }
 }
 
 // ---- fused causal attention ------------------------------------------------------------
-// One workgroup per (batch, head).  The head's keys and values are converted
-// to fp32 into LDS once; 256 threads take 128 query rows at a time, two lanes
-// per row, each lane holding 32 of the 64 dimensions of q and of the output.
-// Keys are visited in blocks of 8 up to the last row of the wave (causality
-// as a loop bound); lanes mask keys past their own row.  The softmax runs
-// online in base 2: q is pre-scaled by log2(e)/sqrt(64), each block raises
-// the running maximum and rescales the running sum and output by
-// exp2(m_old - m_new), and the output is divided by the sum once at the end.
-constexpr int kHeadSize = 64, kKeyBlock = 8;
+// One workgroup per (batch, head) with four waves; each wave takes 32 query
+// rows at a time.  The head's keys and values are converted to fp32 into LDS
+// once.  For each block of 32 keys up to the wave's last row (causality as a
+// loop bound):
+//  * S = Q Kᵀ with fp32 MFMA (Q in registers, pre-scaled by log2(e)/sqrt(64);
+//    16-byte key fragments from LDS) lands in the accumulator layout, where a
+//    lane holds one key column of 16 rows;
+//  * the wave passes S through its LDS tile into the operand layout, where a
+//    lane holds 16 keys of one row: masking, the row maximum (16 local
+//    maxima and one exchange between the two half-waves), the rescaling
+//    factor exp2(m_old - m_new), P = exp2(S - m_new) and the lane's partial
+//    row sum are all per-lane work, and P is already the A operand of P V;
+//  * the 32 rescaling factors return through the tile to the accumulator
+//    layout of the output, which is rescaled before O += P V.
+// The row sums meet at the end the same way.
+//
+// LDS layouts, XOR-swizzled so that the reads are conflict-free without
+// padding (keys, values and four 32x32 tiles fill exactly 80 KiB, two
+// workgroups per CU at T <= 128): key row j holds its sixteen 16-byte
+// chunks at chunk ^ (j % 16); value (j, d) sits at column d ^ 32 for rows
+// with bit 4 of j set; tile (m, n) at column n ^ 4 (m % 8).
+constexpr int kHeadSize = 64, kKeyBlock = 32;
+
+__device__ inline int k_at(int j, int chunk) { return j * kHeadSize + ((chunk ^ (j & 15)) << 2); }
+__device__ inline int v_at(int j, int d) { return j * kHeadSize + (d ^ (((j >> 4) & 1) << 5)); }
+__device__ inline int p_at(int m, int n) { return m * 32 + (n ^ ((m & 7) << 2)); }
 
 template <int DT, bool CAUSAL, int TMAX>
 __global__ __launch_bounds__(256) void attention_kernel(const void* __restrict__ qkv, void* __restrict__ out,
                                                         float* __restrict__ lse, int T, int NH) {
-    constexpr int HS = kHeadSize, HH = HS / 2;
+    constexpr int HS = kHeadSize;
     constexpr int EPV = Elem<DT>::per16;  // elements per 16-byte vector
-    __shared__ __attribute__((aligned(16))) float kv[2 * TMAX * HS];
-    float* Ks = kv;
-    float* Vs = kv + TMAX * HS;
+    __shared__ __attribute__((aligned(16))) float Ks[TMAX * HS];
+    __shared__ __attribute__((aligned(16))) float Vs[TMAX * HS];
+    __shared__ __attribute__((aligned(16))) float Ps[4 * 32 * 32];
     const int bh = blockIdx.x, b = bh / NH, h = bh % NH;
     const int64_t C = (int64_t)NH * HS, C3 = 3 * C;
     const int64_t head = (int64_t)b * T * C3 + (int64_t)h * HS;  // q of row 0 of this head
 
-    // keys and values: T rows of HS elements each, 16-byte vectors
-    constexpr int VPR = HS / EPV;
+    constexpr int VPR = HS / EPV;  // 16-byte vectors per row
     for (int idx = threadIdx.x; idx < 2 * T * VPR; idx += 256) {
-        const int which = idx / (T * VPR), rem = idx % (T * VPR), j = rem / VPR, c = (rem % VPR) * EPV;
+        const int which = idx / (T * VPR), rem = idx % (T * VPR), j = rem / VPR, c0 = (rem % VPR) * EPV;
         float f[EPV];
-        load_vec<DT, EPV>(qkv, head + (int64_t)j * C3 + (which + 1) * C + c, f);
-        float* dst = (which ? Vs : Ks) + j * HS + c;
+        load_vec<DT, EPV>(qkv, head + (int64_t)j * C3 + (which + 1) * C + c0, f);
 #pragma unroll
-        for (int u = 0; u < EPV; u += 4) *reinterpret_cast<f32x4*>(dst + u) = f32x4{f[u], f[u + 1], f[u + 2], f[u + 3]};
+        for (int u = 0; u < EPV; u += 4) {
+            const f32x4 x = {f[u], f[u + 1], f[u + 2], f[u + 3]};
+            float* dst = which ? Vs + v_at(j, c0 + u) : Ks + k_at(j, (c0 + u) >> 2);
+            *reinterpret_cast<f32x4*>(dst) = x;
+        }
     }
     __syncthreads();
 
-    const int wave = threadIdx.x >> 6;
-    const int half = threadIdx.x & 1;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, r = lane & 31, g = lane >> 5;
+    float* P = Ps + wave * 1024;
     const float qscale = 1.4426950408889634f / 8.0f;  // log2(e) / sqrt(64)
+    // the 16 accumulator rows of this lane: 8q + 4g + i, read from a tile row as four 16-byte runs
+    auto gather_rows = [&](float (&dst)[16]) {
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(P + p_at(0, 8 * qd + 4 * g));
+            dst[4 * qd] = x[0], dst[4 * qd + 1] = x[1], dst[4 * qd + 2] = x[2], dst[4 * qd + 3] = x[3];
+        }
+    };
     for (int qb = 0; qb < T; qb += 128) {
-        const int i = qb + (threadIdx.x >> 1);
-        const bool live = i < T;
-        const int row_last = min(T - 1, qb + wave * 32 + 31);  // the wave's last query row
-        if (qb + wave * 32 >= T) break;
-        float q[HH], o[HH];
-        if (live) {
+        const int row0 = qb + wave * 32;
+        if (row0 >= T) break;  // wave-uniform
+        const int myrow = row0 + r;  // the row this lane holds in the operand layout
+        // A operand of S: row myrow, head dimensions g*32 .. g*32+31
+        float q[32];
 #pragma unroll
-            for (int c = 0; c < HH; c += EPV) load_vec<DT, EPV>(qkv, head + (int64_t)i * C3 + half * HH + c, q + c);
-        } else {
+        for (int c = 0; c < 32; c += EPV)
+            load_vec<DT, EPV>(qkv, head + (int64_t)min(myrow, T - 1) * C3 + g * 32 + c, q + c);
 #pragma unroll
-            for (int c = 0; c < HH; ++c) q[c] = 0.0f;
-        }
+        for (int c = 0; c < 32; ++c) q[c] *= qscale;
+        f32x16 o0, o1;
 #pragma unroll
-        for (int c = 0; c < HH; ++c) {
-            q[c] *= qscale;
-            o[c] = 0.0f;
-        }
-        float m = -INFINITY, l = 0.0f;
-        const int jend = CAUSAL ? row_last + 1 : T;
-        for (int j0 = 0; j0 < jend; j0 += kKeyBlock) {
-            float s[kKeyBlock];
+        for (int e = 0; e < 16; ++e) o0[e] = o1[e] = 0.0f;
+        float m = -INFINITY, lp = 0.0f;  // running maximum and this lane's part of the row sum
+        const int kend = CAUSAL ? min(T, row0 + 32) : T;
+        for (int j0 = 0; j0 < kend; j0 += kKeyBlock) {
+            const int kr = min(j0 + r, T - 1);
+            f32x16 sacc;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) sacc[e] = 0.0f;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const f32x4 kv = *reinterpret_cast<const f32x4*>(Ks + k_at(kr, g * 8 + t));
+#pragma unroll
+                for (int u = 0; u < 4; ++u) sacc = mfma32_f32(q[4 * t + u], kv[u], sacc);
+            }
+            // accumulator layout -> operand layout through the wave's tile.  The tile is reused for the
+            // rescaling factors; LDS operations of one wave complete in issue order, and the empty asm
+            // statements keep the compiler from reordering these accesses across each other.
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int e = 0; e < 16; ++e) P[p_at(8 * (e >> 2) + 4 * g + (e & 3), r)] = sacc[e];
+            float p[16];
+#pragma unroll
+            for (int k4 = 0; k4 < 4; ++k4) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(P + p_at(r, g * 16 + 4 * k4));
+                p[4 * k4] = x[0], p[4 * k4 + 1] = x[1], p[4 * k4 + 2] = x[2], p[4 * k4 + 3] = x[3];
+            }
             float bm = -INFINITY;
 #pragma unroll
-            for (int kk = 0; kk < kKeyBlock; ++kk) {
-                const int j = j0 + kk;
-                const float* kr = Ks + min(j, T - 1) * HS + half * HH;
-                float part = 0.0f;
-#pragma unroll
-                for (int c = 0; c < HH; c += 4) {
-                    const f32x4 kv4 = *reinterpret_cast<const f32x4*>(kr + c);
-                    part = fmaf(q[c], kv4[0], part);
-                    part = fmaf(q[c + 1], kv4[1], part);
-                    part = fmaf(q[c + 2], kv4[2], part);
-                    part = fmaf(q[c + 3], kv4[3], part);
-                }
-                const float full = part + __shfl_xor(part, 1, 64);
-                const bool keep = live && j < T && (!CAUSAL || j <= i);
-                s[kk] = keep ? full : -INFINITY;
-                bm = fmaxf(bm, s[kk]);
+            for (int c = 0; c < 16; ++c) {
+                const int key = j0 + g * 16 + c;
+                const bool keep = key < T && myrow < T && (!CAUSAL || key <= myrow);
+                p[c] = keep ? p[c] : -INFINITY;
+                bm = fmaxf(bm, p[c]);
             }
+            bm = fmaxf(bm, __shfl_xor(bm, 32, 64));  // the other half of the row
             const float mn = fmaxf(m, bm);
-            if (mn == -INFINITY) continue;  // nothing visible yet in this row
-            const float corr = __builtin_amdgcn_exp2f(m - mn);  // 0 while m is still -inf
-            l *= corr;
-#pragma unroll
-            for (int c = 0; c < HH; ++c) o[c] *= corr;
-#pragma unroll
-            for (int kk = 0; kk < kKeyBlock; ++kk) {
-                const float p = __builtin_amdgcn_exp2f(s[kk] - mn);  // 0 for masked keys
-                l += p;
-                const float* vr = Vs + min(j0 + kk, T - 1) * HS + half * HH;
-#pragma unroll
-                for (int c = 0; c < HH; c += 4) {
-                    const f32x4 vv = *reinterpret_cast<const f32x4*>(vr + c);
-                    o[c] = fmaf(p, vv[0], o[c]);
-                    o[c + 1] = fmaf(p, vv[1], o[c + 1]);
-                    o[c + 2] = fmaf(p, vv[2], o[c + 2]);
-                    o[c + 3] = fmaf(p, vv[3], o[c + 3]);
-                }
-            }
+            const float ms = mn == -INFINITY ? 0.0f : mn;  // a row with nothing visible yet stays at zero
+            const float corr = __builtin_amdgcn_exp2f(m - ms);
             m = mn;
+            float ps = 0.0f;
+#pragma unroll
+            for (int c = 0; c < 16; ++c) {
+                p[c] = __builtin_amdgcn_exp2f(p[c] - ms);
+                ps += p[c];
+            }
+            lp = lp * corr + ps;
+            // rescaling factors back to the accumulator rows
+            asm volatile("" ::: "memory");
+            if (g == 0) P[p_at(0, r)] = corr;
+            asm volatile("" ::: "memory");
+            float cr[16];
+            gather_rows(cr);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                o0[e] *= cr[e];
+                o1[e] *= cr[e];
+            }
+            // O += P V: keys g*16 + 4 k4 + u of this block
+#pragma unroll
+            for (int k4 = 0; k4 < 4; ++k4)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int vr = min(j0 + g * 16 + 4 * k4 + u, T - 1);  // masked keys carry p = 0
+                    o0 = mfma32_f32(p[4 * k4 + u], Vs[v_at(vr, r)], o0);
+                    o1 = mfma32_f32(p[4 * k4 + u], Vs[v_at(vr, 32 + r)], o1);
+                }
         }
-        if (live) {
-            const float inv = 1.0f / l;
+        const float l = lp + __shfl_xor(lp, 32, 64);
+        if (g == 0 && lse && myrow < T)
+            lse[((int64_t)b * NH + h) * T + myrow] = (m + __builtin_amdgcn_logf(l)) * 0.6931471805599453f;
+        asm volatile("" ::: "memory");
+        if (g == 0) P[p_at(0, r)] = 1.0f / l;
+        asm volatile("" ::: "memory");
+        float inv[16];
+        gather_rows(inv);
 #pragma unroll
-            for (int c = 0; c < HH; ++c) o[c] *= inv;
-            const int64_t orow = ((int64_t)b * T + i) * C + (int64_t)h * HS + half * HH;
-#pragma unroll
-            for (int c = 0; c < HH; c += EPV) store_vec<DT, EPV>(out, orow + c, o + c);
-            // log-sum-exp in natural units: (m + log2 l) * ln 2
-            if (lse && half == 0) lse[((int64_t)b * NH + h) * T + i] = (m + __builtin_amdgcn_logf(l)) * 0.6931471805599453f;
+        for (int e = 0; e < 16; ++e) {
+            const int row = row0 + 8 * (e >> 2) + 4 * g + (e & 3);
+            if (row < T) {
+                const int64_t orow = ((int64_t)b * T + row) * C + (int64_t)h * HS;
+                const float y0 = o0[e] * inv[e], y1 = o1[e] * inv[e];
+                store_vec<DT, 1>(out, orow + r, &y0);
+                store_vec<DT, 1>(out, orow + 32 + r, &y1);
+            }
         }
     }
 }
@@ -257,29 +295,39 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     return x < y + nb && y < x + na;
 }
 
-template <int DT, int VE>
+template <int DT, int VE, int R>
 int launch_layernorm(const void* X, const void* g, const void* b, void* Y, float* mean, float* rstd, int64_t rows,
                      int C, float eps, hipStream_t s) {
-    const int64_t grid = (rows + 1) / 2;
-    hipLaunchKernelGGL((layernorm_kernel<DT, VE>), dim3((unsigned)grid), dim3(256), 0, s, X, g, b, Y, mean, rstd,
+    const int64_t grid = (rows + 4 * R - 1) / (4 * R);
+    hipLaunchKernelGGL((layernorm_kernel<DT, VE, R>), dim3((unsigned)grid), dim3(256), 0, s, X, g, b, Y, mean, rstd,
                        rows, C, eps);
     return check_launch("layernorm_kernel");
+}
+
+// Rows per wave: as many as the 64 values a lane holds allow, up to four.
+template <int DT, int VE>
+int layernorm_ve(const void* X, const void* g, const void* b, void* Y, float* mean, float* rstd, int64_t rows, int C,
+                 float eps, hipStream_t s) {
+    const int per_row = (C + 64 * VE - 1) / (64 * VE) * VE;  // values per lane per row
+    if (per_row * 4 <= kLnMaxPerLane) return launch_layernorm<DT, VE, 4>(X, g, b, Y, mean, rstd, rows, C, eps, s);
+    if (per_row * 2 <= kLnMaxPerLane) return launch_layernorm<DT, VE, 2>(X, g, b, Y, mean, rstd, rows, C, eps, s);
+    return launch_layernorm<DT, VE, 1>(X, g, b, Y, mean, rstd, rows, C, eps, s);
 }
 
 template <int DT>
 int layernorm_dt(const void* X, const void* g, const void* b, void* Y, float* mean, float* rstd, int64_t rows,
                  int C, float eps, hipStream_t s) {
     constexpr int es = (int)sizeof(typename Elem<DT>::storage);
-    // the widest vector that divides both halves and keeps every access aligned
+    // the widest vector that divides the row and keeps every access aligned
     auto fits = [&](int ve) {
         const size_t a = (size_t)ve * es;
-        return C % (2 * ve) == 0 && aligned(X, a) && aligned(Y, a) && aligned(g, a) && aligned(b, a);
+        return C % ve == 0 && aligned(X, a) && aligned(Y, a) && aligned(g, a) && aligned(b, a);
     };
     if constexpr (es == 2)
-        if (fits(8)) return launch_layernorm<DT, 8>(X, g, b, Y, mean, rstd, rows, C, eps, s);
-    if (fits(4)) return launch_layernorm<DT, 4>(X, g, b, Y, mean, rstd, rows, C, eps, s);
-    if (fits(2)) return launch_layernorm<DT, 2>(X, g, b, Y, mean, rstd, rows, C, eps, s);
-    return launch_layernorm<DT, 1>(X, g, b, Y, mean, rstd, rows, C, eps, s);
+        if (fits(8)) return layernorm_ve<DT, 8>(X, g, b, Y, mean, rstd, rows, C, eps, s);
+    if (fits(4)) return layernorm_ve<DT, 4>(X, g, b, Y, mean, rstd, rows, C, eps, s);
+    if (fits(2)) return layernorm_ve<DT, 2>(X, g, b, Y, mean, rstd, rows, C, eps, s);
+    return layernorm_ve<DT, 1>(X, g, b, Y, mean, rstd, rows, C, eps, s);
 }
 
 template <int DT, bool CAUSAL>
@@ -304,8 +352,8 @@ int tlg_layernorm(const void* X, const void* gamma, const void* beta, void* Y, f
         set_error("tlg_layernorm: NULL pointer, rows or C < 1, eps < 0 or unknown dtype");
         return TLG_ERR_INVALID_ARG;
     }
-    if (C > 2 * 64 * kLnMaxPerLane || rows >= (int64_t(1) << 32)) {
-        set_error("tlg_layernorm: C = %lld exceeds %d (or too many rows)", (long long)C, 2 * 64 * kLnMaxPerLane);
+    if (C > 64 * kLnMaxPerLane || rows >= (int64_t(1) << 32)) {
+        set_error("tlg_layernorm: C = %lld exceeds %d (or too many rows)", (long long)C, 64 * kLnMaxPerLane);
         return TLG_ERR_UNSUPPORTED;
     }
     const size_t es = dt == TLG_F32 ? 4 : 2;

@@ -27,14 +27,14 @@ extern "C" {
  * row variance and rstd_r = 1/sqrt(var_r + eps).
  *
  * The layer normalisation of "mage-003: What the kernels were short of"
- * (layer-normalisation section): two waves share a row, each holding half of
- * it in registers; the statistics come from that single read of the row and
- * the two halves meet once through LDS.
+ * (layer-normalisation section), whose statistics come from a single read of
+ * the row held in registers; here a wave holds up to four whole rows, so
+ * that each lane has all of their loads in flight at once.
  *
  * X, Y: [rows][C] row-major; gamma, beta: [C]; all of type dt.  mean and
  * rstd: [rows] fp32, each may be NULL (not written).  Y must not overlap X,
- * gamma or beta.  Requires rows >= 1, 1 <= C <= 8192, eps >= 0, every pointer
- * aligned to its element size (TLG_ERR_MISALIGNED otherwise); C > 8192 is
+ * gamma or beta.  Requires rows >= 1, 1 <= C <= 4096, eps >= 0, every pointer
+ * aligned to its element size (TLG_ERR_MISALIGNED otherwise); C > 4096 is
  * TLG_ERR_UNSUPPORTED.
  */
 int tlg_layernorm(const void* X, const void* gamma, const void* beta, void* Y, float* mean, float* rstd,

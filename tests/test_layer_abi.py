@@ -35,7 +35,7 @@ def test_layernorm_argument_errors():
     assert _ln(G, G + 8192, G + 16384, 3 * G, None, None, 0, 768, 1e-5, t.F32, None) == t.ERR_INVALID_ARG
     assert _ln(G, 2 * G, 3 * G, 4 * G, None, None, 4, 768, -1.0, t.F32, None) == t.ERR_INVALID_ARG
     assert _ln(G, 2 * G, 3 * G, 4 * G, None, None, 4, 768, 1e-5, 7, None) == t.ERR_INVALID_ARG
-    assert _ln(G, 2 * G, 3 * G, 4 * G, None, None, 4, 8193, 1e-5, t.F32, None) == t.ERR_UNSUPPORTED
+    assert _ln(G, 2 * G, 3 * G, 4 * G, None, None, 4, 4097, 1e-5, t.F32, None) == t.ERR_UNSUPPORTED
     assert _ln(G + 2, 2 * G, 3 * G, 4 * G, None, None, 4, 768, 1e-5, t.F32, None) == t.ERR_MISALIGNED
     assert _ln(G, 2 * G, 3 * G, 4 * G, G + 2, None, 4, 768, 1e-5, t.F32, None) == t.ERR_MISALIGNED
     assert _ln(G, 2 * G, 3 * G, G + 64, None, None, 4, 768, 1e-5, t.F32, None) == t.ERR_INVALID_ARG  # Y overlaps X

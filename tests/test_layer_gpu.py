@@ -29,7 +29,7 @@ def _ln_check(rows, C, dtype, seed=0, eps=1e-5):
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 def test_layernorm_shapes(dtype):
     # odd rows (a half-empty last workgroup), odd C (unequal halves, scalar path), vector paths, the limit
-    for rows, C in [(1, 1), (3, 7), (5, 768), (17, 1000), (2, 2), (4, 6), (3, 8192), (33, 1600)]:
+    for rows, C in [(1, 1), (3, 7), (5, 768), (17, 1000), (2, 2), (4, 6), (3, 4096), (33, 1600), (9, 4000)]:
         _ln_check(rows, C, dtype, seed=rows + C)
 
 
