@@ -22,7 +22,9 @@ linears at M = 128 (fp32), each warm and as a layer warm and cold; and one
 pass of the batched GPT-2-small stack at M = 8192 (12 layers × 4 linears, 48
 launches) in fp32 and bf16, with tokens/s; and the backward GEMMs of one
 GPT-2-small layer at 8192 tokens (dX with the [K][N] weight layout, dW with the
-transposed first operand accumulated onto the previous gradient).
+transposed first operand accumulated onto the previous gradient); LayerNorm and
+fused causal attention at GPT-2-small size; and the GPT-2-small forward through
+12 blocks composed from all of them (tokens/s).
 
 The oracle (plain C, double accumulation) is timed on this host's cores on
 a bounded row sample of the square workload and reported as
@@ -518,6 +520,64 @@ def bench_layer_ops(torch, dev, stream, dtype: str, no_parity: bool, reps: int =
     return res
 
 
+def bench_gpt2_forward(torch, dev, stream, dtype: str, no_parity: bool, layers: int = 12, reps: int = 10):
+    """GPT-2-small forward through ``layers`` transformer blocks at 64 x 128 tokens: per block two LayerNorms,
+    the qkv projection, fused causal attention, the attention output projection and proj with the residual
+    fused, fc with GELU (7 launches; embeddings, final LayerNorm and logits excluded)."""
+    from dense_gemm_transformer_amd import block, inputs
+
+    B, T, C, NH = 64, 128, 768, 12
+    shape = block.BlockShape(B, T, C, NH, dtype)
+    blocks = []
+    params0 = None
+    for li in range(layers):
+        P = inputs.gpt2_block_params(10, li, C, dtype)
+        if li == 0:
+            params0 = P
+        blocks.append(block.GPT2Block(shape, {k: dev_tensor(torch, v, dtype, dev) for k, v in P.items()}))
+    x0 = inputs.normal(inputs.seed_for(10, 0, 1), (B * T, C), 1.0, dtype)
+    x = dev_tensor(torch, x0, dtype, dev)
+    res = {}
+    if not no_parity:  # the first block on a fresh input, its first two sequences against the oracle stages
+        import oracle
+
+        blocks[0].forward(x, stream.cuda_stream)
+        torch.cuda.synchronize()
+        st = lambda a: inputs.store(a, dtype)
+        rows = 2 * T
+        xs = x0[:rows]
+        Pp = params0
+        h, _, _ = oracle.layernorm(xs, Pp["ln1_g"], Pp["ln1_b"], dtype=dtype)
+        qkv = oracle.linear(st(h), Pp["w_qkv"], Pp["b_qkv"], dtype=dtype)
+        att, _ = oracle.attention(st(qkv).reshape(2, T, -1), NH, dtype=dtype)
+        x1 = oracle.linear(st(att.reshape(rows, -1)), Pp["w_attn"], Pp["b_attn"], dtype=dtype, residual=xs)
+        h2, _, _ = oracle.layernorm(st(x1), Pp["ln2_g"], Pp["ln2_b"], dtype=dtype)
+        f = oracle.linear(st(h2), Pp["w_fc"], Pp["b_fc"], dtype=dtype, gelu=True)
+        ref = oracle.linear(st(f), Pp["w_proj"], Pp["b_proj"], dtype=dtype, residual=st(x1))
+        res["parity_err_block0"] = oracle.normalized_error(host_f64(torch, x)[:rows], ref)
+        res["parity_pass"] = res["parity_err_block0"] <= (1e-5 if dtype == "f32" else 1e-2)
+        x.copy_(dev_tensor(torch, x0, dtype, dev))
+
+    def one_pass():
+        for blk in blocks:
+            blk.forward(x, stream.cuda_stream)
+
+    for _ in range(2):
+        one_pass()
+    ms = median_span_ms(torch, one_pass, reps, stream)
+    flops = layers * shape.flops()
+    peak = PEAK_F32_TFLOPS if dtype == "f32" else PEAK_BF16_TFLOPS
+    res.update({"workload": f"GPT-2-small forward through {layers} blocks, {B} x {T} tokens, {dtype}: per block "
+                            "LayerNorm, qkv, fused causal attention, attn-out (+residual), LayerNorm, fc+GELU, "
+                            "proj (+residual); no embeddings, final LayerNorm or logits",
+                "pass_ms": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
+                "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2),
+                "frac_mfma_peak": round(flops / (ms * 1e-3) / 1e12 / peak, 4), "flops_per_pass": flops,
+                "launches_per_pass": 7 * layers,
+                "timing": f"median over {reps} passes of the HIP-event span of one pass on one stream"})
+    return res
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -624,6 +684,10 @@ def main(argv=None) -> int:
         for dt in ("f32", "bf16"):
             log(f"GPT-2 stack at M=8192, {dt}")
             extra[f"gpt2_stack_m8192_{dt}"] = bench_c5(torch, dev, stream, dt, args.no_parity)
+            torch.cuda.empty_cache()
+        for dt in ("f32", "bf16"):
+            log(f"GPT-2-small forward, 12 blocks, {dt}")
+            extra[f"gpt2_forward_12x_b64_t128_{dt}"] = bench_gpt2_forward(torch, dev, stream, dt, args.no_parity)
             torch.cuda.empty_cache()
         for dt in ("f32", "bf16"):
             log(f"GPT-2 layer ops (LayerNorm, attention), {dt}")

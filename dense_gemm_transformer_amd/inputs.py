@@ -214,6 +214,25 @@ def workload_gpt2_attention(workload: int = 8, B: int = 64, T: int = 128, n_head
     return normal(seed_for(workload, 0, TENSOR_X), (B, T, 3 * n_head * head_size), 1.0, dtype)
 
 
+def gpt2_block_params(workload: int, layer: int, C: int, dtype: str) -> dict:
+    """One GPT-2 block's parameters (storage arrays): weights and biases ~ N(0, 0.02) as in the linear
+    workloads, layer-norm gains ~ 1 + N(0, 0.1) and shifts ~ N(0, 0.1).  Seed of parameter i (in the order
+    of ``block.PARAM_NAMES``): ``seed_for(workload, layer, 10 + i)``."""
+    shapes = {"ln1_g": (C,), "ln1_b": (C,), "w_qkv": (3 * C, C), "b_qkv": (3 * C,), "w_attn": (C, C),
+              "b_attn": (C,), "ln2_g": (C,), "ln2_b": (C,), "w_fc": (4 * C, C), "b_fc": (4 * C,),
+              "w_proj": (C, 4 * C), "b_proj": (C,)}
+    out = {}
+    for i, (name, shape) in enumerate(shapes.items()):
+        seed = seed_for(workload, layer, 10 + i)
+        if name.endswith("_g"):
+            out[name] = normal_around(seed, shape, 1.0, 0.1, dtype)
+        elif name.startswith("ln"):
+            out[name] = normal(seed, shape, 0.1, dtype)
+        else:
+            out[name] = normal(seed, shape, 0.02, dtype)
+    return out
+
+
 TENSOR_DY, TENSOR_G = 5, 6  # output gradient and the weight gradient accumulated so far
 
 
