@@ -51,7 +51,7 @@ constexpr TileCfg kTiled16[] = {
     {128, 128, 64, 2, 2},   // 0
     {64, 64, 64, 2, 2},     // 1: narrow grids, pairs with split-K
     {256, 128, 64, 2, 2},   // 2
-    {128, 128, 128, 2, 2},  // 3
+    {256, 128, 32, 2, 2},   // 3: short slices; two workgroups per CU fit in LDS (the 64-deep 256x128 tile fits one)
     {256, 256, 64, 2, 2},   // 4
     {256, 256, 64, 2, 4},   // 5: eight waves, two per SIMD: one's stalls are the other's MFMA time
 };
