@@ -28,8 +28,8 @@ extern "C" {
  *
  * The layer normalisation of "mage-003: What the kernels were short of"
  * (layer-normalisation section), whose statistics come from a single read of
- * the row held in registers; here a wave holds up to four whole rows, so
- * that each lane has all of their loads in flight at once.
+ * the row held in registers; here a wave holds two whole rows, so that
+ * each lane has all of their loads in flight at once.
  *
  * X, Y: [rows][C] row-major; gamma, beta: [C]; all of type dt.  mean and
  * rstd: [rows] fp32, each may be NULL (not written).  Y must not overlap X,
