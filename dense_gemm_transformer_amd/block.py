@@ -73,6 +73,8 @@ class GPT2Block:
         self.qkv = torch.empty((M, 3 * C), dtype=tdt, device=dev)
         self.att = torch.empty((M, C), dtype=tdt, device=dev)
         self.fc = torch.empty((M, 4 * C), dtype=tdt, device=dev)
+        # the workspaces were zero-filled on the current stream; forward may run on another one
+        torch.cuda.synchronize(dev)
 
     def _gemm(self, name, X, W, b, Y, stream):
         p = self.plans[name]

@@ -363,9 +363,20 @@ int tlg_layernorm(const void* X, const void* gamma, const void* beta, void* Y, f
         set_error("tlg_layernorm: pointers must be aligned to their element size");
         return TLG_ERR_MISALIGNED;
     }
-    const size_t bytes = (size_t)rows * (size_t)C * es;
+    const size_t bytes = (size_t)rows * (size_t)C * es, sb = (size_t)rows * 4;
     if (overlaps(Y, bytes, X, bytes) || overlaps(Y, bytes, gamma, C * es) || overlaps(Y, bytes, beta, C * es)) {
         set_error("tlg_layernorm: Y overlaps an input");
+        return TLG_ERR_INVALID_ARG;
+    }
+    for (const float* st : {mean, rstd}) {
+        if (st && (overlaps(st, sb, X, bytes) || overlaps(st, sb, Y, bytes) || overlaps(st, sb, gamma, C * es) ||
+                   overlaps(st, sb, beta, C * es))) {
+            set_error("tlg_layernorm: mean or rstd overlaps X, Y, gamma or beta");
+            return TLG_ERR_INVALID_ARG;
+        }
+    }
+    if (mean && rstd && overlaps(mean, sb, rstd, sb)) {
+        set_error("tlg_layernorm: mean overlaps rstd");
         return TLG_ERR_INVALID_ARG;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -392,9 +403,9 @@ int tlg_attention(const void* qkv, void* out, float* lse, int64_t B, int64_t T, 
     }
     const size_t es = dt == TLG_F32 ? 4 : 2;
     const size_t C = (size_t)n_head * head_size;
-    if (overlaps(out, (size_t)B * T * C * es, qkv, (size_t)B * T * 3 * C * es) ||
-        (lse && overlaps(lse, (size_t)B * n_head * T * 4, out, (size_t)B * T * C * es))) {
-        set_error("tlg_attention: out overlaps qkv (or lse overlaps out)");
+    const size_t ob = (size_t)B * T * C * es, qb = (size_t)B * T * 3 * C * es, lb = (size_t)B * n_head * T * 4;
+    if (overlaps(out, ob, qkv, qb) || (lse && (overlaps(lse, lb, out, ob) || overlaps(lse, lb, qkv, qb)))) {
+        set_error("tlg_attention: out overlaps qkv, or lse overlaps out or qkv");
         return TLG_ERR_INVALID_ARG;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);

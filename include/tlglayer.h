@@ -32,8 +32,8 @@ extern "C" {
  * each lane has all of their loads in flight at once.
  *
  * X, Y: [rows][C] row-major; gamma, beta: [C]; all of type dt.  mean and
- * rstd: [rows] fp32, each may be NULL (not written).  Y must not overlap X,
- * gamma or beta.  Requires rows >= 1, 1 <= C <= 4096, eps >= 0, every pointer
+ * rstd: [rows] fp32, each may be NULL (not written).  Y, mean and rstd must
+ * not overlap each other, X, gamma or beta.  Requires rows >= 1, 1 <= C <= 4096, eps >= 0, every pointer
  * aligned to its element size (TLG_ERR_MISALIGNED otherwise); C > 4096 is
  * TLG_ERR_UNSUPPORTED.
  */
@@ -55,7 +55,7 @@ int tlg_layernorm(const void* X, const void* gamma, const void* beta, void* Y, f
  * sum_j p_ij v_j[d] with p_ij = softmax_j(q_i . k_j / sqrt(head_size)) over
  * j <= i (causal != 0) or all j.  lse: [B][n_head][T] fp32, the log-sum-exp
  * of each row of scores (what a backward pass rebuilds the probabilities
- * from), or NULL.  out must not overlap qkv.
+ * from), or NULL.  out and lse must not overlap qkv or each other.
  *
  * Requires B, T, n_head >= 1, head_size == 64, T <= 256 (keys and values of
  * one head stay in LDS), B * n_head < 2^31, qkv and out 16-byte aligned

@@ -39,6 +39,8 @@ def test_layernorm_argument_errors():
     assert _ln(G + 2, 2 * G, 3 * G, 4 * G, None, None, 4, 768, 1e-5, t.F32, None) == t.ERR_MISALIGNED
     assert _ln(G, 2 * G, 3 * G, 4 * G, G + 2, None, 4, 768, 1e-5, t.F32, None) == t.ERR_MISALIGNED
     assert _ln(G, 2 * G, 3 * G, G + 64, None, None, 4, 768, 1e-5, t.F32, None) == t.ERR_INVALID_ARG  # Y overlaps X
+    assert _ln(G, 2 * G, 3 * G, 4 * G, 4 * G + 8, None, 4, 768, 1e-5, t.F32, None) == t.ERR_INVALID_ARG  # mean in Y
+    assert _ln(G, 2 * G, 3 * G, 4 * G, 5 * G, 5 * G + 8, 4, 768, 1e-5, t.F32, None) == t.ERR_INVALID_ARG  # rstd in mean
 
 
 def test_attention_argument_errors():
@@ -50,4 +52,5 @@ def test_attention_argument_errors():
     assert _att(G + 4, 2 * G, None, *ok, t.F32, 1, None) == t.ERR_MISALIGNED
     assert _att(G, 2 * G + 8, None, *ok, t.F32, 1, None) == t.ERR_MISALIGNED
     assert _att(G, G + 1024, None, *ok, t.F32, 1, None) == t.ERR_INVALID_ARG  # out overlaps qkv
+    assert _att(G, 2 * G, G + 4096, *ok, t.F32, 1, None) == t.ERR_INVALID_ARG  # lse overlaps qkv
     assert "head_size 64" in t.gemm_last_error() or "overlaps" in t.gemm_last_error()
