@@ -289,6 +289,155 @@ __global__ __launch_bounds__(256) void attention_kernel(const void* __restrict__
     }
 }
 
+// 16-bit inputs: the same algorithm on v_mfma_f32_32x32x16_{bf16,f16}.  Keys
+// and values stay 16-bit in LDS.  A key row's eight 16-byte chunks sit at
+// chunk ^ ((j/2) % 8) (two 128-byte rows share the 64 banks, so sixteen rows
+// read one chunk each without conflict).  Value rows are padded to 80
+// elements; the B operand of P V (eight consecutive keys of one dimension)
+// comes from two LDS transpose reads, and rows past T are zero so that masked
+// keys (p = 0) multiply finite values.  A lane's 16 keys of a row are
+// 8g..8g+7 and 16+8g..16+8g+7, the two 8-key halves of the P operand.
+constexpr int kVStride16 = 80;
+
+__device__ inline int k16_at(int j, int chunk) { return j * kHeadSize + ((chunk ^ ((j >> 1) & 7)) << 3); }
+
+template <int DT, bool CAUSAL, int TMAX>
+__global__ __launch_bounds__(256) void attention16_kernel(const void* __restrict__ qkv, void* __restrict__ out,
+                                                          float* __restrict__ lse, int T, int NH) {
+    using S = typename Elem<DT>::storage;
+    constexpr int HS = kHeadSize, VST = kVStride16;
+    constexpr int TPAD = (TMAX + 31) / 32 * 32;
+    __shared__ __attribute__((aligned(16))) S Ks[TMAX * HS];
+    __shared__ __attribute__((aligned(16))) S Vs[TPAD * VST];
+    __shared__ __attribute__((aligned(16))) float Ps[4 * 32 * 32];
+    const int bh = blockIdx.x, b = bh / NH, h = bh % NH;
+    const int64_t C = (int64_t)NH * HS, C3 = 3 * C;
+    const int64_t head = (int64_t)b * T * C3 + (int64_t)h * HS;  // q of row 0 of this head
+    const S* X = static_cast<const S*>(qkv);
+
+    // keys and values: 16-byte vectors of 8 elements, copied as they are
+    const int tz = (T + 31) / 32 * 32;  // value rows up to the last key block, zero past T
+    for (int idx = threadIdx.x; idx < (T + tz) * 8; idx += 256) {
+        const bool isv = idx >= T * 8;
+        const int i2 = isv ? idx - T * 8 : idx, j = i2 >> 3, ch = i2 & 7;
+        if (!isv) {
+            *reinterpret_cast<u32x4*>(Ks + k16_at(j, ch)) =
+                *reinterpret_cast<const u32x4*>(X + head + (int64_t)j * C3 + C + ch * 8);
+        } else {
+            const u32x4 v = j < T ? *reinterpret_cast<const u32x4*>(X + head + (int64_t)j * C3 + 2 * C + ch * 8)
+                                  : u32x4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4*>(Vs + j * VST + ch * 8) = v;
+        }
+    }
+    __syncthreads();
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, r = lane & 31, g = lane >> 5;
+    float* P = Ps + wave * 1024;
+    const float sscale = 1.4426950408889634f / 8.0f;  // log2(e) / sqrt(64), applied to the fp32 scores
+    const int tr_row = 8 * g + ((lane & 15) >> 2), tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    auto gather_rows = [&](float (&dst)[16]) {
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(P + p_at(0, 8 * qd + 4 * g));
+            dst[4 * qd] = x[0], dst[4 * qd + 1] = x[1], dst[4 * qd + 2] = x[2], dst[4 * qd + 3] = x[3];
+        }
+    };
+    for (int qb = 0; qb < T; qb += 128) {
+        const int row0 = qb + wave * 32;
+        if (row0 >= T) break;  // wave-uniform
+        const int myrow = row0 + r;
+        // A operand of S, chunk c: row myrow, head dimensions 16c + 8g .. +7
+        u32x4 q[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            q[c] = *reinterpret_cast<const u32x4*>(X + head + (int64_t)min(myrow, T - 1) * C3 + 16 * c + 8 * g);
+        f32x16 o0, o1;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o0[e] = o1[e] = 0.0f;
+        float m = -INFINITY, lp = 0.0f;
+        const int kend = CAUSAL ? min(T, row0 + 32) : T;
+        for (int j0 = 0; j0 < kend; j0 += kKeyBlock) {
+            const int kr = min(j0 + r, T - 1);
+            f32x16 sacc;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) sacc[e] = 0.0f;
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                sacc = mfma32_16bit<DT>(q[c], *reinterpret_cast<const u32x4*>(Ks + k16_at(kr, 2 * c + g)), sacc);
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int e = 0; e < 16; ++e) P[p_at(8 * (e >> 2) + 4 * g + (e & 3), r)] = sacc[e] * sscale;
+            float p[16];  // keys 8g+c (c < 8) and 16+8g+c-8 (c >= 8) of this block
+#pragma unroll
+            for (int k4 = 0; k4 < 4; ++k4) {
+                const int n = (k4 < 2 ? 8 * g : 16 + 8 * g) + 4 * (k4 & 1);
+                const f32x4 x = *reinterpret_cast<const f32x4*>(P + p_at(r, n));
+                p[4 * k4] = x[0], p[4 * k4 + 1] = x[1], p[4 * k4 + 2] = x[2], p[4 * k4 + 3] = x[3];
+            }
+            float bm = -INFINITY;
+#pragma unroll
+            for (int c = 0; c < 16; ++c) {
+                const int key = j0 + (c < 8 ? 8 * g + c : 16 + 8 * g + c - 8);
+                const bool keep = key < T && myrow < T && (!CAUSAL || key <= myrow);
+                p[c] = keep ? p[c] : -INFINITY;
+                bm = fmaxf(bm, p[c]);
+            }
+            bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+            const float mn = fmaxf(m, bm);
+            const float ms = mn == -INFINITY ? 0.0f : mn;
+            const float corr = __builtin_amdgcn_exp2f(m - ms);
+            m = mn;
+            float ps = 0.0f;
+#pragma unroll
+            for (int c = 0; c < 16; ++c) {
+                p[c] = __builtin_amdgcn_exp2f(p[c] - ms);
+                ps += p[c];
+            }
+            lp = lp * corr + ps;
+            asm volatile("" ::: "memory");
+            if (g == 0) P[p_at(0, r)] = corr;
+            asm volatile("" ::: "memory");
+            float cr[16];
+            gather_rows(cr);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                o0[e] *= cr[e];
+                o1[e] *= cr[e];
+            }
+            // O += P V over the block's two 16-key halves
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc) {
+                const u32x4 a = pack16<DT>(p + 8 * kc);
+                const S* vb = Vs + (j0 + 16 * kc) * VST;
+                const u32x2 b0l = lds_read_tr16(vb + tr_row * VST + tr_col);
+                const u32x2 b0h = lds_read_tr16(vb + (tr_row + 4) * VST + tr_col);
+                const u32x2 b1l = lds_read_tr16(vb + tr_row * VST + 32 + tr_col);
+                const u32x2 b1h = lds_read_tr16(vb + (tr_row + 4) * VST + 32 + tr_col);
+                o0 = mfma32_16bit<DT>(a, u32x4{b0l[0], b0l[1], b0h[0], b0h[1]}, o0);
+                o1 = mfma32_16bit<DT>(a, u32x4{b1l[0], b1l[1], b1h[0], b1h[1]}, o1);
+            }
+        }
+        const float l = lp + __shfl_xor(lp, 32, 64);
+        if (g == 0 && lse && myrow < T)
+            lse[((int64_t)b * NH + h) * T + myrow] = (m + __builtin_amdgcn_logf(l)) * 0.6931471805599453f;
+        asm volatile("" ::: "memory");
+        if (g == 0) P[p_at(0, r)] = 1.0f / l;
+        asm volatile("" ::: "memory");
+        float inv[16];
+        gather_rows(inv);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int row = row0 + 8 * (e >> 2) + 4 * g + (e & 3);
+            if (row < T) {
+                const int64_t orow = ((int64_t)b * T + row) * C + (int64_t)h * HS;
+                const float y0 = o0[e] * inv[e], y1 = o1[e] * inv[e];
+                store_vec<DT, 1>(out, orow + r, &y0);
+                store_vec<DT, 1>(out, orow + 32 + r, &y1);
+            }
+        }
+    }
+}
+
 bool aligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
@@ -334,8 +483,15 @@ int layernorm_dt(const void* X, const void* g, const void* b, void* Y, float* me
 template <int DT, bool CAUSAL>
 int attention_dt(const void* qkv, void* out, float* lse, int64_t B, int T, int NH, hipStream_t s) {
     const dim3 grid((unsigned)(B * NH));
-    if (T <= 128) hipLaunchKernelGGL((attention_kernel<DT, CAUSAL, 128>), grid, dim3(256), 0, s, qkv, out, lse, T, NH);
-    else hipLaunchKernelGGL((attention_kernel<DT, CAUSAL, 256>), grid, dim3(256), 0, s, qkv, out, lse, T, NH);
+    if constexpr (DT == TLG_F32) {
+        if (T <= 128) hipLaunchKernelGGL((attention_kernel<DT, CAUSAL, 128>), grid, dim3(256), 0, s, qkv, out, lse, T, NH);
+        else hipLaunchKernelGGL((attention_kernel<DT, CAUSAL, 256>), grid, dim3(256), 0, s, qkv, out, lse, T, NH);
+    } else {
+        if (T <= 128)
+            hipLaunchKernelGGL((attention16_kernel<DT, CAUSAL, 128>), grid, dim3(256), 0, s, qkv, out, lse, T, NH);
+        else
+            hipLaunchKernelGGL((attention16_kernel<DT, CAUSAL, 256>), grid, dim3(256), 0, s, qkv, out, lse, T, NH);
+    }
     return check_launch("attention_kernel");
 }
 
