@@ -565,8 +565,18 @@ def bench_gpt2_forward(torch, dev, stream, dtype: str, no_parity: bool, layers: 
     for _ in range(2):
         one_pass()
     ms = median_span_ms(torch, one_pass, reps, stream)
+    # the same pass captured once in a HIP graph, starting from a device copy of the input
+    xin = dev_tensor(torch, x0, dtype, dev)
+
+    def graph_pass(s):  # called with the capturing stream current
+        x.copy_(xin)
+        for blk in blocks:
+            blk.forward(x, s)
+
+    ms_graph, same = graph_span_ms(torch, graph_pass, reps, [x])
     flops = layers * shape.flops()
     peak = PEAK_F32_TFLOPS if dtype == "f32" else PEAK_BF16_TFLOPS
+    res.update({"pass_ms_graph": round(ms_graph, 4), "graph_bitwise_equal": same})
     res.update({"workload": f"GPT-2-small forward through {layers} blocks, {B} x {T} tokens, {dtype}: per block "
                             "LayerNorm, qkv, fused causal attention, attn-out (+residual), LayerNorm, fc+GELU, "
                             "proj (+residual); no embeddings, final LayerNorm or logits",
@@ -574,7 +584,9 @@ def bench_gpt2_forward(torch, dev, stream, dtype: str, no_parity: bool, layers: 
                 "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2),
                 "frac_mfma_peak": round(flops / (ms * 1e-3) / 1e12 / peak, 4), "flops_per_pass": flops,
                 "launches_per_pass": 7 * layers,
-                "timing": f"median over {reps} passes of the HIP-event span of one pass on one stream"})
+                "timing": f"median over {reps} passes of the HIP-event span of one pass on one stream; pass_ms_graph: "
+                          "the pass (plus a copy of the input into place) captured once in a HIP graph, median "
+                          "replay span, its output bitwise equal to the eager pass"})
     return res
 
 

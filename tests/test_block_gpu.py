@@ -39,3 +39,35 @@ def test_block_forward_matches_the_oracle_composition(dtype, B, T):
     ref = _oracle_block(x, P, B, T, NH, dtype)
     err = oracle.normalized_error(to_f64(xd), ref)
     assert err <= TOL[dtype], err
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_block_forward_replays_bitwise_from_a_graph(dtype):
+    """Two blocks captured once (after a device copy of the input into place) replay bitwise equal to the
+    eager forward, with eager work on the same buffers between replays."""
+    B, T, C, NH = 2, 64, 768, 12
+    blocks = [block.GPT2Block(block.BlockShape(B, T, C, NH, dtype),
+                              {k: to_device(v, dtype) for k, v in inputs.gpt2_block_params(9, li, C, dtype).items()})
+              for li in range(2)]
+    x0 = to_device(inputs.normal(inputs.seed_for(9, 0, 1), (B * T, C), 1.0, dtype), dtype)
+    x = x0.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for blk in blocks:
+            blk.forward(x, s.cuda_stream)
+    s.synchronize()
+    want = x.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        x.copy_(x0)
+        for blk in blocks:
+            blk.forward(x, s.cuda_stream)
+    for rep in range(3):
+        x.fill_(float("nan"))
+        with torch.cuda.stream(s):  # eager work on the same buffers between replays
+            blocks[rep % 2].forward(x0.clone(), s.cuda_stream)
+        s.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(x, want), f"replay {rep}"
