@@ -16,6 +16,11 @@
 //    the current slice (scheduling group barriers), and exact-fit tiles load
 //    through buffer descriptors: one lane offset per operand instead of a
 //    64-bit address per load, which keeps the loop free of register spills.
+//  * Tiles that list a stage count (16-bit [M][K]·[N][K] operands, exact
+//    fit) skip the registers: global_load_lds_dwordx4 writes each slice
+//    straight into one of that many LDS buffers, unpadded and swizzled, with
+//    no LDS stores and no staging registers; waits on the vector-memory
+//    counter and one barrier per slice order the buffers.
 //  * LDS rows are k-contiguous with a 16-byte pad (stride 80 B), so the
 //    16-byte operand reads of 16 consecutive rows hit 64 distinct banks.
 //    A [K][N] weight or [K][M] first operand is stored to LDS as it lies in
@@ -50,18 +55,29 @@ constexpr int tiled_occupancy() {
 }
 
 // Static LDS of one workgroup: two buffers of each operand tile (the arrays
-// the kernel declares; the padded row lengths are the kernel's).
-template <int IN, int LAYOUT, int BM, int BN, int BK>
+// the kernel declares; the padded row lengths are the kernel's), or ST
+// unpadded, swizzled buffers when the operands are loaded straight into LDS.
+template <int IN, int LAYOUT, int BM, int BN, int BK, int ST = 0>
 constexpr int tiled_lds_bytes() {
     constexpr bool f32 = IN == TLG_F32;
     constexpr int es = f32 ? 4 : 2, epv = 16 / es;
+    if constexpr (ST > 0) return ST * (BM + BN) * BK * es;
     constexpr int a = layout_a_transposed(LAYOUT) ? BK * (BM + (f32 ? 8 : 32)) : BM * (BK + epv);
     constexpr int b = layout_b_kn(LAYOUT) ? BK * (BN + (f32 ? 8 : 32)) : BN * (BK + epv);
     return 2 * (a + b) * es;
 }
 
+// s_waitcnt that waits until at most n vector-memory operations of this wave
+// are outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt and
+// lgkmcnt left at their maxima, i.e. not waited for).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 template <int IN, int OUT, int LAYOUT, uint32_t EPI, int BM, int BN, int BK, int WM, int WN, bool EVEN,
-          bool SPLIT>
+          bool SPLIT, int ST>
 __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) void tiled_kernel(const void* __restrict__ Xv,
                                                             const void* __restrict__ Wv,
                                                             const void* __restrict__ bias,
@@ -89,19 +105,31 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) 
     static_assert(AV >= 1 && BV >= 1, "every thread loads");
     static_assert(AV * THREADS == (A_MMAJOR ? BK * MV : BM * VPR), "A loads divide evenly");
     static_assert(BV * THREADS == (KNB ? BK * NV : BN * VPR), "weight loads divide evenly");
-    constexpr int A_ELEMS = A_MMAJOR ? BK * LDAM : BM * LDA;
-    constexpr int B_ELEMS = B_NMAJOR ? BK * LDBN : BN * LDA;
-    static_assert(2 * (A_ELEMS + B_ELEMS) * (int)sizeof(S) == tiled_lds_bytes<IN, LAYOUT, BM, BN, BK>(),
+    // ST > 0: operands go from memory straight into LDS (global_load_lds,
+    // no staging registers, no LDS stores) through ST buffers.
+    constexpr bool DL = ST > 0;
+    static_assert(!DL || (!F32 && !AT && !KNB && EVEN && ST >= 2 && ST <= 4),
+                  "direct loads: 16-bit, exact fit, both operands k-contiguous");
+    constexpr int A_ELEMS = DL ? BM * BK : A_MMAJOR ? BK * LDAM : BM * LDA;
+    constexpr int B_ELEMS = DL ? BN * BK : B_NMAJOR ? BK * LDBN : BN * LDA;
+    static_assert((DL ? ST : 2) * (A_ELEMS + B_ELEMS) * (int)sizeof(S) ==
+                      tiled_lds_bytes<IN, LAYOUT, BM, BN, BK, ST>(),
                   "the launcher's LDS figure matches the arrays");
 
-    // Four LDS arrays (A and B operand, two buffers each): separate objects,
-    // so the compiler sees that stores into one buffer never alias operand
-    // reads from the other, and every access lies within 64 KiB of its
+    // One LDS array per operand and buffer: separate objects, so the compiler
+    // sees that stores (or direct loads) into one buffer never alias operand
+    // reads from another, and every access lies within 64 KiB of its
     // operand's base (the reach of the DS offset field).
     __shared__ __attribute__((aligned(16))) S lds_a0[A_ELEMS];
     __shared__ __attribute__((aligned(16))) S lds_a1[A_ELEMS];
     __shared__ __attribute__((aligned(16))) S lds_b0[B_ELEMS];
     __shared__ __attribute__((aligned(16))) S lds_b1[B_ELEMS];
+    __shared__ __attribute__((aligned(16))) S lds_a2[ST > 2 ? A_ELEMS : 8];
+    __shared__ __attribute__((aligned(16))) S lds_b2[ST > 2 ? B_ELEMS : 8];
+    __shared__ __attribute__((aligned(16))) S lds_a3[ST > 3 ? A_ELEMS : 8];
+    __shared__ __attribute__((aligned(16))) S lds_b3[ST > 3 ? B_ELEMS : 8];
+    auto abuf = [&](int b) -> S* { return b == 0 ? lds_a0 : b == 1 ? lds_a1 : b == 2 ? lds_a2 : lds_a3; };
+    auto bbuf = [&](int b) -> S* { return b == 0 ? lds_b0 : b == 1 ? lds_b1 : b == 2 ? lds_b2 : lds_b3; };
 
     const S* __restrict__ X = static_cast<const S*>(Xv);
     const S* __restrict__ W = static_cast<const S*>(Wv);
@@ -227,6 +255,51 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) 
         }
     };
 
+    // ---- direct loads into swizzled, unpadded LDS tiles ----
+    // One global_load_lds_dwordx4 of a wave fills 1 KiB of LDS: lane l lands
+    // at base + 16·l, the base being the same for all lanes, so the layout is
+    // set by which memory each lane fetches.  A k-contiguous tile (rows of
+    // VPR 16-byte chunks) keeps logical chunk c of row R at chunk position
+    // c ^ ((R / RPB) % VPR), RPB = 16 / VPR rows per 256 bytes: the operand
+    // reads of 16 consecutive rows at one chunk then hit 64 distinct banks, as
+    // the padded rows of the staged path do.  Instruction q of an operand
+    // fills its bytes [1 KiB·q, 1 KiB·(q+1)); wave w issues q = w, w + WAVES,
+    // ...  The swizzle repeats every 4·WAVES·RPB rows, so each lane's fetch
+    // offset is the same in all of its instructions up to a uniform row step
+    // and is computed once.  (The transposed fragment reads of a [K][N]
+    // weight are library intrinsics without alias information, before which
+    // the compiler waits for every outstanding direct load; such tiles keep
+    // the staged path.)
+    constexpr int WAVES = WM * WN;
+    constexpr int RPB = VPR <= 16 ? 16 / VPR : 1;
+    uint32_t dl_off = 0;  // element offset of this lane's first fetch within either operand tile
+    if constexpr (DL) {
+        static_assert(VPR <= 16 && (4 * WAVES) % VPR == 0 && 64 % VPR == 0, "k-contiguous swizzle repeats per wave");
+        static_assert((BM * VPR) % (64 * WAVES) == 0 && (BN * VPR) % (64 * WAVES) == 0, "whole instructions per wave");
+        const int R = (64 / VPR) * wave + lane / VPR;
+        dl_off = (uint32_t)(R * K + EPV * ((lane % VPR) ^ ((R / RPB) % VPR)));
+    }
+    constexpr int AQ = BM * VPR / (64 * WAVES);  // direct loads per wave per slice: first operand
+    constexpr int BQ = BN * VPR / (64 * WAVES);  // and the weight
+    auto dload = [&](int s, int buf) {
+        const int k0 = kbeg + s * BK;
+        const S* xa = X + (int64_t)m0 * K + k0 + dl_off;
+        const S* wb = W + (int64_t)n0 * K + k0 + dl_off;
+        S* As = abuf(buf);
+        S* Bs = bbuf(buf);
+        constexpr int64_t step = (int64_t)(64 / VPR) * WAVES;  // rows between a wave's instructions
+#pragma unroll
+        for (int i = 0; i < AQ; ++i)
+            __builtin_amdgcn_global_load_lds((const void*)(xa + i * step * K),
+                                             (__attribute__((address_space(3))) void*)(As + (wave + WAVES * i) * 512),
+                                             16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < BQ; ++i)
+            __builtin_amdgcn_global_load_lds((const void*)(wb + i * step * K),
+                                             (__attribute__((address_space(3))) void*)(Bs + (wave + WAVES * i) * 512),
+                                             16, 0, 0);
+    };
+
     using Acc = f32x16;
     Acc acc[TM][TN];
 #pragma unroll
@@ -237,8 +310,8 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) 
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
     auto compute = [&](int buf, auto mid) {
-        const S* As = buf ? lds_a1 : lds_a0;
-        const S* Bs = buf ? lds_b1 : lds_b0;
+        const S* As = abuf(buf);
+        const S* Bs = bbuf(buf);
         if constexpr (F32) {
 #pragma unroll
             for (int kq = 0; kq < BK / 8; ++kq) {
@@ -286,7 +359,19 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) 
                 const u32x2 hi = lds_read_tr16(p + (tr_row + 4) * ld + tr_col);
                 return u32x4{lo[0], lo[1], hi[0], hi[1]};
             };
+            // Swizzled tiles (direct loads): this lane's chunk permutation.  Its
+            // rows wm0 + 32i + r and wn0 + 32j + r all share r's swizzle.
+            const int sw = (r / RPB) % VPR;
             auto frag = [&](int kq, u32x4(&fa)[TM], u32x4(&fb)[TN]) {
+                if constexpr (DL) {
+#pragma unroll
+                    for (int i = 0; i < TM; ++i)
+                        fa[i] = *reinterpret_cast<const u32x4*>(As + (wm0 + i * 32 + r) * BK + EPV * ((2 * kq + g) ^ sw));
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        fb[j] = *reinterpret_cast<const u32x4*>(Bs + (wn0 + j * 32 + r) * BK + EPV * ((2 * kq + g) ^ sw));
+                    return;
+                }
 #pragma unroll
                 for (int i = 0; i < TM; ++i) {
                     if constexpr (A_MMAJOR)
@@ -357,6 +442,14 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) 
         for (int m = HALF; m < NMF; ++m) slot(m, false, true);
         __builtin_amdgcn_sched_barrier(0);
     };
+    // Direct-load phase: no LDS stores; the next slices' loads over the first
+    // half of the MFMAs.
+    auto dl_phase = [&]() {
+        __builtin_amdgcn_sched_group_barrier(0x100, FR, 0);
+#pragma unroll
+        for (int m = 0; m < NMF; ++m) slot(m, true, false);
+        __builtin_amdgcn_sched_barrier(0);
+    };
     auto nothing = [] {};
     // One steady-state phase: multiply buffer cb, store `st` into the other
     // buffer, load slice ls into `ld`.
@@ -385,7 +478,33 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) 
     // prefetches past the last slice re-read the last one (an L2 hit; the
     // copy lands in a buffer nothing reads), so no tail code with its own
     // register allocation follows the loop: an odd count leaves one multiply.
-    if (nslices > 0) {
+    if constexpr (DL) {
+        // ST-1 slices in flight ahead of the one being multiplied; buffer
+        // s % ST holds slice s.  Unrolled by ST so that every buffer is named
+        // statically (the host guarantees a slice count that is a positive
+        // multiple of ST).  Before slice s is read, this wave waits for its
+        // own loads of it, and the barrier that follows covers every wave's
+        // loads and frees the buffer read one step earlier, which the next
+        // load then refills.  Prefetches past the last slice re-read it into
+        // a buffer nothing reads again.
+        constexpr int LPW = AQ + BQ;
+        if (nslices > 0) {
+            const int last = nslices - 1;
+#pragma unroll
+            for (int q = 0; q < ST - 1; ++q) dload(min(q, last), q);
+            for (int s = 0; s < nslices; s += ST) {
+#pragma unroll
+                for (int u = 0; u < ST; ++u) {
+                    wait_vmcnt<(ST - 2) * LPW>();
+                    __syncthreads();
+                    dload(min(s + u + ST - 1, last), (u + ST - 1) % ST);
+                    compute(u, nothing);
+                    dl_phase();
+                }
+            }
+            wait_vmcnt<0>();  // the re-reads have landed before the LDS is reused below
+        }
+    } else if (nslices > 0) {
         u32x4 ra0[AV], rb0[BV], ra1[AV], rb1[BV];
         const int last = nslices - 1;
         gload(0, ra0, rb0);
@@ -546,14 +665,25 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     }
 }
 
-template <int I, int O, int L, uint32_t E, int BM, int BN, int BK, int WM, int WN, int CAP>
-static int launch_tiled_cfg(const tlg_plan& p, const void* X, const void* W, const void* bias, void* Y,
-                            float* ws, hipStream_t stream) {
-    // A workgroups-per-CU cap is enforced by asking for unused dynamic LDS:
-    // just past 1/(CAP+1) of the CU's 160 KiB per workgroup.
-    constexpr int kLdsPerCu = 160 * 1024, st = tiled_lds_bytes<I, L, BM, BN, BK>();
+// A workgroups-per-CU cap is enforced by asking for unused dynamic LDS:
+// just past 1/(CAP+1) of the CU's 160 KiB per workgroup.
+template <int CAP, int STATIC_LDS>
+constexpr int tiled_dyn_lds() {
+    constexpr int kLdsPerCu = 160 * 1024, st = STATIC_LDS;
     constexpr int dyn = CAP > 0 && st < kLdsPerCu / (CAP + 1) + 1024 ? kLdsPerCu / (CAP + 1) + 1024 - st : 0;
     static_assert(CAP == 0 || (st + dyn) * CAP <= kLdsPerCu, "the cap still fits CAP workgroups");
+    return dyn;
+}
+
+template <int I, int O, int L, uint32_t E, int BM, int BN, int BK, int WM, int WN, int CAP, int DLS>
+static int launch_tiled_cfg(const tlg_plan& p, const void* X, const void* W, const void* bias, void* Y,
+                            float* ws, hipStream_t stream) {
+    constexpr int dyn = tiled_dyn_lds<CAP, tiled_lds_bytes<I, L, BM, BN, BK>()>();
+    // Direct loads into LDS where the tile takes them: 16-bit operands, both
+    // k-contiguous, exact-fit tiles and a slice count per split that is a
+    // multiple of the stage count.
+    constexpr int ST = DLS > 0 && I != TLG_F32 && !layout_a_transposed(L) && !layout_b_kn(L) ? DLS : 0;
+    constexpr int dyn_dl = ST > 0 ? tiled_dyn_lds<CAP, tiled_lds_bytes<I, L, BM, BN, BK, ST>()>() : 0;
     const int S = p.split;
     const int kper = (int)(ceil_div(ceil_div(p.K, S), BK) * BK);
     const int64_t es = I == TLG_F32 ? 4 : 2;
@@ -562,22 +692,39 @@ static int launch_tiled_cfg(const tlg_plan& p, const void* X, const void* W, con
                         (layout_b_kn(L) ? p.K * p.N * es : (int64_t)BN * p.K * es) < INT32_MAX;
     const int resid = (p.epi & TLG_EPI_RESIDUAL) != 0;
     const bool even = p.M % BM == 0 && p.N % BN == 0 && (int64_t)kper * S == p.K && fits32;
+    // The plan decides (its stage count); the conditions are checked again here.
+    const bool direct = p.stages > 0;
+    if (direct && (p.stages != ST || !even || (kper / BK) % (ST > 0 ? ST : 1) != 0)) {
+        set_error("tiled kernel: plan asks for direct loads the tile cannot take");
+        return (int)TLG_ERR_INVALID_ARG;
+    }
     const dim3 grid((unsigned)(p.grid_x * p.grid_y), (unsigned)S), block(64 * WM * WN);
-    auto go = [&](auto ev, auto sp) {
-        hipLaunchKernelGGL((tiled_kernel<I, O, L, E, BM, BN, BK, WM, WN, decltype(ev)::value, decltype(sp)::value>),
-                           grid, block, dyn, stream, X, W, bias, Y, ws, (int)p.M, (int)p.N, (int)p.K, kper, resid);
+    // stc: the direct-load stage count (0: staged loads)
+    auto go = [&](auto ev, auto sp, auto stc) {
+        constexpr int st = decltype(stc)::value;
+        hipLaunchKernelGGL((tiled_kernel<I, O, L, E, BM, BN, BK, WM, WN, decltype(ev)::value, decltype(sp)::value, st>),
+                           grid, block, st > 0 ? dyn_dl : dyn, stream, X, W, bias, Y, ws, (int)p.M, (int)p.N, (int)p.K,
+                           kper, resid);
         return check_launch("tiled_kernel");
     };
-    auto go_split = [&](auto ev) {
-        hipLaunchKernelGGL((tiled_kernel<I, TLG_F32, L, 0u, BM, BN, BK, WM, WN, decltype(ev)::value, true>), grid,
-                           block, dyn, stream, X, W, nullptr, nullptr, ws, (int)p.M, (int)p.N, (int)p.K, kper, 0);
+    auto go_split = [&](auto ev, auto stc) {
+        constexpr int st = decltype(stc)::value;
+        hipLaunchKernelGGL((tiled_kernel<I, TLG_F32, L, 0u, BM, BN, BK, WM, WN, decltype(ev)::value, true, st>), grid,
+                           block, st > 0 ? dyn_dl : dyn, stream, X, W, nullptr, nullptr, ws, (int)p.M, (int)p.N,
+                           (int)p.K, kper, 0);
         return check_launch("tiled_kernel");
     };
     int rc;
-    if (S > 1)  // partials carry no epilogue: the reducer applies it
-        rc = even ? go_split(std::true_type{}) : go_split(std::false_type{});
-    else
-        rc = even ? go(std::true_type{}, std::false_type{}) : go(std::false_type{}, std::false_type{});
+    if (direct) {
+        if constexpr (ST > 0)
+            rc = S > 1 ? go_split(std::true_type{}, ic<ST>{}) : go(std::true_type{}, std::false_type{}, ic<ST>{});
+        else
+            rc = (int)TLG_ERR_UNSUPPORTED;  // not reached: direct implies ST > 0
+    } else if (S > 1) {  // partials carry no epilogue: the reducer applies it
+        rc = even ? go_split(std::true_type{}, ic<0>{}) : go_split(std::false_type{}, ic<0>{});
+    } else {
+        rc = even ? go(std::true_type{}, std::false_type{}, ic<0>{}) : go(std::false_type{}, std::false_type{}, ic<0>{});
+    }
     if (rc != TLG_OK || S == 1) return rc;
     const int64_t MN = p.M * p.N;
     hipLaunchKernelGGL((splitk_reduce_kernel<I, O, E>), dim3((unsigned)ceil_div(MN, 1024)), dim3(256), 0, stream,
@@ -603,12 +750,16 @@ int launch_tiled_in(const tlg_plan& p, const void* X, const void* W, const void*
                 constexpr int O = decltype(out)::value, L = decltype(lay)::value;
                 constexpr uint32_t E = (uint32_t)decltype(epi)::value;
                 constexpr const TileCfg* T = I == TLG_F32 ? kTiledF32 : kTiled16;
-                static_assert(kNumTiledF32 == 6 && kNumTiled16 == 6, "tile lists changed");
-#define TLG_TILED_CASE(i)                                                                                 \
-    case i: {                                                                                             \
-        constexpr TileCfg c = T[i];                                                                       \
-        return launch_tiled_cfg<I, O, L, E, c.bm, c.bn, c.bk, c.wm, c.wn, c.cap>(p, X, W, bias, Y, wsf, stream); \
-    }
+                constexpr int count = I == TLG_F32 ? kNumTiledF32 : kNumTiled16;
+                static_assert(kNumTiledF32 == 6 && kNumTiled16 == 9, "tile lists changed");
+#define TLG_TILED_CASE(i)                                                                                     \
+    case i:                                                                                                   \
+        if constexpr (i < count) {                                                                            \
+            constexpr TileCfg c = T[i];                                                                       \
+            return launch_tiled_cfg<I, O, L, E, c.bm, c.bn, c.bk, c.wm, c.wn, c.cap, c.dl>(p, X, W, bias, Y, wsf, \
+                                                                                           stream);           \
+        }                                                                                                     \
+        break;
                 switch (p.tile) {
                     TLG_TILED_CASE(0)
                     TLG_TILED_CASE(1)
@@ -616,8 +767,13 @@ int launch_tiled_in(const tlg_plan& p, const void* X, const void* W, const void*
                     TLG_TILED_CASE(3)
                     TLG_TILED_CASE(4)
                     TLG_TILED_CASE(5)
-                default: set_error("bad tiled tile"); return (int)TLG_ERR_INVALID_ARG;
+                    TLG_TILED_CASE(6)
+                    TLG_TILED_CASE(7)
+                    TLG_TILED_CASE(8)
+                default: break;
                 }
+                set_error("bad tiled tile");
+                return (int)TLG_ERR_INVALID_ARG;
 #undef TLG_TILED_CASE
             };
             // the planner admits no bias or GELU with a transposed first operand

@@ -31,6 +31,7 @@ struct TileCfg {
     int bm, bn, bk;  // workgroup tile (rows of Y, columns of Y, K per pipeline stage)
     int wm, wn;      // waves along M and N
     int cap = 0;     // workgroups per CU at most (enforced with unused LDS); 0: as registers and LDS allow
+    int dl = 0;      // 16-bit [M][K]·[N][K] exact fit: LDS stages filled by direct loads (0: staged in registers)
 };
 
 // Tiles of the LDS-tiled MFMA kernel, per input class.  The index is what
@@ -46,14 +47,22 @@ constexpr TileCfg kTiledF32[] = {
 };
 // 16-bit operands: v_mfma_f32_32x32x16_{f16,bf16}.  A slice of 32 elements
 // is only 256 MFMA cycles per wave, too short to hide one slice of load
-// latency, so the default slice is 64 or 128 elements deep.
+// latency, so the default slice is 64 or 128 elements deep.  Entries 6-8
+// fill their LDS stages with direct loads (dl stages) where the operands
+// allow it ([M][K]·[N][K], exact fit) and otherwise run as the staged tile of
+// the same shape.  Measured against staging on the GPT-2 linears at 8192
+// rows: faster for some shapes (attention output, proj), slower for others
+// (qkv), so they are separate entries for the table search to choose from.
 constexpr TileCfg kTiled16[] = {
-    {128, 128, 64, 2, 2},   // 0
-    {64, 64, 64, 2, 2},     // 1: narrow grids, pairs with split-K
-    {256, 128, 64, 2, 2},   // 2
-    {256, 128, 32, 2, 2},   // 3: short slices; two workgroups per CU fit in LDS (the 64-deep 256x128 tile fits one)
-    {256, 256, 64, 2, 2},   // 4
-    {256, 256, 64, 2, 4},   // 5: eight waves, two per SIMD: one's stalls are the other's MFMA time
+    {128, 128, 64, 2, 2},         // 0
+    {64, 64, 64, 2, 2},           // 1: narrow grids, pairs with split-K
+    {256, 128, 64, 2, 2},         // 2
+    {256, 128, 32, 2, 2},         // 3: short slices; two workgroups per CU fit in LDS (the 64-deep 256x128 tile fits one)
+    {256, 256, 64, 2, 2},         // 4
+    {256, 256, 64, 2, 4},         // 5: eight waves, two per SIMD: one's stalls are the other's MFMA time
+    {128, 128, 64, 2, 2, 0, 2},   // 6: direct loads, two stages
+    {256, 128, 64, 2, 2, 0, 2},   // 7: direct loads, two stages
+    {128, 128, 32, 2, 2, 0, 4},   // 8: direct loads, four 32-deep stages (three slices in flight)
 };
 constexpr int kNumTiledF32 = sizeof(kTiledF32) / sizeof(kTiledF32[0]);
 constexpr int kNumTiled16 = sizeof(kTiled16) / sizeof(kTiled16[0]);
@@ -109,6 +118,7 @@ struct tlg_plan {
     int launches;
     size_t ws_bytes;
     int bm, bn, bk;
+    int stages;  // TILED: LDS stages filled by direct loads (0: loads staged through registers)
 };
 
 namespace tlg {

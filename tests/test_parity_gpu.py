@@ -89,12 +89,47 @@ def test_stream_forced_split(pair, split):
 @pytest.mark.parametrize("layout", ["NK", "KN"])
 @pytest.mark.parametrize("epi", EPIS, ids=["none", "bias", "gelu", "bias+gelu"])
 def test_tiled(pair, layout, epi):
-    for tile in (1, 2, 3, 4, 5, 6):
+    for tile in range(1, 7 if pair[0] == "f32" else 10):
         for (M, N, K), split in [((130, 136, 72), 1), ((256, 256, 256), 1), ((64, 64, 32), 1),
                                  ((200, 264, 400), 3), ((33, 520, 1024), 4)]:
             c = _case(3, M, N, K, pair, layout, epi)
             _, desc = _check(c, variant=tlgemm.VARIANT_TILED, tile=tile, split_k=split)
             assert "variant=tiled" in desc
+
+
+@pytest.mark.parametrize("tile", [7, 8, 9])
+def test_tiled_direct_loads(tile):
+    """Exact-fit 16-bit [M][K]·[N][K] tiles whose operands go straight into swizzled LDS stages.
+
+    Long K (many stage rounds), split-K partials, every epilogue and both
+    output widths; the plan must report the direct-load path.  K per split is
+    a multiple of 768, a whole number of stage rounds.
+    """
+    for (M, N, K), split, epi, pair in [((512, 512, 1536), 1, (True, True), ("bf16", "bf16")),
+                                        ((256, 512, 1536), 2, (True, False), ("f16", "f32")),
+                                        ((512, 256, 768), 1, (False, False), ("f16", "f16")),
+                                        ((256, 256, 3072), 4, (False, True), ("bf16", "f32"))]:
+        c = _case(13, M, N, K, pair, "NK", epi)
+        _, desc = _check(c, variant=tlgemm.VARIANT_TILED, tile=tile, split_k=split)
+        assert "load=direct" in desc, desc
+
+
+def test_tiled_direct_loads_residual():
+    for tile in (7, 9):
+        c = inputs.random_case(14, 512, 512, 1536, "bf16", "bf16", "NK", bias=True, residual=True)
+        _, desc = _check(c, variant=tlgemm.VARIANT_TILED, tile=tile)
+        assert "load=direct" in desc and "+res" in desc, desc
+
+
+def test_tiled_staged_when_direct_loads_do_not_fit():
+    """Ragged tiles, an odd slice count per split, [K][N] weights and tiles without direct loads
+    keep the register-staged path."""
+    for (M, N, K), split, layout, tile in [((500, 512, 1024), 1, "NK", 7), ((512, 512, 192), 1, "NK", 7),
+                                           ((512, 512, 1024), 1, "KN", 7), ((512, 512, 1056), 1, "NK", 9),
+                                           ((512, 512, 1024), 1, "NK", 1)]:
+        c = _case(16, M, N, K, ("bf16", "bf16"), layout, (True, False))
+        _, desc = _check(c, variant=tlgemm.VARIANT_TILED, tile=tile, split_k=split)
+        assert "load=direct" not in desc, desc
 
 
 # --- the workloads at their full sizes ---------------------------------------------------
