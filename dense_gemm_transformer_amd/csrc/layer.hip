@@ -147,6 +147,9 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const void* __restrict__
 // with bit 4 of j set; tile (m, n) at column n ^ 4 (m % 8).
 constexpr int kHeadSize = 64, kKeyBlock = 32;
 
+// 16-byte loads each thread keeps in flight while filling the key and value tiles.
+constexpr int kLoadGroup = 8;
+
 __device__ inline int k_at(int j, int chunk) { return j * kHeadSize + ((chunk ^ (j & 15)) << 2); }
 __device__ inline int v_at(int j, int d) { return j * kHeadSize + (d ^ (((j >> 4) & 1) << 5)); }
 __device__ inline int p_at(int m, int n) { return m * 32 + (n ^ ((m & 7) << 2)); }
@@ -163,16 +166,33 @@ __global__ __launch_bounds__(256) void attention_kernel(const void* __restrict__
     const int64_t C = (int64_t)NH * HS, C3 = 3 * C;
     const int64_t head = (int64_t)b * T * C3 + (int64_t)h * HS;  // q of row 0 of this head
 
+    // Keys and values, 16-byte vectors: each thread has kLoadGroup loads in
+    // flight before it stores any of them (one load, wait, store per vector
+    // would chain the memory latency kLoadGroup times).
     constexpr int VPR = HS / EPV;  // 16-byte vectors per row
-    for (int idx = threadIdx.x; idx < 2 * T * VPR; idx += 256) {
-        const int which = idx / (T * VPR), rem = idx % (T * VPR), j = rem / VPR, c0 = (rem % VPR) * EPV;
-        float f[EPV];
-        load_vec<DT, EPV>(qkv, head + (int64_t)j * C3 + (which + 1) * C + c0, f);
+    const int nvec = 2 * T * VPR;
+    for (int base = threadIdx.x; base < nvec; base += 256 * kLoadGroup) {
+        float f[kLoadGroup][EPV];
 #pragma unroll
-        for (int u = 0; u < EPV; u += 4) {
-            const f32x4 x = {f[u], f[u + 1], f[u + 2], f[u + 3]};
-            float* dst = which ? Vs + v_at(j, c0 + u) : Ks + k_at(j, (c0 + u) >> 2);
-            *reinterpret_cast<f32x4*>(dst) = x;
+        for (int i = 0; i < kLoadGroup; ++i) {
+            const int idx = base + 256 * i;
+            if (idx < nvec) {
+                const int which = idx / (T * VPR), rem = idx % (T * VPR), j = rem / VPR, c0 = (rem % VPR) * EPV;
+                load_vec<DT, EPV>(qkv, head + (int64_t)j * C3 + (which + 1) * C + c0, f[i]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kLoadGroup; ++i) {
+            const int idx = base + 256 * i;
+            if (idx < nvec) {
+                const int which = idx / (T * VPR), rem = idx % (T * VPR), j = rem / VPR, c0 = (rem % VPR) * EPV;
+#pragma unroll
+                for (int u = 0; u < EPV; u += 4) {
+                    const f32x4 x = {f[i][u], f[i][u + 1], f[i][u + 2], f[i][u + 3]};
+                    float* dst = which ? Vs + v_at(j, c0 + u) : Ks + k_at(j, (c0 + u) >> 2);
+                    *reinterpret_cast<f32x4*>(dst) = x;
+                }
+            }
         }
     }
     __syncthreads();
@@ -315,18 +335,27 @@ __global__ __launch_bounds__(256) void attention16_kernel(const void* __restrict
     const int64_t head = (int64_t)b * T * C3 + (int64_t)h * HS;  // q of row 0 of this head
     const S* X = static_cast<const S*>(qkv);
 
-    // keys and values: 16-byte vectors of 8 elements, copied as they are
+    // keys and values: 16-byte vectors of 8 elements, copied as they are, with
+    // kLoadGroup loads of each thread in flight before it stores any of them
     const int tz = (T + 31) / 32 * 32;  // value rows up to the last key block, zero past T
-    for (int idx = threadIdx.x; idx < (T + tz) * 8; idx += 256) {
-        const bool isv = idx >= T * 8;
-        const int i2 = isv ? idx - T * 8 : idx, j = i2 >> 3, ch = i2 & 7;
-        if (!isv) {
-            *reinterpret_cast<u32x4*>(Ks + k16_at(j, ch)) =
-                *reinterpret_cast<const u32x4*>(X + head + (int64_t)j * C3 + C + ch * 8);
-        } else {
-            const u32x4 v = j < T ? *reinterpret_cast<const u32x4*>(X + head + (int64_t)j * C3 + 2 * C + ch * 8)
-                                  : u32x4{0u, 0u, 0u, 0u};
-            *reinterpret_cast<u32x4*>(Vs + j * VST + ch * 8) = v;
+    const int nvec = (T + tz) * 8;
+    for (int base = threadIdx.x; base < nvec; base += 256 * kLoadGroup) {
+        u32x4 v[kLoadGroup];
+#pragma unroll
+        for (int i = 0; i < kLoadGroup; ++i) {
+            const int idx = base + 256 * i;
+            const bool isv = idx >= T * 8;
+            const int i2 = isv ? idx - T * 8 : idx, j = i2 >> 3, ch = i2 & 7;
+            v[i] = u32x4{0u, 0u, 0u, 0u};
+            if (idx < nvec && (!isv || j < T))
+                v[i] = *reinterpret_cast<const u32x4*>(X + head + (int64_t)j * C3 + (isv ? 2 * C : C) + ch * 8);
+        }
+#pragma unroll
+        for (int i = 0; i < kLoadGroup; ++i) {
+            const int idx = base + 256 * i;
+            const bool isv = idx >= T * 8;
+            const int i2 = isv ? idx - T * 8 : idx, j = i2 >> 3, ch = i2 & 7;
+            if (idx < nvec) *reinterpret_cast<u32x4*>(isv ? Vs + j * VST + ch * 8 : Ks + k16_at(j, ch)) = v[i];
         }
     }
     __syncthreads();
