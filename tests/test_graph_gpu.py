@@ -47,7 +47,12 @@ def test_captured_sequence_replays_bitwise():
                variant=tlgemm.VARIANT_TILED, tile=2, split_k=4),                      # tiled split + reducer
         _setup(inputs.random_case(43, 256, 384, 512, "bf16", bias=True, gelu=True)),  # planner's choice
         _setup(inputs.workload_fp16_narrow()),                                         # the narrow layer
+        _setup(inputs.random_case(44, 512, 512, 1536, "bf16", bias=True),
+               variant=tlgemm.VARIANT_TILED, tile=7, split_k=2),                      # direct LDS loads, split
+        _setup(inputs.random_case(45, 512, 256, 768, "f16", gelu=True),
+               variant=tlgemm.VARIANT_TILED, tile=9),                                 # four direct-load stages
     ]
+    assert all("load=direct" in g["plan"].describe() for g in gemms[-2:])
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())  # inputs, outputs and zeroed workspaces come from the default stream
     with torch.cuda.stream(s):
