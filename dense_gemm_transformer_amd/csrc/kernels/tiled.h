@@ -77,7 +77,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 template <int IN, int OUT, int LAYOUT, uint32_t EPI, int BM, int BN, int BK, int WM, int WN, bool EVEN,
-          bool SPLIT, int ST>
+          bool SPLIT, int ST, bool PERS>
 __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) void tiled_kernel(const void* __restrict__ Xv,
                                                             const void* __restrict__ Wv,
                                                             const void* __restrict__ bias,
@@ -140,15 +140,19 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) 
     // ---- tile coordinates: XCD-aware remap, then groups of 8 tile-rows ----
     const int gx = (N + BN - 1) / BN, gy = (M + BM - 1) / BM;
     const int total = gx * gy;
-    int lin = blockIdx.x;
-    if ((total & 7) == 0) lin = (lin & 7) * (total >> 3) + (lin >> 3);
     constexpr int GROUP = 8;
-    const int group_tiles = GROUP * gx;
-    const int first = (lin / group_tiles) * GROUP;
-    const int rows_in_group = min(gy - first, GROUP);
-    const int within = lin % group_tiles;
-    const int m0 = (first + within % rows_in_group) * BM;
-    const int n0 = (within / rows_in_group) * BN;
+    auto tile_origin = [&](int id, int& tm0, int& tn0) {
+        int lin = id;
+        if ((total & 7) == 0) lin = (lin & 7) * (total >> 3) + (lin >> 3);
+        const int group_tiles = GROUP * gx;
+        const int first = (lin / group_tiles) * GROUP;
+        const int rows_in_group = min(gy - first, GROUP);
+        const int within = lin % group_tiles;
+        tm0 = (first + within % rows_in_group) * BM;
+        tn0 = (within / rows_in_group) * BN;
+    };
+    int m0, n0;  // this tile's origin (a persistent workgroup moves on to further tiles)
+    tile_origin(blockIdx.x, m0, n0);
 
     const int z = blockIdx.y;
     const int kbeg = z * kper;
@@ -166,29 +170,42 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) 
     const uint32_t b_lane = !KNB ? (uint32_t)(((t / VPR) * K + (t % VPR) * EPV) * ES)
                                  : (uint32_t)(((t / NV) * N + (t % NV) * EPV) * ES);
     i32x4 rsrc_a = {0, 0, 0, 0}, rsrc_b = {0, 0, 0, 0};
-    if constexpr (EVEN) {
-        rsrc_a = AT ? buffer_rsrc(X + m0, ((int64_t)K * M - m0) * ES) : buffer_rsrc(X + (int64_t)m0 * K, (int64_t)BM * K * ES);
-        rsrc_b = KNB ? buffer_rsrc(W + n0, ((int64_t)K * N - n0) * ES) : buffer_rsrc(W + (int64_t)n0 * K, (int64_t)BN * K * ES);
-    }
+    auto make_rsrc = [&](int tm0, int tn0, i32x4& qa, i32x4& qb) {
+        qa = AT ? buffer_rsrc(X + tm0, ((int64_t)K * M - tm0) * ES) : buffer_rsrc(X + (int64_t)tm0 * K, (int64_t)BM * K * ES);
+        qb = KNB ? buffer_rsrc(W + tn0, ((int64_t)K * N - tn0) * ES) : buffer_rsrc(W + (int64_t)tn0 * K, (int64_t)BN * K * ES);
+    };
+    if constexpr (EVEN) make_rsrc(m0, n0, rsrc_a, rsrc_b);
+    // The next tile's descriptors (persistent loop): slice index s >= nslices
+    // loads slice s - nslices of that tile.
+    i32x4 nrsrc_a = rsrc_a, nrsrc_b = rsrc_b;
     auto gload = [&](int s, u32x4 (&ra)[AV], u32x4 (&rbv)[BV]) {
-        const int k0 = kbeg + s * BK;
         if constexpr (EVEN) {
+            i32x4 qa = rsrc_a, qb = rsrc_b;
+            if constexpr (PERS) {
+                if (s >= nslices) {
+                    s -= nslices;
+                    qa = nrsrc_a;
+                    qb = nrsrc_b;
+                }
+            }
+            const int k0 = kbeg + s * BK;
 #pragma unroll
             for (int i = 0; i < AV; ++i) {
                 if constexpr (A_MMAJOR)
-                    ra[i] = buffer_load16(rsrc_a, a_lane, (k0 + i * (THREADS / MV)) * M * ES, 0);
+                    ra[i] = buffer_load16(qa, a_lane, (k0 + i * (THREADS / MV)) * M * ES, 0);
                 else
-                    ra[i] = buffer_load16(rsrc_a, a_lane, (k0 + i * (THREADS / VPR) * K) * ES, 0);
+                    ra[i] = buffer_load16(qa, a_lane, (k0 + i * (THREADS / VPR) * K) * ES, 0);
             }
 #pragma unroll
             for (int i = 0; i < BV; ++i) {
                 if constexpr (!KNB)
-                    rbv[i] = buffer_load16(rsrc_b, b_lane, (k0 + i * (THREADS / VPR) * K) * ES, 0);
+                    rbv[i] = buffer_load16(qb, b_lane, (k0 + i * (THREADS / VPR) * K) * ES, 0);
                 else
-                    rbv[i] = buffer_load16(rsrc_b, b_lane, (k0 + i * (THREADS / NV)) * N * ES, 0);
+                    rbv[i] = buffer_load16(qb, b_lane, (k0 + i * (THREADS / NV)) * N * ES, 0);
             }
             return;
         }
+        const int k0 = kbeg + s * BK;
         // Ragged tiles: out-of-range rows and columns are clamped to valid
         // ones (their outputs are never stored), K past the range loads zeros.
 #pragma unroll
@@ -467,61 +484,6 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) 
         }
     };
 
-    // Two slices of loads in flight: while slice s is multiplied from one LDS
-    // buffer, slice s+1 waits in registers for the other buffer and slice s+2
-    // is being fetched.  The loop is unrolled by two so each register set is
-    // named statically.  Buffer b is rewritten only after the barrier that
-    // follows its last read.
-    // Every compute and load in the loop is unconditional, which keeps the
-    // accumulators in place across iterations and lets each wait cover only
-    // the slice about to be stored.  The loop runs over every pair of slices;
-    // prefetches past the last slice re-read the last one (an L2 hit; the
-    // copy lands in a buffer nothing reads), so no tail code with its own
-    // register allocation follows the loop: an odd count leaves one multiply.
-    if constexpr (DL) {
-        // ST-1 slices in flight ahead of the one being multiplied; buffer
-        // s % ST holds slice s.  Unrolled by ST so that every buffer is named
-        // statically (the host guarantees a slice count that is a positive
-        // multiple of ST).  Before slice s is read, this wave waits for its
-        // own loads of it, and the barrier that follows covers every wave's
-        // loads and frees the buffer read one step earlier, which the next
-        // load then refills.  Prefetches past the last slice re-read it into
-        // a buffer nothing reads again.
-        constexpr int LPW = AQ + BQ;
-        if (nslices > 0) {
-            const int last = nslices - 1;
-#pragma unroll
-            for (int q = 0; q < ST - 1; ++q) dload(min(q, last), q);
-            for (int s = 0; s < nslices; s += ST) {
-#pragma unroll
-                for (int u = 0; u < ST; ++u) {
-                    wait_vmcnt<(ST - 2) * LPW>();
-                    __syncthreads();
-                    dload(min(s + u + ST - 1, last), (u + ST - 1) % ST);
-                    compute(u, nothing);
-                    dl_phase();
-                }
-            }
-            wait_vmcnt<0>();  // the re-reads have landed before the LDS is reused below
-        }
-    } else if (nslices > 0) {
-        u32x4 ra0[AV], rb0[BV], ra1[AV], rb1[BV];
-        const int last = nslices - 1;
-        gload(0, ra0, rb0);
-        gload(min(1, last), ra1, rb1);
-        lstore(0, ra0, rb0);
-        __syncthreads();
-        // At the top of each pair: buffer 0 holds slice s, ra1 slice s+1.
-        int s = 0;
-        for (; s + 1 < nslices; s += 2) {
-            phase(0, min(s + 2, last), ra0, rb0, ra1, rb1);  // multiply s, store s+1, load s+2
-            __syncthreads();
-            phase(1, min(s + 3, last), ra1, rb1, ra0, rb0);  // multiply s+1, store s+2, load s+3
-            __syncthreads();
-        }
-        if (s < nslices) compute(0, nothing);  // odd count: the last slice is in buffer 0
-    }
-
     // ---- epilogue: a 32×32 accumulator holds column (lane % 32) and rows
     // 8*(e/4) + 4*(lane/32) + e%4 for register e.
     // Exact-fit tiles leave through LDS: each wave stages 16 rows × WTN of its
@@ -538,16 +500,14 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) 
     // w of a0, a1, b0, b1 in turn.
     constexpr int SA = A_ELEMS * (int)sizeof(S) / (STG * 4), SB = B_ELEMS * (int)sizeof(S) / (STG * 4);
     constexpr bool STAGED = 2 * SA + 2 * SB >= WM * WN;
-    if constexpr (EVEN && STAGED) {
-        constexpr int OB = SPLIT ? 4 : (OUT == TLG_F32 ? 4 : 2);  // bytes per written element
-        constexpr int EPC = 16 / OB;                               // elements per 16-byte store
-        constexpr int CPR = WTN / EPC;                             // 16-byte runs per staged row
+    constexpr int OB = SPLIT ? 4 : (OUT == TLG_F32 ? 4 : 2);  // bytes per written element
+    constexpr int EPC = 16 / OB;                               // elements per 16-byte store
+    constexpr int CPR = WTN / EPC;                             // 16-byte runs per staged row
+    // Stage the accumulators through this wave's strip stg, then apply bias,
+    // GELU and the residual and store (generic, so that it is instantiated
+    // only where it is used).
+    auto store_staged = [&](auto* stg) {
         static_assert(64 % CPR == 0 && (16 * CPR) % 64 == 0, "runs divide evenly over the lanes");
-        __syncthreads();
-        float* stg = wave < SA           ? reinterpret_cast<float*>(lds_a0) + wave * STG
-                     : wave < 2 * SA       ? reinterpret_cast<float*>(lds_a1) + (wave - SA) * STG
-                     : wave < 2 * SA + SB  ? reinterpret_cast<float*>(lds_b0) + (wave - 2 * SA) * STG
-                                           : reinterpret_cast<float*>(lds_b1) + (wave - 2 * SA - SB) * STG;
         // Opaque copy of the lane index: everything the epilogue derives from
         // it is computed here, after the loop, instead of being hoisted in
         // front of it and held in registers through it (which spilled the
@@ -605,8 +565,125 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) 
                 }
             }
         }
+    };
+
+    if constexpr (PERS) {
+        // Persistent workgroup: tiles blockIdx.x, blockIdx.x + gridDim.x, ...
+        // (the host sizes the grid to the workgroups resident at once).  The
+        // slice pipeline runs on across tiles: the last phases of a tile load
+        // the next tile's first two slices, and the finished tile leaves
+        // through the LDS buffer its last slice was read from while the next
+        // tile's first slice waits in the other.  The host guarantees an even
+        // slice count, so a tile always ends after the second phase of a pair.
+        static_assert(EVEN && !SPLIT && !DL && SA + SB >= WM * WN,
+                      "persistent tiles: exact fit, no split, one buffer holds every wave's staging strip");
+        const int last = nslices - 1;
+        u32x4 ra0[AV], rb0[BV], ra1[AV], rb1[BV];
+        gload(0, ra0, rb0);
+        gload(1, ra1, rb1);
+        lstore(0, ra0, rb0);
+        __syncthreads();
+        for (int tile = blockIdx.x;;) {
+            const int next = tile + (int)gridDim.x;
+            const bool more = next < total;
+            int nm0 = m0, nn0 = n0;
+            if (more) {
+                tile_origin(next, nm0, nn0);
+                make_rsrc(nm0, nn0, nrsrc_a, nrsrc_b);
+            }
+            // slice j <= last of this tile; past it slice j - nslices of the next
+            // tile, or this tile's last slice again when there is none
+            auto src = [&](int j) { return j <= last || more ? j : last; };
+            for (int s = 0; s < nslices; s += 2) {
+                phase(0, src(s + 2), ra0, rb0, ra1, rb1);
+                __syncthreads();
+                phase(1, src(s + 3), ra1, rb1, ra0, rb0);
+                __syncthreads();
+            }
+            store_staged(wave < SA ? reinterpret_cast<float*>(lds_a1) + wave * STG
+                                   : reinterpret_cast<float*>(lds_b1) + (wave - SA) * STG);
+            __syncthreads();  // staging read back before the next tile's slice 1 is stored to buffer 1
+            if (!more) break;
+            tile = next;
+            m0 = nm0;
+            n0 = nn0;
+            rsrc_a = nrsrc_a;
+            rsrc_b = nrsrc_b;
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+        }
         return;
     }
+
+    // Two slices of loads in flight: while slice s is multiplied from one LDS
+    // buffer, slice s+1 waits in registers for the other buffer and slice s+2
+    // is being fetched.  The loop is unrolled by two so each register set is
+    // named statically.  Buffer b is rewritten only after the barrier that
+    // follows its last read.
+    // Every compute and load in the loop is unconditional, which keeps the
+    // accumulators in place across iterations and lets each wait cover only
+    // the slice about to be stored.  The loop runs over every pair of slices;
+    // prefetches past the last slice re-read the last one (an L2 hit; the
+    // copy lands in a buffer nothing reads), so no tail code with its own
+    // register allocation follows the loop: an odd count leaves one multiply.
+    if constexpr (DL) {
+        // ST-1 slices in flight ahead of the one being multiplied; buffer
+        // s % ST holds slice s.  Unrolled by ST so that every buffer is named
+        // statically (the host guarantees a slice count that is a positive
+        // multiple of ST).  Before slice s is read, this wave waits for its
+        // own loads of it, and the barrier that follows covers every wave's
+        // loads and frees the buffer read one step earlier, which the next
+        // load then refills.  Prefetches past the last slice re-read it into
+        // a buffer nothing reads again.
+        constexpr int LPW = AQ + BQ;
+        if (nslices > 0) {
+            const int last = nslices - 1;
+#pragma unroll
+            for (int q = 0; q < ST - 1; ++q) dload(min(q, last), q);
+            for (int s = 0; s < nslices; s += ST) {
+#pragma unroll
+                for (int u = 0; u < ST; ++u) {
+                    wait_vmcnt<(ST - 2) * LPW>();
+                    __syncthreads();
+                    dload(min(s + u + ST - 1, last), (u + ST - 1) % ST);
+                    compute(u, nothing);
+                    dl_phase();
+                }
+            }
+            wait_vmcnt<0>();  // the re-reads have landed before the LDS is reused below
+        }
+    } else if (nslices > 0) {
+        u32x4 ra0[AV], rb0[BV], ra1[AV], rb1[BV];
+        const int last = nslices - 1;
+        gload(0, ra0, rb0);
+        gload(min(1, last), ra1, rb1);
+        lstore(0, ra0, rb0);
+        __syncthreads();
+        // At the top of each pair: buffer 0 holds slice s, ra1 slice s+1.
+        int s = 0;
+        for (; s + 1 < nslices; s += 2) {
+            phase(0, min(s + 2, last), ra0, rb0, ra1, rb1);  // multiply s, store s+1, load s+2
+            __syncthreads();
+            phase(1, min(s + 3, last), ra1, rb1, ra0, rb0);  // multiply s+1, store s+2, load s+3
+            __syncthreads();
+        }
+        if (s < nslices) compute(0, nothing);  // odd count: the last slice is in buffer 0
+    }
+
+    if constexpr (EVEN && STAGED) {
+        __syncthreads();
+        float* stg = wave < SA           ? reinterpret_cast<float*>(lds_a0) + wave * STG
+                     : wave < 2 * SA       ? reinterpret_cast<float*>(lds_a1) + (wave - SA) * STG
+                     : wave < 2 * SA + SB  ? reinterpret_cast<float*>(lds_b0) + (wave - 2 * SA) * STG
+                                           : reinterpret_cast<float*>(lds_b1) + (wave - 2 * SA - SB) * STG;
+        store_staged(stg);
+        return;
+    }
+    // ---- per-element epilogue (ragged tiles) ----
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -675,7 +752,23 @@ constexpr int tiled_dyn_lds() {
     return dyn;
 }
 
-template <int I, int O, int L, uint32_t E, int BM, int BN, int BK, int WM, int WN, int CAP, int DLS>
+// Workgroups of `kernel` resident on the whole device at once (a multiple of
+// eight, so that persistent workgroup b keeps XCD b % 8 for all its tiles),
+// at most `total`.
+static int resident_grid(const void* kernel, int threads, int dyn, int total) {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (cus[dev] <= 0 && hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus[dev] = 0;
+    int per = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, dyn) != hipSuccess) per = 0;
+    int g = (cus[dev] > 0 ? cus[dev] : 1) * (per > 0 ? per : 1);
+    if (g >= 8) g &= ~7;
+    return g < total ? g : total;
+}
+
+template <int I, int O, int L, uint32_t E, int BM, int BN, int BK, int WM, int WN, int CAP, int DLS, int PRS>
 static int launch_tiled_cfg(const tlg_plan& p, const void* X, const void* W, const void* bias, void* Y,
                             float* ws, hipStream_t stream) {
     constexpr int dyn = tiled_dyn_lds<CAP, tiled_lds_bytes<I, L, BM, BN, BK>()>();
@@ -702,18 +795,35 @@ static int launch_tiled_cfg(const tlg_plan& p, const void* X, const void* W, con
     // stc: the direct-load stage count (0: staged loads)
     auto go = [&](auto ev, auto sp, auto stc) {
         constexpr int st = decltype(stc)::value;
-        hipLaunchKernelGGL((tiled_kernel<I, O, L, E, BM, BN, BK, WM, WN, decltype(ev)::value, decltype(sp)::value, st>),
+        hipLaunchKernelGGL((tiled_kernel<I, O, L, E, BM, BN, BK, WM, WN, decltype(ev)::value, decltype(sp)::value, st,
+                                         false>),
                            grid, block, st > 0 ? dyn_dl : dyn, stream, X, W, bias, Y, ws, (int)p.M, (int)p.N, (int)p.K,
                            kper, resid);
         return check_launch("tiled_kernel");
     };
     auto go_split = [&](auto ev, auto stc) {
         constexpr int st = decltype(stc)::value;
-        hipLaunchKernelGGL((tiled_kernel<I, TLG_F32, L, 0u, BM, BN, BK, WM, WN, decltype(ev)::value, true, st>), grid,
+        hipLaunchKernelGGL((tiled_kernel<I, TLG_F32, L, 0u, BM, BN, BK, WM, WN, decltype(ev)::value, true, st, false>), grid,
                            block, st > 0 ? dyn_dl : dyn, stream, X, W, nullptr, nullptr, ws, (int)p.M, (int)p.N,
                            (int)p.K, kper, 0);
         return check_launch("tiled_kernel");
     };
+    if (p.persist) {
+        if constexpr (PRS > 0) {
+            if (!even || S != 1 || direct || (kper / BK) % 2 != 0 || kper < 2 * BK) {
+                set_error("tiled kernel: plan asks for persistent workgroups the shape cannot take");
+                return (int)TLG_ERR_INVALID_ARG;
+            }
+            const int G = resident_grid(
+                reinterpret_cast<const void*>(&tiled_kernel<I, O, L, E, BM, BN, BK, WM, WN, true, false, 0, true>),
+                64 * WM * WN, dyn, (int)(p.grid_x * p.grid_y));
+            hipLaunchKernelGGL((tiled_kernel<I, O, L, E, BM, BN, BK, WM, WN, true, false, 0, true>), dim3((unsigned)G),
+                               block, dyn, stream, X, W, bias, Y, ws, (int)p.M, (int)p.N, (int)p.K, kper, resid);
+            return check_launch("tiled_kernel");
+        }
+        set_error("tiled kernel: persistent workgroups on a tile without them");
+        return (int)TLG_ERR_INVALID_ARG;
+    }
     int rc;
     if (direct) {
         if constexpr (ST > 0)
@@ -751,13 +861,13 @@ int launch_tiled_in(const tlg_plan& p, const void* X, const void* W, const void*
                 constexpr uint32_t E = (uint32_t)decltype(epi)::value;
                 constexpr const TileCfg* T = I == TLG_F32 ? kTiledF32 : kTiled16;
                 constexpr int count = I == TLG_F32 ? kNumTiledF32 : kNumTiled16;
-                static_assert(kNumTiledF32 == 6 && kNumTiled16 == 9, "tile lists changed");
+                static_assert(kNumTiledF32 == 6 && kNumTiled16 == 10, "tile lists changed");
 #define TLG_TILED_CASE(i)                                                                                     \
     case i:                                                                                                   \
         if constexpr (i < count) {                                                                            \
             constexpr TileCfg c = T[i];                                                                       \
-            return launch_tiled_cfg<I, O, L, E, c.bm, c.bn, c.bk, c.wm, c.wn, c.cap, c.dl>(p, X, W, bias, Y, wsf, \
-                                                                                           stream);           \
+            return launch_tiled_cfg<I, O, L, E, c.bm, c.bn, c.bk, c.wm, c.wn, c.cap, c.dl, c.pers>(p, X, W, bias, Y, \
+                                                                                                   wsf, stream);   \
         }                                                                                                     \
         break;
                 switch (p.tile) {
@@ -770,6 +880,7 @@ int launch_tiled_in(const tlg_plan& p, const void* X, const void* W, const void*
                     TLG_TILED_CASE(6)
                     TLG_TILED_CASE(7)
                     TLG_TILED_CASE(8)
+                    TLG_TILED_CASE(9)
                 default: break;
                 }
                 set_error("bad tiled tile");

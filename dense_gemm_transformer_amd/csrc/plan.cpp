@@ -203,14 +203,17 @@ static int fill_tiled(tlg_plan& p, int tile, int split) {
     p.ws_bytes = p.split > 1 ? (size_t)p.split * (size_t)p.M * (size_t)p.N * sizeof(float) : 0;
     // Direct loads into LDS: 16-bit [M][K]·[N][K] operands, exact-fit tiles,
     // each split a whole number of stage rounds, operand panels in 32-bit range.
+    const int64_t kper = ceil_div(ceil_div(p.K, p.split), c.bk) * c.bk;
+    const int64_t es = dtype_size(p.in_dt);
+    const bool at = layout_a_transposed(p.layout), kn = layout_b_kn(p.layout);
+    const bool exact = p.M % c.bm == 0 && p.N % c.bn == 0 && kper * p.split == p.K &&
+                       (at ? p.K * p.M * es : (int64_t)c.bm * p.K * es) < INT32_MAX &&
+                       (kn ? p.K * p.N * es : (int64_t)c.bn * p.K * es) < INT32_MAX;
     p.stages = 0;
-    if (c.dl > 0 && p.in_dt != TLG_F32 && p.layout == TLG_NK) {
-        const int64_t kper = ceil_div(ceil_div(p.K, p.split), c.bk) * c.bk;
-        const int64_t es = dtype_size(p.in_dt);
-        if (p.M % c.bm == 0 && p.N % c.bn == 0 && kper * p.split == p.K && (kper / c.bk) % c.dl == 0 &&
-            (int64_t)c.bm * p.K * es < INT32_MAX && (int64_t)c.bn * p.K * es < INT32_MAX)
-            p.stages = c.dl;
-    }
+    if (c.dl > 0 && p.in_dt != TLG_F32 && p.layout == TLG_NK && exact && (kper / c.bk) % c.dl == 0)
+        p.stages = c.dl;
+    // Persistent workgroups: exact fit, no split, an even number of slices.
+    p.persist = c.pers && p.stages == 0 && exact && p.split == 1 && (kper / c.bk) % 2 == 0 && kper >= 2 * c.bk;
     return TLG_OK;
 }
 
@@ -381,13 +384,14 @@ int gemm_plan_describe(tlg_plan_t p, char* buf, size_t n) {
     char tmp[320];
     int len = snprintf(tmp, sizeof tmp,
                        "variant=%s M=%lld N=%lld K=%lld in=%s out=%s layout=%s epi=%s%s%s tile=%dx%dx%d "
-                       "split=%d threads=%d grid=%lldx%lldx%lld launches=%d ws=%zu%s",
+                       "split=%d threads=%d grid=%lldx%lldx%lld launches=%d ws=%zu%s%s",
                        vname[p->variant], (long long)p->M, (long long)p->N, (long long)p->K,
                        dname[p->in_dt], dname[p->out_dt], lname[p->layout],
                        (p->epi & TLG_EPI_BIAS) ? "bias" : "none", (p->epi & TLG_EPI_GELU_TANH) ? "+gelu" : "",
                        (p->epi & TLG_EPI_RESIDUAL) ? "+res" : "", p->bm, p->bn, p->bk, p->split,
                        p->threads, (long long)p->grid_x, (long long)p->grid_y, (long long)p->grid_z,
-                       p->launches, p->ws_bytes, p->variant == TLG_VARIANT_TILED && p->stages ? " load=direct" : "");
+                       p->launches, p->ws_bytes, p->variant == TLG_VARIANT_TILED && p->stages ? " load=direct" : "",
+                       p->variant == TLG_VARIANT_TILED && p->persist ? " persistent" : "");
     if (buf && n) {
         size_t c = (size_t)len < n - 1 ? (size_t)len : n - 1;
         memcpy(buf, tmp, c);

@@ -32,6 +32,7 @@ struct TileCfg {
     int wm, wn;      // waves along M and N
     int cap = 0;     // workgroups per CU at most (enforced with unused LDS); 0: as registers and LDS allow
     int dl = 0;      // 16-bit [M][K]·[N][K] exact fit: LDS stages filled by direct loads (0: staged in registers)
+    int pers = 0;    // exact fit, no split, even slice count: one workgroup per resident slot loops over tiles
 };
 
 // Tiles of the LDS-tiled MFMA kernel, per input class.  The index is what
@@ -63,6 +64,7 @@ constexpr TileCfg kTiled16[] = {
     {128, 128, 64, 2, 2, 0, 2},   // 6: direct loads, two stages
     {256, 128, 64, 2, 2, 0, 2},   // 7: direct loads, two stages
     {128, 128, 32, 2, 2, 0, 4},   // 8: direct loads, four 32-deep stages (three slices in flight)
+    {128, 128, 64, 2, 2, 0, 0, 1},  // 9: persistent, the next tile's first slices loaded during this one's end
 };
 constexpr int kNumTiledF32 = sizeof(kTiledF32) / sizeof(kTiledF32[0]);
 constexpr int kNumTiled16 = sizeof(kTiled16) / sizeof(kTiled16[0]);
@@ -119,6 +121,7 @@ struct tlg_plan {
     size_t ws_bytes;
     int bm, bn, bk;
     int stages;  // TILED: LDS stages filled by direct loads (0: loads staged through registers)
+    int persist;  // TILED: workgroups loop over tiles (grid sized at launch to the resident workgroups)
 };
 
 namespace tlg {

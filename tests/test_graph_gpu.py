@@ -51,8 +51,11 @@ def test_captured_sequence_replays_bitwise():
                variant=tlgemm.VARIANT_TILED, tile=7, split_k=2),                      # direct LDS loads, split
         _setup(inputs.random_case(45, 512, 256, 768, "f16", gelu=True),
                variant=tlgemm.VARIANT_TILED, tile=9),                                 # four direct-load stages
+        _setup(inputs.random_case(46, 1024, 512, 256, "bf16", bias=True),
+               variant=tlgemm.VARIANT_TILED, tile=10),                                # persistent workgroups
     ]
-    assert all("load=direct" in g["plan"].describe() for g in gemms[-2:])
+    assert all("load=direct" in g["plan"].describe() for g in gemms[-3:-1])
+    assert "persistent" in gemms[-1]["plan"].describe()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())  # inputs, outputs and zeroed workspaces come from the default stream
     with torch.cuda.stream(s):

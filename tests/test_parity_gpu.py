@@ -151,8 +151,8 @@ def test_gpt2_layer_m128(dtype):
         _check(c)
 
 
-def _sampled(case, npts=3000, rows=8, seed=0):
-    Y, desc = run_case(case)
+def _sampled(case, npts=3000, rows=8, seed=0, **force):
+    Y, desc = run_case(case, **force)
     y = to_f64(Y)
     rng = np.random.default_rng(seed)
     mi = rng.integers(0, case.M, npts)
@@ -166,6 +166,32 @@ def _sampled(case, npts=3000, rows=8, seed=0):
     assert err <= TOL[case.in_dtype], f"{desc}: err {err:.3e}"
     assert np.all(np.isfinite(y))
     return y, desc
+
+
+def test_tiled_persistent():
+    """Persistent workgroups (tile option 10, 128x128x64): a workgroup per resident slot loops over tiles, loading
+    the next tile's first slices while the current one finishes.  1024 or 512 tiles: several per workgroup."""
+    for (M, N, K), pair, layout, epi, res in [((4096, 4096, 256), ("bf16", "bf16"), "NK", (True, True), False),
+                                              ((4096, 2048, 512), ("f16", "f32"), "NK", (True, False), False),
+                                              ((2048, 4096, 128), ("bf16", "f32"), "KN", (False, False), False),
+                                              ((4096, 4096, 128), ("bf16", "bf16"), "NK", (True, False), True)]:
+        c = inputs.random_case(17, M, N, K, pair[0], pair[1], layout, bias=epi[0], gelu=epi[1], residual=res)
+        if res:  # the sampled check below compares against the oracle with the residual added
+            _, desc = _check(c, variant=tlgemm.VARIANT_TILED, tile=10)
+        else:
+            _, desc = _sampled(c, npts=2000, variant=tlgemm.VARIANT_TILED, tile=10)
+        assert "persistent" in desc, desc
+
+
+def test_tiled_persistent_small_and_fallbacks():
+    """Fewer tiles than resident workgroups (one tile each), and shapes the persistent loop does not take."""
+    c = _case(18, 512, 512, 512, ("bf16", "bf16"), "NK", (True, True))
+    _, desc = _check(c, variant=tlgemm.VARIANT_TILED, tile=10)
+    assert "persistent" in desc, desc
+    for (M, N, K), split in [((512, 512, 192), 1), ((512, 512, 1024), 2), ((500, 512, 512), 1)]:
+        c = _case(19, M, N, K, ("bf16", "bf16"), "NK", (True, False))
+        _, desc = _check(c, variant=tlgemm.VARIANT_TILED, tile=10, split_k=split)
+        assert "persistent" not in desc, desc
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
