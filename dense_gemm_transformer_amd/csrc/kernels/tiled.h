@@ -21,6 +21,9 @@
 //    straight into one of that many LDS buffers, unpadded and swizzled, with
 //    no LDS stores and no staging registers; waits on the vector-memory
 //    counter and one barrier per slice order the buffers.
+//  * Tiles marked persistent run one workgroup per resident slot, each
+//    walking tiles b, b + grid, ...; the last phases of a tile load the next
+//    tile's first slices, so its start overlaps this tile's end.
 //  * LDS rows are k-contiguous with a 16-byte pad (stride 80 B), so the
 //    16-byte operand reads of 16 consecutive rows hit 64 distinct banks.
 //    A [K][N] weight or [K][M] first operand is stored to LDS as it lies in

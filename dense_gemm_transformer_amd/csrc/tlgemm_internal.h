@@ -54,6 +54,8 @@ constexpr TileCfg kTiledF32[] = {
 // the same shape.  Measured against staging on the GPT-2 linears at 8192
 // rows: faster for some shapes (attention output, proj), slower for others
 // (qkv), so they are separate entries for the table search to choose from.
+// Entry 9 is the staged 128x128x64 tile with persistent workgroups (faster
+// for qkv and fc, whose grids span two to three rounds of resident slots).
 constexpr TileCfg kTiled16[] = {
     {128, 128, 64, 2, 2},         // 0
     {64, 64, 64, 2, 2},           // 1: narrow grids, pairs with split-K
