@@ -570,6 +570,33 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) 
         }
     };
 
+    // Per-element epilogue: ragged tiles, and persistent tiles whose free LDS
+    // buffer holds fewer staging strips than there are waves.
+    auto store_direct = [&]() {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int n = n0 + wn0 + j * 32 + r;
+                float b = 0.0f;
+                if constexpr (!SPLIT && (EPI & TLG_EPI_BIAS) != 0)
+                    if (n < N) b = load_elem<IN>(bias, n);
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int m = m0 + wm0 + i * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
+                    if (m >= M || n >= N) continue;
+                    if constexpr (SPLIT) {
+                        ws[((int64_t)z * M + m) * N + n] = acc[i][j][e];
+                    } else {
+                        float v = epilogue<EPI>(acc[i][j][e], b);
+                        if (resid) v += load_elem<OUT>(Y, (int64_t)m * N + n);
+                        store_out<OUT>(Y, (int64_t)m * N + n, v);
+                    }
+                }
+            }
+        }
+    };
+
     if constexpr (PERS) {
         // Persistent workgroup: tiles blockIdx.x, blockIdx.x + gridDim.x, ...
         // (the host sizes the grid to the workgroups resident at once).  The
@@ -578,8 +605,7 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) 
         // through the LDS buffer its last slice was read from while the next
         // tile's first slice waits in the other.  The host guarantees an even
         // slice count, so a tile always ends after the second phase of a pair.
-        static_assert(EVEN && !SPLIT && !DL && SA + SB >= WM * WN,
-                      "persistent tiles: exact fit, no split, one buffer holds every wave's staging strip");
+        static_assert(EVEN && !SPLIT && !DL, "persistent tiles: exact fit, no split, staged loads");
         const int last = nslices - 1;
         u32x4 ra0[AV], rb0[BV], ra1[AV], rb1[BV];
         gload(0, ra0, rb0);
@@ -603,8 +629,11 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) 
                 phase(1, src(s + 3), ra1, rb1, ra0, rb0);
                 __syncthreads();
             }
-            store_staged(wave < SA ? reinterpret_cast<float*>(lds_a1) + wave * STG
-                                   : reinterpret_cast<float*>(lds_b1) + (wave - SA) * STG);
+            if constexpr (SA + SB >= WM * WN)  // every wave's strip in the buffer the last slice freed
+                store_staged(wave < SA ? reinterpret_cast<float*>(lds_a1) + wave * STG
+                                       : reinterpret_cast<float*>(lds_b1) + (wave - SA) * STG);
+            else
+                store_direct();
             __syncthreads();  // staging read back before the next tile's slice 1 is stored to buffer 1
             if (!more) break;
             tile = next;
@@ -687,28 +716,7 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) 
         return;
     }
     // ---- per-element epilogue (ragged tiles) ----
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int n = n0 + wn0 + j * 32 + r;
-            float b = 0.0f;
-            if constexpr (!SPLIT && (EPI & TLG_EPI_BIAS) != 0)
-                if (n < N) b = load_elem<IN>(bias, n);
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int m = m0 + wm0 + i * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
-                if (m >= M || n >= N) continue;
-                if constexpr (SPLIT) {
-                    ws[((int64_t)z * M + m) * N + n] = acc[i][j][e];
-                } else {
-                    float v = epilogue<EPI>(acc[i][j][e], b);
-                    if (resid) v += load_elem<OUT>(Y, (int64_t)m * N + n);
-                    store_out<OUT>(Y, (int64_t)m * N + n, v);
-                }
-            }
-        }
-    }
+    store_direct();
 }
 
 // Sum the split partials in split order, then the epilogue.  Four outputs per thread.
@@ -864,7 +872,7 @@ int launch_tiled_in(const tlg_plan& p, const void* X, const void* W, const void*
                 constexpr uint32_t E = (uint32_t)decltype(epi)::value;
                 constexpr const TileCfg* T = I == TLG_F32 ? kTiledF32 : kTiled16;
                 constexpr int count = I == TLG_F32 ? kNumTiledF32 : kNumTiled16;
-                static_assert(kNumTiledF32 == 6 && kNumTiled16 == 10, "tile lists changed");
+                static_assert(kNumTiledF32 == 8 && kNumTiled16 == 10, "tile lists changed");
 #define TLG_TILED_CASE(i)                                                                                     \
     case i:                                                                                                   \
         if constexpr (i < count) {                                                                            \

@@ -45,6 +45,8 @@ constexpr TileCfg kTiledF32[] = {
     {128, 128, 32, 2, 2},  // 3: deeper K slice
     {256, 256, 16, 2, 2},  // 4: 128×128 wave tiles
     {256, 256, 16, 2, 4},  // 5: eight waves, two per SIMD, 128×64 wave tiles
+    {128, 128, 16, 2, 2, 2, 0, 1},  // 6: entry 0 with persistent workgroups
+    {64, 64, 16, 2, 2, 0, 0, 1},    // 7: entry 1 with persistent workgroups
 };
 // 16-bit operands: v_mfma_f32_32x32x16_{f16,bf16}.  A slice of 32 elements
 // is only 256 MFMA cycles per wave, too short to hide one slice of load

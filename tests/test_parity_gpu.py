@@ -89,7 +89,7 @@ def test_stream_forced_split(pair, split):
 @pytest.mark.parametrize("layout", ["NK", "KN"])
 @pytest.mark.parametrize("epi", EPIS, ids=["none", "bias", "gelu", "bias+gelu"])
 def test_tiled(pair, layout, epi):
-    for tile in range(1, 7 if pair[0] == "f32" else 10):
+    for tile in range(1, 9 if pair[0] == "f32" else 11):
         for (M, N, K), split in [((130, 136, 72), 1), ((256, 256, 256), 1), ((64, 64, 32), 1),
                                  ((200, 264, 400), 3), ((33, 520, 1024), 4)]:
             c = _case(3, M, N, K, pair, layout, epi)
@@ -180,6 +180,14 @@ def test_tiled_persistent():
             _, desc = _check(c, variant=tlgemm.VARIANT_TILED, tile=10)
         else:
             _, desc = _sampled(c, npts=2000, variant=tlgemm.VARIANT_TILED, tile=10)
+        assert "persistent" in desc, desc
+
+
+def test_tiled_persistent_f32():
+    """fp32 persistent entries (options 7 and 8: 128x128x16 capped at two per CU, 64x64x16)."""
+    for tile, (M, N, K) in [(7, (4096, 4096, 64)), (8, (2048, 2048, 96))]:
+        c = inputs.random_case(20, M, N, K, "f32", "f32", "KN" if tile == 7 else "NK", bias=tile == 8, gelu=tile == 8)
+        _, desc = _sampled(c, npts=2000, variant=tlgemm.VARIANT_TILED, tile=tile)
         assert "persistent" in desc, desc
 
 
