@@ -301,10 +301,19 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) 
     }
     constexpr int AQ = BM * VPR / (64 * WAVES);  // direct loads per wave per slice: first operand
     constexpr int BQ = BN * VPR / (64 * WAVES);  // and the weight
+    int nm0 = 0, nn0 = 0;  // the next tile's origin (persistent loop)
     auto dload = [&](int s, int buf) {
+        int tm0 = m0, tn0 = n0;
+        if constexpr (PERS) {
+            if (s >= nslices) {  // slice s - nslices of the next tile
+                s -= nslices;
+                tm0 = nm0;
+                tn0 = nn0;
+            }
+        }
         const int k0 = kbeg + s * BK;
-        const S* xa = X + (int64_t)m0 * K + k0 + dl_off;
-        const S* wb = W + (int64_t)n0 * K + k0 + dl_off;
+        const S* xa = X + (int64_t)tm0 * K + k0 + dl_off;
+        const S* wb = W + (int64_t)tn0 * K + k0 + dl_off;
         S* As = abuf(buf);
         S* Bs = bbuf(buf);
         constexpr int64_t step = (int64_t)(64 / VPR) * WAVES;  // rows between a wave's instructions
@@ -605,29 +614,51 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) 
         // through the LDS buffer its last slice was read from while the next
         // tile's first slice waits in the other.  The host guarantees an even
         // slice count, so a tile always ends after the second phase of a pair.
-        static_assert(EVEN && !SPLIT && !DL, "persistent tiles: exact fit, no split, staged loads");
+        static_assert(EVEN && !SPLIT && (ST == 0 || ST == 2), "persistent tiles: exact fit, no split, two buffers");
         const int last = nslices - 1;
         u32x4 ra0[AV], rb0[BV], ra1[AV], rb1[BV];
-        gload(0, ra0, rb0);
-        gload(1, ra1, rb1);
-        lstore(0, ra0, rb0);
-        __syncthreads();
+        if constexpr (DL) {
+            dload(0, 0);
+        } else {
+            gload(0, ra0, rb0);
+            gload(1, ra1, rb1);
+            lstore(0, ra0, rb0);
+            __syncthreads();
+        }
         for (int tile = blockIdx.x;;) {
             const int next = tile + (int)gridDim.x;
             const bool more = next < total;
-            int nm0 = m0, nn0 = n0;
+            nm0 = m0;
+            nn0 = n0;
             if (more) {
                 tile_origin(next, nm0, nn0);
-                make_rsrc(nm0, nn0, nrsrc_a, nrsrc_b);
+                if constexpr (!DL) make_rsrc(nm0, nn0, nrsrc_a, nrsrc_b);
             }
             // slice j <= last of this tile; past it slice j - nslices of the next
             // tile, or this tile's last slice again when there is none
             auto src = [&](int j) { return j <= last || more ? j : last; };
-            for (int s = 0; s < nslices; s += 2) {
-                phase(0, src(s + 2), ra0, rb0, ra1, rb1);
-                __syncthreads();
-                phase(1, src(s + 3), ra1, rb1, ra0, rb0);
-                __syncthreads();
+            if constexpr (DL) {
+                // buffer 0 holds (or is receiving) slice s, as in the direct-load loop below
+                for (int s = 0; s < nslices; s += 2) {
+                    wait_vmcnt<0>();
+                    __syncthreads();
+                    dload(src(s + 1), 1);
+                    compute(0, nothing);
+                    dl_phase();
+                    wait_vmcnt<0>();
+                    __syncthreads();
+                    dload(src(s + 2), 0);
+                    compute(1, nothing);
+                    dl_phase();
+                }
+                __syncthreads();  // every wave is past its reads of buffer 1
+            } else {
+                for (int s = 0; s < nslices; s += 2) {
+                    phase(0, src(s + 2), ra0, rb0, ra1, rb1);
+                    __syncthreads();
+                    phase(1, src(s + 3), ra1, rb1, ra0, rb0);
+                    __syncthreads();
+                }
             }
             if constexpr (SA + SB >= WM * WN)  // every wave's strip in the buffer the last slice freed
                 store_staged(wave < SA ? reinterpret_cast<float*>(lds_a1) + wave * STG
@@ -635,7 +666,10 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) 
             else
                 store_direct();
             __syncthreads();  // staging read back before the next tile's slice 1 is stored to buffer 1
-            if (!more) break;
+            if (!more) {
+                if constexpr (DL) wait_vmcnt<0>();  // the last re-read has landed before the workgroup ends
+                break;
+            }
             tile = next;
             m0 = nm0;
             n0 = nn0;
@@ -821,16 +855,25 @@ static int launch_tiled_cfg(const tlg_plan& p, const void* X, const void* W, con
     };
     if (p.persist) {
         if constexpr (PRS > 0) {
-            if (!even || S != 1 || direct || (kper / BK) % 2 != 0 || kper < 2 * BK) {
+            if (!even || S != 1 || (kper / BK) % 2 != 0 || kper < 2 * BK || (direct && ST != 2)) {
                 set_error("tiled kernel: plan asks for persistent workgroups the shape cannot take");
                 return (int)TLG_ERR_INVALID_ARG;
             }
-            const int G = resident_grid(
-                reinterpret_cast<const void*>(&tiled_kernel<I, O, L, E, BM, BN, BK, WM, WN, true, false, 0, true>),
-                64 * WM * WN, dyn, (int)(p.grid_x * p.grid_y));
-            hipLaunchKernelGGL((tiled_kernel<I, O, L, E, BM, BN, BK, WM, WN, true, false, 0, true>), dim3((unsigned)G),
-                               block, dyn, stream, X, W, bias, Y, ws, (int)p.M, (int)p.N, (int)p.K, kper, resid);
-            return check_launch("tiled_kernel");
+            auto go_persistent = [&](auto stc) {
+                constexpr int st = decltype(stc)::value;
+                const int d = st > 0 ? dyn_dl : dyn;
+                const int G = resident_grid(
+                    reinterpret_cast<const void*>(&tiled_kernel<I, O, L, E, BM, BN, BK, WM, WN, true, false, st, true>),
+                    64 * WM * WN, d, (int)(p.grid_x * p.grid_y));
+                hipLaunchKernelGGL((tiled_kernel<I, O, L, E, BM, BN, BK, WM, WN, true, false, st, true>),
+                                   dim3((unsigned)G), block, d, stream, X, W, bias, Y, ws, (int)p.M, (int)p.N, (int)p.K,
+                                   kper, resid);
+                return check_launch("tiled_kernel");
+            };
+            if constexpr (ST == 2) {
+                if (direct) return go_persistent(ic<2>{});
+            }
+            return go_persistent(ic<0>{});
         }
         set_error("tiled kernel: persistent workgroups on a tile without them");
         return (int)TLG_ERR_INVALID_ARG;
@@ -872,7 +915,7 @@ int launch_tiled_in(const tlg_plan& p, const void* X, const void* W, const void*
                 constexpr uint32_t E = (uint32_t)decltype(epi)::value;
                 constexpr const TileCfg* T = I == TLG_F32 ? kTiledF32 : kTiled16;
                 constexpr int count = I == TLG_F32 ? kNumTiledF32 : kNumTiled16;
-                static_assert(kNumTiledF32 == 8 && kNumTiled16 == 10, "tile lists changed");
+                static_assert(kNumTiledF32 == 8 && kNumTiled16 == 11, "tile lists changed");
 #define TLG_TILED_CASE(i)                                                                                     \
     case i:                                                                                                   \
         if constexpr (i < count) {                                                                            \
@@ -892,6 +935,7 @@ int launch_tiled_in(const tlg_plan& p, const void* X, const void* W, const void*
                     TLG_TILED_CASE(7)
                     TLG_TILED_CASE(8)
                     TLG_TILED_CASE(9)
+                    TLG_TILED_CASE(10)
                 default: break;
                 }
                 set_error("bad tiled tile");

@@ -213,7 +213,8 @@ static int fill_tiled(tlg_plan& p, int tile, int split) {
     if (c.dl > 0 && p.in_dt != TLG_F32 && p.layout == TLG_NK && exact && (kper / c.bk) % c.dl == 0)
         p.stages = c.dl;
     // Persistent workgroups: exact fit, no split, an even number of slices.
-    p.persist = c.pers && p.stages == 0 && exact && p.split == 1 && (kper / c.bk) % 2 == 0 && kper >= 2 * c.bk;
+    p.persist = c.pers && (p.stages == 0 || p.stages == 2) && exact && p.split == 1 && (kper / c.bk) % 2 == 0 &&
+                kper >= 2 * c.bk;
     return TLG_OK;
 }
 

@@ -69,6 +69,7 @@ constexpr TileCfg kTiled16[] = {
     {256, 128, 64, 2, 2, 0, 2},   // 7: direct loads, two stages
     {128, 128, 32, 2, 2, 0, 4},   // 8: direct loads, four 32-deep stages (three slices in flight)
     {128, 128, 64, 2, 2, 0, 0, 1},  // 9: persistent, the next tile's first slices loaded during this one's end
+    {128, 128, 64, 2, 2, 0, 2, 1},  // 10: persistent with direct loads (warm-fast, slower in a cold pass of GPT-2 layers)
 };
 constexpr int kNumTiledF32 = sizeof(kTiledF32) / sizeof(kTiledF32[0]);
 constexpr int kNumTiled16 = sizeof(kTiled16) / sizeof(kTiled16[0]);

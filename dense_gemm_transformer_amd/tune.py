@@ -87,7 +87,7 @@ def candidates(case, tlgemm):
     if case.layout == "NK" and case.M <= 256:
         for tile in range(1, 6):
             opts += [(tlgemm.VARIANT_STREAM, tile, 0), (tlgemm.VARIANT_STREAM, tile, 1)]
-    for tile in range(1, 11):  # past the dtype's tile list the planner refuses, and the option is skipped
+    for tile in range(1, 12):  # past the dtype's tile list the planner refuses, and the option is skipped
         for split in (1, 2, 4, 8):
             opts.append((tlgemm.VARIANT_TILED, tile, split))
     for v, tile, split in opts:
@@ -285,7 +285,7 @@ def table_tile(plan) -> int:
     from . import tlgemm
 
     i = plan.info
-    for t in range(1, 11):
+    for t in range(1, 12):
         try:
             q = tlgemm.Plan.create(plan.M, plan.N, plan.K, plan.in_dtype, plan.out_dtype, plan.layout,
                                    bool(plan.epi_flags & 1), bool(plan.epi_flags & 2), i.variant, max(i.split_k, 1)

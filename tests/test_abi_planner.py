@@ -74,7 +74,7 @@ def _table_rows():
     path = os.path.join(os.path.dirname(t.__file__), "csrc", "dispatch_table.inc")
     rows = []
     for line in open(path):
-        m = re.match(r"\{(\d+), (\d+), (\d+), (\d), (\d), (\d), (\d)u, (\d), (\d), (\d+)\},", line.strip())
+        m = re.match(r"\{(\d+), (\d+), (\d+), (\d), (\d), (\d), (\d)u, (\d), (\d+), (\d+)\},", line.strip())
         if m and int(m.group(1)) > 0:
             rows.append(tuple(int(x) for x in m.groups()))
     return rows

@@ -89,7 +89,7 @@ def test_stream_forced_split(pair, split):
 @pytest.mark.parametrize("layout", ["NK", "KN"])
 @pytest.mark.parametrize("epi", EPIS, ids=["none", "bias", "gelu", "bias+gelu"])
 def test_tiled(pair, layout, epi):
-    for tile in range(1, 9 if pair[0] == "f32" else 11):
+    for tile in range(1, 9 if pair[0] == "f32" else 12):
         for (M, N, K), split in [((130, 136, 72), 1), ((256, 256, 256), 1), ((64, 64, 32), 1),
                                  ((200, 264, 400), 3), ((33, 520, 1024), 4)]:
             c = _case(3, M, N, K, pair, layout, epi)
@@ -176,11 +176,13 @@ def test_tiled_persistent():
                                               ((2048, 4096, 128), ("bf16", "f32"), "KN", (False, False), False),
                                               ((4096, 4096, 128), ("bf16", "bf16"), "NK", (True, False), True)]:
         c = inputs.random_case(17, M, N, K, pair[0], pair[1], layout, bias=epi[0], gelu=epi[1], residual=res)
-        if res:  # the sampled check below compares against the oracle with the residual added
-            _, desc = _check(c, variant=tlgemm.VARIANT_TILED, tile=10)
-        else:
-            _, desc = _sampled(c, npts=2000, variant=tlgemm.VARIANT_TILED, tile=10)
-        assert "persistent" in desc, desc
+        for tile in (10, 11):  # staged; direct loads where the operands allow them
+            if res:  # the sampled check below compares against the oracle with the residual added
+                _, desc = _check(c, variant=tlgemm.VARIANT_TILED, tile=tile)
+            else:
+                _, desc = _sampled(c, npts=2000, variant=tlgemm.VARIANT_TILED, tile=tile)
+            assert "persistent" in desc, desc
+            assert ("load=direct" in desc) == (tile == 11 and layout == "NK"), desc
 
 
 def test_tiled_persistent_f32():
