@@ -1,7 +1,7 @@
 """Search the plan space per shape and write the dispatch table.
 
     python -m dense_gemm_transformer_amd.tune [--out csrc/dispatch_table.inc] [--rounds 7]
-        [--budget 6] [--explore 2] [--exhaustive] [--only a,b] [--jsonl log] [--report md]
+        [--budget 6] [--explore 2] [--exhaustive] [--cold] [--only a,b] [--jsonl log] [--report md]
 
 The search loop of "Optimizing a GPT-2-class transformer on a GPU" (Act V),
 with its cost model and rules in ``search.py``.  For every workload shape (the
@@ -16,7 +16,9 @@ five linear-layer workloads and the backward GEMMs of a GPT-2-small layer):
    predictions, the ``--explore`` candidates the model is least sure of, and
    the incumbent, in paired rounds: one timing of each per round, the order
    rotating, all in one window.  Each timing replays a graph of back-to-back
-   launches, so host launch overhead does not hide microsecond kernels.  A
+   launches, so host launch overhead does not hide microsecond kernels; with
+   ``--cold`` the launches rotate over copies of the operands larger than the
+   Infinity Cache, as a pass over distinct layers reads them.  A
    candidate whose output differs from the incumbent's by more than the
    parity tolerance is dropped.
 4. Select: the fastest candidate replaces the incumbent only if the paired
@@ -115,6 +117,9 @@ def main(argv=None) -> int:
     ap.add_argument("--out", default=TABLE)
     ap.add_argument("--rounds", type=int, default=7)
     ap.add_argument("--launches", type=int, default=20, help="launches per captured graph")
+    ap.add_argument("--cold", action="store_true",
+                    help="rotate the launches over copies of X and W totalling over 512 MiB (more than the "
+                         "Infinity Cache), so that operands come from HBM as in a pass over distinct layers")
     ap.add_argument("--budget", type=int, default=6, help="candidates measured by best prediction")
     ap.add_argument("--explore", type=int, default=2, help="candidates measured by largest model uncertainty")
     ap.add_argument("--exhaustive", action="store_true", help="measure every allowed candidate")
@@ -152,6 +157,12 @@ def main(argv=None) -> int:
         shape = search.Shape(case.M, case.N, case.K, case.in_dtype, case.out_dtype)
         X, W = put(case.X, case.in_dtype), put(case.W, case.in_dtype)
         b = None if case.b is None else put(case.b, case.in_dtype)
+        # operand copies the captured launches rotate over (one: warm, the same operands every launch)
+        ncopy = 1
+        if args.cold:
+            nbytes = X.numel() * X.element_size() + W.numel() * W.element_size()
+            ncopy = min(64, max(2, -(-(512 << 20) // nbytes)))
+        XW = [(X, W)] + [(X.clone(), W.clone()) for _ in range(ncopy - 1)]
         ydt = tlgemm.torch_dtype(case.out_dtype)
         inc_plan = tlgemm.Plan.create(case.M, case.N, case.K, case.in_dtype, case.out_dtype, case.layout,
                                       case.b is not None, case.gelu)
@@ -182,8 +193,9 @@ def main(argv=None) -> int:
                 return None
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=s):
-                for _ in range(args.launches):
-                    p.run_ptrs(*args_, s.cuda_stream)
+                for i in range(args.launches):
+                    Xi, Wi = XW[i % ncopy]
+                    p.run_ptrs(Xi.data_ptr(), Wi.data_ptr(), *args_[2:], s.cuda_stream)
             g.replay()
             torch.cuda.synchronize()
             return (key, g, Y, ws)
