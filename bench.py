@@ -603,8 +603,8 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU layout is described "
-              "in DESIGN.md and not built.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this library has no multi-GPU path.",
+              file=sys.stderr)
         return 2
 
     import torch
