@@ -86,6 +86,7 @@ def tile_str(plan) -> str:
 PEAK_F32_TFLOPS = 157.3      # MI355X dense fp32 matrix
 PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16/fp16 matrix
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+PEAK_SCLK_MHZ = 2400.0       # the core clock the datasheet peaks assume
 COLD_COPIES = 16
 
 
@@ -141,25 +142,85 @@ def sampled_parity(case, y64, npts=2000, seed=0):
     return float(np.max(np.abs(y64[mi, ni] - ref)) / np.max(np.abs(ref)))
 
 
-def cpu_baseline(case, budget_s: float = 15.0):
-    """Time the oracle on a bounded row sample of ``case``; TFLOP/s-equivalent of the sample."""
-    import oracle
+def cpu_baseline(budget_s: float = 6.0):
+    """The oracle (plain C, fp64 accumulation, OpenMP over output rows) timed on this host's cores.
 
-    threads = oracle.max_threads()
-    probe = max(1, min(case.M, 2 * threads))  # one row per thread, twice: calibrates the per-row cost
-    t0 = time.perf_counter()
-    oracle.linear_case(case, rows=(0, probe))
-    per_row = max(time.perf_counter() - t0, 1e-3) / probe
-    rows = int(max(probe, min(case.M, budget_s / per_row)))
-    t0 = time.perf_counter()
-    oracle.linear_case(case, rows=(0, rows))
-    dt = time.perf_counter() - t0
-    flops = 2.0 * rows * case.N * case.K
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{rows} of {case.M} output rows of the {case.M}x{case.N}x{case.K} fp32 GEMM "
-                      f"({dt:.1f} s, fp64 accumulation, OpenMP over rows)",
+    Every workload: the whole output on all cores for the small ones (the
+    128x768x768 linear, the narrow 16x4096x4096 linear, the 128-row GPT-2
+    layer) together with a single-thread run of the whole output; for the
+    square 4096^3 GEMM and the M=8192 stack, a row sample on all cores and a
+    64-row slice on one thread, scaled to the whole workload and labelled
+    extrapolated.  The top-level value is the square fp32 all-core rate, the
+    workload the headline measures.
+    """
+    import oracle
+    from dense_gemm_transformer_amd import inputs
+
+    cores = oracle.max_threads()  # before any single-thread call changes the OpenMP default
+
+    def timed(case, rows, threads):
+        t0 = time.perf_counter()
+        oracle.linear_case(case, threads=threads, rows=rows)
+        return time.perf_counter() - t0
+
+    def full(cases):
+        flops = sum(c.flops for c in cases)
+        t_all = sum(timed(c, None, cores) for c in cases)
+        t_one = sum(timed(c, None, 1) for c in cases)
+        return {"flops": flops, "all_cores_s": round(t_all, 4), "single_thread_s": round(t_one, 4),
+                "all_cores_GFLOP/s": round(flops / t_all / 1e9, 2), "single_thread_GFLOP/s": round(flops / t_one / 1e9, 3),
+                "kind": "whole output"}
+
+    def sampled(cases, repeat: int, budget: float):
+        """Row sample per GEMM on all cores (about ``budget`` s in total) and a 64-row slice on one thread."""
+        flops = repeat * sum(c.flops for c in cases)
+        t_all = t_one = 0.0
+        rows_all = []
+        for c in cases:
+            probe = min(c.M, 2 * cores)
+            per_row = max(timed(c, (0, probe), cores), 1e-4) / probe
+            rows = int(min(c.M, max(probe, budget / len(cases) / per_row)))
+            t = timed(c, (0, rows), cores)
+            t_all += t * c.M / rows * repeat
+            rows_all.append(rows)
+            one = min(64, c.M)
+            t_one += timed(c, (0, one), 1) * c.M / one * repeat
+        return {"flops": flops, "all_cores_s": round(t_all, 3), "single_thread_s": round(t_one, 3),
+                "all_cores_GFLOP/s": round(flops / t_all / 1e9, 2), "single_thread_GFLOP/s": round(flops / t_one / 1e9, 3),
+                "kind": f"extrapolated: all cores from rows {rows_all} of each GEMM, one thread from 64 rows"
+                        + (f", times {repeat} layers" if repeat > 1 else "")}
+
+    per = {}
+    per["linear_128x768x768_f32"] = full([inputs.workload_fp32_linear_128x768()])
+    per["narrow_16x4096x4096_f16"] = full([inputs.workload_fp16_narrow()])
+    per["gpt2_layer_m128_f32"] = full(inputs.workload_gpt2_layer(M=128, dtype="f32"))
+    sq = inputs.workload_square(dtype="f32")
+    per["square_4096_f32"] = sampled([sq], 1, budget_s)
+    per["square_4096_bf16"] = sampled([inputs.workload_square(dtype="bf16")], 1, budget_s / 3)
+    for dt in ("f32", "bf16"):
+        layer0 = inputs.workload_gpt2_layer(5, 8192, dt, 0)
+        per[f"gpt2_stack_m8192_{dt}"] = sampled(layer0, 12, budget_s / 3)
+    head = per["square_4096_f32"]
+    return {"value": round(head["flops"] / head["all_cores_s"] / 1e12, 5), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"square fp32 4096^3 on {cores} threads, {head['kind']} ({head['all_cores_s']} s for the "
+                      "whole output); fp64 accumulation, OpenMP over rows",
             "affinity_cpus": len(os.sched_getaffinity(0)),
-            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
+            "per_workload": per}
+
+
+def clock_adjusted(ceilings, achieved: float, peak: float, dt: str) -> dict:
+    """The datasheet peak scaled to the core clock measured under the MFMA probe (the datasheet
+    figure assumes 2400 MHz), and the achieved fraction of it; empty without the probe."""
+    if not ceilings:
+        return {}
+    mhz = ceilings.get(f"sclk_MHz_under_mfma_{dt}")
+    if not mhz:
+        return {}
+    adj = peak * mhz / PEAK_SCLK_MHZ
+    return {"sclk_MHz_measured": mhz, "peak_clock_adjusted": round(adj, 2),
+            "frac_clock_adjusted": round(achieved / adj, 4)}
 
 
 def dev_tensor(torch, a, dt, dev):
@@ -241,20 +302,28 @@ def bench_ceilings(torch, dev, stream, cold_bufs):
         read(cold_bufs[i % len(cold_bufs)])
     cold_ms = time_launches(lambda i: read(cold_bufs[i % len(cold_bufs)]), 2000, stream)
     warm_ms = time_launches(lambda i: read(cold_bufs[0]), 2000, stream)
-    mfma = {}
+    mfma, clock_mhz = {}, {}
+    stamps = torch.zeros(4 * 256, dtype=torch.int64, device=dev)
+    khz = ctypes.c_int(0)
+    ok(lib.tlg_ceil_wall_clock_khz(ctypes.byref(khz)))
     for name, bf16, iters, flop in (("f32", 0, 2000, 4096), ("bf16", 1, 4000, 32768)):
-        call = lambda i: ok(lib.tlg_ceil_mfma(bf16, 256, iters, vp(sink.data_ptr()), s))
+        call = lambda i: ok(lib.tlg_ceil_mfma_clock(bf16, 256, iters, vp(sink.data_ptr()), vp(stamps.data_ptr()), s))
         call(0)
         ms = time_launches(call, 10, stream)
         mfma[name] = 256 * 4 * iters * 16 * flop / (ms * 1e-3) / 1e12
+        st = stamps.view(256, 4).cpu().numpy().astype(np.float64)  # the last launch's counters
+        clock_mhz[name] = float(np.median((st[:, 1] - st[:, 0]) / (st[:, 3] - st[:, 2]))) * khz.value / 1e3
     return {"empty_kernel_event_us": round(empty_ms * 1e3, 3),
             "read_cold_us": round(cold_ms * 1e3, 3), "read_cold_GB/s": round(nbytes / (cold_ms * 1e-3) / 1e9, 1),
             "read_warm_us": round(warm_ms * 1e3, 3), "read_bytes": nbytes,
             "mfma_f32_TFLOP/s": round(mfma["f32"], 1), "mfma_bf16_TFLOP/s": round(mfma["bf16"], 1),
+            "sclk_MHz_under_mfma_f32": round(clock_mhz["f32"], 1),
+            "sclk_MHz_under_mfma_bf16": round(clock_mhz["bf16"], 1),
             "method": "HIP events over back-to-back launches of the probes in libtlgceil.so: empty kernel "
                       "(256 workgroups), plain read of 32 MiB (256 workgroups x 8 waves x 16 loads of 16 B, "
                       f"cold = rotating {len(cold_bufs)} buffers), 16 independent 32x32 MFMA chains per wave "
-                      "on all CUs"}
+                      "on all CUs; sclk = median over workgroups of shader-clock ticks / constant-rate ticks "
+                      "(s_memtime / s_memrealtime) across the MFMA loop, times the constant rate"}
 
 
 def bench_c1(torch, dev, stream, no_parity: bool):
@@ -590,6 +659,65 @@ def bench_gpt2_forward(torch, dev, stream, dtype: str, no_parity: bool, layers: 
     return res
 
 
+def rocprof_summary(outdir: str, segments: list[str]) -> str:
+    """Markdown summary of a ``rocprofv3 --kernel-trace --stats --output-format csv`` run under ``outdir``.
+
+    One row per (kernel, launch grid in workgroups): launches, median, p10,
+    p90 and minimum duration, so that kernels of one template with different
+    tiles or grids are never pooled.  ``segments`` entries ``NAME@GRID=n1,n2,...``
+    split that row's launches, in dispatch order, into consecutive runs of
+    n1, n2, ... launches (for example the parity call, the cold launches and
+    the warm launches of one kernel), each summarised on its own.
+    """
+    import csv
+
+    traces = sorted(glob.glob(os.path.join(outdir, "**", "*kernel_trace.csv"), recursive=True))
+    stats = sorted(glob.glob(os.path.join(outdir, "**", "*kernel_stats.csv"), recursive=True))
+    if not traces:
+        raise SystemExit(f"no kernel_trace.csv under {outdir}")
+    groups: dict = {}
+    for path in traces:
+        with open(path, newline="") as f:
+            for row in csv.DictReader(f):
+                wg = [int(row[f"Workgroup_Size_{a}"]) for a in "XYZ"]
+                grid = [int(row[f"Grid_Size_{a}"]) // max(w, 1) for a, w in zip("XYZ", wg)]
+                key = (row["Kernel_Name"], "x".join(map(str, grid)))
+                dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
+                groups.setdefault(key, []).append((int(row["Dispatch_Id"]), dur))
+    lines = ["| kernel | grid (workgroups) | launches | median µs | p10 µs | p90 µs | min µs |",
+             "|---|---|---|---|---|---|---|"]
+    for (name, grid), v in sorted(groups.items(), key=lambda kv: -sum(d for _, d in kv[1])):
+        d = np.array([x for _, x in v])
+        lines.append(f"| `{name}` | {grid} | {len(d)} | {np.median(d):.2f} | {np.percentile(d, 10):.2f} | "
+                     f"{np.percentile(d, 90):.2f} | {d.min():.2f} |")
+    out = ["Per launch configuration (kernel begin to end, from the kernel trace):", "", *lines, ""]
+    for spec in segments:
+        key, counts = spec.rsplit("=", 1)
+        name, grid = key.rsplit("@", 1)
+        v = sorted(groups.get((name, grid), []))
+        sizes = [int(c) for c in counts.split(",")]
+        if sum(sizes) != len(v):
+            raise SystemExit(f"{name}@{grid}: {len(v)} launches in the trace, segments sum to {sum(sizes)}")
+        out += [f"`{name}` at grid {grid}, launches in dispatch order split into runs of {counts}:", "",
+                "| run | launches | median µs | p10 µs | p90 µs |", "|---|---|---|---|---|"]
+        i = 0
+        for k, n in enumerate(sizes):
+            d = np.array([x for _, x in v[i:i + n]])
+            i += n
+            out.append(f"| {k} | {n} | {np.median(d):.2f} | {np.percentile(d, 10):.2f} | {np.percentile(d, 90):.2f} |")
+        out.append("")
+    for path in stats:
+        with open(path, newline="") as f:
+            rows = list(csv.DictReader(f))
+        out += [f"rocprofv3 `--stats` ({os.path.basename(path)}):", "",
+                "| kernel | calls | average µs | min µs | max µs |", "|---|---|---|---|---|"]
+        for r in rows:
+            out.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                       f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+        out.append("")
+    return "\n".join(out)
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -600,7 +728,15 @@ def main(argv=None) -> int:
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the ceiling probes and the 128-row layer and M=8192 stack workloads")
+    ap.add_argument("--rocprof-summary", metavar="DIR",
+                    help="print a markdown summary of a rocprofv3 kernel-trace run under DIR and exit (no GPU)")
+    ap.add_argument("--segment", action="append", default=[], metavar="NAME@GRID=n1,n2,...",
+                    help="with --rocprof-summary: split one kernel's launches into consecutive runs")
     args = ap.parse_args(argv)
+
+    if args.rocprof_summary:
+        print(rocprof_summary(args.rocprof_summary, args.segment))
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this library has no multi-GPU path.",
@@ -712,8 +848,19 @@ def main(argv=None) -> int:
 
     cpu = None
     if not args.no_cpu_baseline:
-        log("cpu baseline: timing the oracle on a row sample")
-        cpu = cpu_baseline(sq)
+        log("cpu baseline: timing the oracle on every workload (whole outputs or row samples)")
+        cpu = cpu_baseline()
+        gpu_s = {"square_4096_f32": ms * 1e-3, "square_4096_bf16": msb * 1e-3,
+                 "narrow_16x4096x4096_f16": n_ms * 1e-3}
+        if "linear_128x768x768_f32" in extra:
+            gpu_s["linear_128x768x768_f32"] = extra["linear_128x768x768_f32"]["warm_us"] * 1e-6
+            gpu_s["gpt2_layer_m128_f32"] = extra["gpt2_layer_m128_f32"]["layer_warm_us"] * 1e-6
+            for dt in ("f32", "bf16"):
+                gpu_s[f"gpt2_stack_m8192_{dt}"] = extra[f"gpt2_stack_m8192_{dt}"]["pass_ms"] * 1e-3
+        for k, v in cpu["per_workload"].items():
+            if k in gpu_s:
+                v["gpu_s"] = gpu_s[k]
+                v["gpu_over_oracle_all_cores"] = round(v["all_cores_s"] / gpu_s[k], 1)
 
     tol32, tol16 = 1e-5, 1e-2
     out = {
@@ -737,7 +884,8 @@ def main(argv=None) -> int:
                      "traffic_unit": "bytes per launch (L2<->memory, rocprofv3 FETCH_SIZE+WRITE_SIZE)",
                      "algorithmic_bytes_per_launch": 3 * sq.M * sq.N * 4,
                      "kernel": f"tiled_kernel fp32 {plan.info.tile_m}x{plan.info.tile_n}x{plan.info.tile_k}",
-                     "algorithmic_flops_per_launch": sq.flops},
+                     "algorithmic_flops_per_launch": sq.flops,
+                     **clock_adjusted(extra.get("ceilings"), sq_tflops, PEAK_F32_TFLOPS, "f32")},
         "cpu_baseline": cpu,
         "parity": {"square_f32_err": sq_err, "square_f32_pass": None if sq_err is None else sq_err <= tol32,
                    "square_bf16_err": sqb_err, "narrow_f16_err": n_err,
@@ -745,6 +893,8 @@ def main(argv=None) -> int:
                    "measure": "max|err|/max|ref| on sampled outputs vs the CPU oracle"},
         "square_bf16": {"us": round(msb * 1e3, 2), "TFLOP/s": round(sqb.flops / (msb * 1e-3) / 1e12, 2),
                         "frac_mfma_peak": round(sqb.flops / (msb * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                        **clock_adjusted(extra.get("ceilings"), sqb.flops / (msb * 1e-3) / 1e12, PEAK_BF16_TFLOPS,
+                                         "bf16"),
                         "plan": planb.describe()},
         "narrow_fp16": {"workload": "fp16 linear Y=X.W^T, M=16, K=4096, N=4096, W out x in, fp16 out, cold W "
                                     f"({COLD_COPIES} rotated copies)",

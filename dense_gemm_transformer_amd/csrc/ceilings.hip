@@ -46,8 +46,17 @@ __global__ __launch_bounds__(64 * kReadWaves) void read_kernel(const char* __res
 // Sixteen independent 32x32 accumulators per wave, so consecutive MFMAs never
 // wait on each other; the operands stay in registers.  One wave per SIMD
 // (256 threads per workgroup, one workgroup per CU when the grid is the CU count).
+// With `stamps`, thread 0 of each workgroup records the shader-clock counter
+// (s_memtime) and the constant-rate counter (s_memrealtime) before and after
+// the MFMA loop: their ratio is the core clock the loop ran at.
 template <bool BF16>
-__global__ __launch_bounds__(256) void mfma_kernel(int iters, float* __restrict__ sink) {
+__global__ __launch_bounds__(256) void mfma_kernel(int iters, float* __restrict__ sink,
+                                                   unsigned long long* __restrict__ stamps) {
+    unsigned long long c0 = 0, r0 = 0;
+    if (stamps && threadIdx.x == 0) {
+        c0 = __builtin_amdgcn_s_memtime();
+        r0 = __builtin_amdgcn_s_memrealtime();
+    }
     f32x16 acc[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i)
@@ -74,6 +83,14 @@ __global__ __launch_bounds__(256) void mfma_kernel(int iters, float* __restrict_
     for (int i = 0; i < 16; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e) s += acc[i][e];
+    if (stamps && threadIdx.x == 0) {
+        const unsigned long long c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+        unsigned long long* o = stamps + 4 * (size_t)blockIdx.x;
+        o[0] = c0;
+        o[1] = c1;
+        o[2] = r0;
+        o[3] = r1;
+    }
     if (s == 1234.5f) sink[threadIdx.x] = s;
 }
 
@@ -101,12 +118,27 @@ int tlg_ceil_read(const void* p, size_t bytes, float* sink, void* stream) {
 // 16·iters MFMAs (bf16 != 0: 32x32x16 bf16, 32768 flop each; else 32x32x2
 // fp32, 4096 flop each).  `sink` must hold 256 floats.
 int tlg_ceil_mfma(int bf16, int grid, int iters, float* sink, void* stream) {
+    return tlg_ceil_mfma_clock(bf16, grid, iters, sink, nullptr, stream);
+}
+
+// The same probe; `stamps` (NULL or 4·grid counters) receives per workgroup
+// the shader-clock counter before and after the loop, then the constant-rate
+// counter before and after.
+int tlg_ceil_mfma_clock(int bf16, int grid, int iters, float* sink, unsigned long long* stamps, void* stream) {
     if (grid <= 0 || iters <= 0 || !sink) return -1;
     if (bf16)
-        hipLaunchKernelGGL(mfma_kernel<true>, dim3(grid), dim3(256), 0, (hipStream_t)stream, iters, sink);
+        hipLaunchKernelGGL(mfma_kernel<true>, dim3(grid), dim3(256), 0, (hipStream_t)stream, iters, sink, stamps);
     else
-        hipLaunchKernelGGL(mfma_kernel<false>, dim3(grid), dim3(256), 0, (hipStream_t)stream, iters, sink);
+        hipLaunchKernelGGL(mfma_kernel<false>, dim3(grid), dim3(256), 0, (hipStream_t)stream, iters, sink, stamps);
     return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+// Rate of the constant-rate counter (s_memrealtime) of the current device, in kHz.
+int tlg_ceil_wall_clock_khz(int* khz) {
+    if (!khz) return -1;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return -6;
+    return hipDeviceGetAttribute(khz, hipDeviceAttributeWallClockRate, dev) == hipSuccess ? 0 : -6;
 }
 
 }  // extern "C"

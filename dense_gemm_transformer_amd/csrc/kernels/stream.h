@@ -238,8 +238,7 @@ static int launch_stream_cfg(const tlg_plan& p, const void* X, const void* W, co
     const bool even = (int64_t)kper * S == p.K && kper % (KW * LOADS * 4 * Elem<I>::per16) == 0;
     const dim3 grid((unsigned)p.grid_x, (unsigned)S, (unsigned)p.grid_z), block(64 * NB * KW);
     unsigned* tickets = static_cast<unsigned*>(ws);
-    float* part =
-        ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + stream_ticket_bytes(p.grid_x * p.grid_z)) : nullptr;
+    float* part = ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + kWsCounterBytes) : nullptr;
     auto with_out = [&](auto f) {
         if constexpr (I == TLG_F32) return f(ic<TLG_F32>{});
         else if (p.out_dt == TLG_F32) return f(ic<TLG_F32>{});

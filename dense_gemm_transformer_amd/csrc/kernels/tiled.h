@@ -902,7 +902,8 @@ static int launch_tiled_cfg(const tlg_plan& p, const void* X, const void* W, con
 template <int I>
 int launch_tiled_in(const tlg_plan& p, const void* X, const void* W, const void* bias, void* Y, void* ws,
                     hipStream_t stream) {
-    float* wsf = static_cast<float*>(ws);
+    // split partials follow the workspace's counter block, which tiled plans leave untouched
+    float* wsf = ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + kWsCounterBytes) : nullptr;
     auto with_out = [&](auto f) {
         if constexpr (I == TLG_F32) return f(ic<TLG_F32>{});
         else if (p.out_dt == TLG_F32) return f(ic<TLG_F32>{});

@@ -150,7 +150,12 @@ static int fill_stream(tlg_plan& p, int tile, int split) {
     p.grid_z = ceil_div(p.M, 16 * rowb);
     p.launches = 1;
     const int64_t slots = tiles * p.grid_z;  // (row block, tile) pairs, one ticket each
-    p.ws_bytes = S > 1 ? stream_ticket_bytes(slots) + (size_t)S * slots * bn * 16 * rowb * sizeof(float) : 0;
+    if (S > 1 && slots > kWsMaxTickets) {
+        set_error("stream split-K: %lld output tiles exceed the %lld arrival counters of a workspace",
+                  (long long)slots, (long long)kWsMaxTickets);
+        return TLG_ERR_UNSUPPORTED;
+    }
+    p.ws_bytes = S > 1 ? kWsCounterBytes + (size_t)S * slots * bn * 16 * rowb * sizeof(float) : 0;
     return TLG_OK;
 }
 
@@ -200,7 +205,7 @@ static int fill_tiled(tlg_plan& p, int tile, int split) {
         return TLG_ERR_UNSUPPORTED;
     }
     p.launches = p.split > 1 ? 2 : 1;
-    p.ws_bytes = p.split > 1 ? (size_t)p.split * (size_t)p.M * (size_t)p.N * sizeof(float) : 0;
+    p.ws_bytes = p.split > 1 ? kWsCounterBytes + (size_t)p.split * (size_t)p.M * (size_t)p.N * sizeof(float) : 0;
     // Direct loads into LDS: 16-bit [M][K]·[N][K] operands, exact-fit tiles,
     // each split a whole number of stage rounds, operand panels in 32-bit range.
     const int64_t kper = ceil_div(ceil_div(p.K, p.split), c.bk) * c.bk;

@@ -133,7 +133,12 @@ namespace tlg {
 void set_error(const char* fmt, ...);
 int launch_plan(const tlg_plan& p, const void* X, const void* W, const void* bias, void* Y,
                 void* ws, void* stream);
-// Workspace of a split stream plan: one ticket per tile (a 256-byte aligned
-// block), then the fp32 partials [S][M][N].
-inline size_t stream_ticket_bytes(int64_t tiles) { return (size_t)ceil_div(tiles * 4, 256) * 256; }
+// Workspace of every split plan: a fixed block of arrival counters first,
+// then the fp32 partials.  Split stream plans keep one counter per
+// (row block, tile) there and their last workgroup per tile resets it;
+// tiled split plans never touch the block.  So every completed run of any
+// plan leaves the counters zero, and one workspace, zeroed once, serves any
+// sequence of plans.
+constexpr size_t kWsCounterBytes = 64 * 1024;
+constexpr int64_t kWsMaxTickets = (int64_t)(kWsCounterBytes / 4);
 }  // namespace tlg

@@ -34,6 +34,17 @@ int tlg_ceil_read(const void* p, size_t bytes, float* sink, void* stream);
  * each).  `sink` holds 256 floats, written like `tlg_ceil_read`'s. */
 int tlg_ceil_mfma(int bf16, int grid, int iters, float* sink, void* stream);
 
+/* tlg_ceil_mfma, and the core clock it ran at: `stamps` is NULL or holds
+ * 4·`grid` counters; thread 0 of workgroup g writes stamps[4g .. 4g+3] = the
+ * shader-clock counter (s_memtime) before and after its MFMA loop, then the
+ * constant-rate counter (s_memrealtime) before and after.  The clock is
+ * (s1 - s0) / (r1 - r0) times the constant rate. */
+int tlg_ceil_mfma_clock(int bf16, int grid, int iters, float* sink, unsigned long long* stamps, void* stream);
+
+/* Rate of the constant-rate counter of the current device in kHz (the HIP
+ * wall-clock rate attribute); 0 on success, -6 if the runtime refuses. */
+int tlg_ceil_wall_clock_khz(int* khz);
+
 #ifdef __cplusplus
 }
 #endif

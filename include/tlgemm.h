@@ -137,12 +137,15 @@ int gemm_plan_info(tlg_plan_t p, tlg_plan_info* info);
  * X, W, Y (and bias if TLG_EPI_BIAS) must be non-NULL device pointers, 16-byte aligned; bias must
  * be NULL when TLG_EPI_BIAS is not set.  Y must not overlap X, W or bias.
  * workspace: device memory of at least gemm_workspace_size(p) bytes when
- * that is non-zero; it may be NULL when the size is 0.  It must be
- * zero-filled before its first use, and every completed run leaves it
- * reusable: split stream plans keep one arrival counter per output tile in
- * it, which the last workgroup of each tile resets to zero.  Runs in flight
- * at the same time need distinct workspaces.  A plan is immutable:
- * concurrent runs of one plan are safe when each has its own workspace.
+ * that is non-zero; it may be NULL when the size is 0.  Its first 64 KiB
+ * hold arrival counters and the rest fp32 split partials.  It must be
+ * zero-filled before its first use; after that every completed run of any
+ * plan leaves the counters zero (split stream plans reset the counter of
+ * each output tile in their last workgroup, tiled split plans write only
+ * past the counters), so one workspace serves any sequence of plans whose
+ * sizes it covers.  Runs in flight at the same time need distinct
+ * workspaces.  A plan is immutable: concurrent runs of one plan are safe
+ * when each has its own workspace.
  */
 int gemm_run(tlg_plan_t p, const void* X, const void* W, const void* bias, void* Y,
              void* workspace, size_t ws_bytes, void* stream);

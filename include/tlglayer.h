@@ -44,7 +44,7 @@ int tlg_layernorm(const void* X, const void* gamma, const void* beta, void* Y, f
  * tlg_attention — scaled dot-product attention of each head over the output
  * of a GPT-2 qkv projection, fused: the score matrix is never written.
  *
- * "Optimizing a GPT-2-class transformer on a GPU", section "Fusing attention:
+ * "Writing a CUDA matmul that catches cuBLAS", section "Fusing attention:
  * the score matrix never exists": an online softmax (running maximum and sum,
  * earlier partial results rescaled when the maximum rises), causality as a
  * loop bound, and q, k, v read in place from the (B, T, 3C) projection.

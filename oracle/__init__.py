@@ -247,11 +247,22 @@ def max_threads() -> int:
 def normalized_error(y, ref) -> float:
     """max|y - ref| / max|ref|, the matmul error measure of "Writing a CUDA
     matmul that catches cuBLAS", section "The measurement was nearly wrong".
+
+    Both maxima run over the whole output; the denominator is the reference's
+    largest magnitude, never the result's.  Shapes must match exactly (no
+    broadcasting).  A NaN anywhere in ``y`` yields NaN, which passes no
+    tolerance; a zero reference gives 0 for a zero result and inf otherwise.
     """
     y = np.asarray(y, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
-    denom = np.max(np.abs(ref)) if ref.size else 0.0
-    num = np.max(np.abs(y - ref)) if ref.size else 0.0
+    if y.shape != ref.shape:
+        raise ValueError(f"result shape {y.shape} != reference shape {ref.shape}")
+    if ref.size == 0:
+        return 0.0
+    denom = np.max(np.abs(ref))
+    num = np.max(np.abs(y - ref))
+    if np.isnan(num):
+        return float("nan")
     if denom == 0.0:
         return 0.0 if num == 0.0 else float("inf")
     return float(num / denom)

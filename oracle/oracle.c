@@ -194,7 +194,7 @@ int oracle_layernorm(int64_t rows, int64_t C, int dtype, const void* X, const vo
 
 /*
  * Scaled dot-product attention over the output of the qkv projection
- * ("Optimizing a GPT-2-class transformer on a GPU", section "Fusing attention:
+ * ("Writing a CUDA matmul that catches cuBLAS", section "Fusing attention:
  * the score matrix never exists"): qkv is [B][T][3C] with C = NH * HS, the
  * query of head h at columns h*HS .. h*HS+HS-1, its key C further and its
  * value 2C further.  For each (b, h, i):

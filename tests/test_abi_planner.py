@@ -30,7 +30,8 @@ def test_ceiling_probe_library_exports_its_header():
     hdr = os.path.join(os.path.dirname(HEADER), "tlgceil.h")
     text = re.sub(r"/\*.*?\*/", "", open(hdr).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(tlg_ceil_\w+)\s*\(", text)))
-    assert names == ["tlg_ceil_empty", "tlg_ceil_mfma", "tlg_ceil_read"]
+    assert names == ["tlg_ceil_empty", "tlg_ceil_mfma", "tlg_ceil_mfma_clock", "tlg_ceil_read",
+                     "tlg_ceil_wall_clock_khz"]
     lib = ctypes.CDLL(os.path.join(os.path.dirname(t.LIB_PATH), "libtlgceil.so"))
     for name in names:
         assert hasattr(lib, name), name
@@ -52,7 +53,7 @@ def test_stream_split_rules():
     # narrow N: 128-row tiles with K split across workgroups
     i = _plan(16, 768, 3072, "f16").info
     assert (i.variant, i.tile_n, i.split_k) == (t.VARIANT_STREAM, 128, 6)
-    assert i.workspace_bytes == 256 + 6 * 6 * 128 * 16 * 4  # tickets, then fragment-order partials
+    assert i.workspace_bytes == 65536 + 6 * 6 * 128 * 16 * 4  # the counter block, then fragment-order partials
     i = _plan(5, 1000, 1000, "f32").info  # fp32 chunk of 256: 4 chunks over 8 tiles
     assert (i.variant, i.split_k) == (t.VARIANT_STREAM, 4)
     i = _plan(16, 4096, 4096, "f16", variant=t.VARIANT_STREAM, tile=3, split_k=1).info
@@ -123,7 +124,7 @@ def test_gpt2_layer_shapes_m128(N, K):
         assert i.variant == t.VARIANT_TILED and i.split_k > 1
         tiles = -(-128 // i.tile_m) * -(-N // i.tile_n)
         assert tiles * i.split_k >= 256 or K // (i.tile_k * i.split_k) < 8
-        assert i.workspace_bytes == i.split_k * 128 * N * 4
+        assert i.workspace_bytes == 65536 + i.split_k * 128 * N * 4  # counter block (left alone), partials
     j = _plan(128, N, K, "f32", bias=True, gelu=(N == 3072)).info
     assert (j.variant == t.VARIANT_STREAM and j.workspace_bytes == 0) or j.split_k > 1
 
@@ -152,7 +153,7 @@ def test_forced_variants_and_errors():
     assert e.value.status == t.ERR_UNSUPPORTED
     p = _plan(100, 64, 64, "f32", variant=t.VARIANT_TILED, split_k=3, tile=2)
     i = p.info
-    assert (i.split_k, i.tile_m, i.launches, i.workspace_bytes) == (3, 64, 2, 3 * 100 * 64 * 4)
+    assert (i.split_k, i.tile_m, i.launches, i.workspace_bytes) == (3, 64, 2, 65536 + 3 * 100 * 64 * 4)
     with pytest.raises(t.TlgError) as e:
         _plan(100, 64, 64, "f32", variant=t.VARIANT_TILED, split_k=5)  # 4 slices of 16
     assert e.value.status == t.ERR_UNSUPPORTED
@@ -262,3 +263,15 @@ def test_bad_layout_and_flags_rejected():
     assert lib.gemm_plan(ctypes.byref(h), 8, 8, 8, 0, 0, 0, 8) == t.ERR_INVALID_ARG
     assert lib.gemm_plan(ctypes.byref(h), 8, 8, 8, 0, 0, 2, 4) == t.OK
     lib.gemm_destroy(h)
+
+
+def test_stream_split_counter_block_limit():
+    """Split stream plans keep one arrival counter per (row block, tile) in the workspace's fixed
+    64 KiB counter block; a forced split with more tiles than counters is refused, not overrun."""
+    i = _plan(16, 16384 * 16, 8192, "f16", variant=t.VARIANT_STREAM, tile=1, split_k=2).info  # 16384 tiles: fits
+    assert i.split_k == 2 and i.workspace_bytes == 65536 + 2 * 16384 * 16 * 16 * 4
+    with pytest.raises(t.TlgError) as e:
+        _plan(16, 16385 * 16, 8192, "f16", variant=t.VARIANT_STREAM, tile=1, split_k=2)
+    assert e.value.status == t.ERR_UNSUPPORTED and "counters" in str(e.value)
+    i = _plan(16, 16385 * 16, 8192, "f16", variant=t.VARIANT_STREAM, tile=1, split_k=1).info  # no split: no counters
+    assert i.workspace_bytes == 0

@@ -1,6 +1,6 @@
 """Captured launch sequences: the path recorded in a HIP graph and replayed.
 
-"Optimizing a GPT-2-class transformer on a GPU" (Act IV, the launch tax)
+"Optimizing a GPT-2-class transformer on a GPU" (Act III, the launch tax)
 records a layer's launches once and replays them.  The library launches only
 kernels on the caller's stream (no memsets; split-K tickets are reset by the
 kernels themselves), so a captured sequence replays unchanged.  Each replay

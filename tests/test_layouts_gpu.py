@@ -92,18 +92,11 @@ def test_zero_weight_residual_and_transposed_identity_bitwise(variant, tile, spl
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_weight_gradient_fc_shape(dtype):
     """dW = dYᵀ·X for the GPT-2 fc layer at 8192 tokens ([3072][8192]ᵀ·[8192][768]), accumulated onto
-    a previous gradient; sampled outputs plus two full rows against the oracle."""
+    a previous gradient; every output against the oracle."""
     M, N, K = 3072, 768, 8192
     dY = inputs.normal(81, (K, M), 1.0, dtype)   # stored [tokens][out]
     X = inputs.normal(82, (K, N), 1.0, dtype)    # stored [tokens][in]
     G = inputs.normal(83, (M, N), 1.0, dtype)    # previous gradient (residual)
     c = inputs.LinearCase("dW_fc", M, N, K, dtype, dtype, "AT_KN", False, False, dY, X, None, G)
-    Y, desc = run_case(c)
+    _, desc = _check(c)
     assert "variant=tiled" in desc
-    y = to_f64(Y)
-    rng = np.random.default_rng(0)
-    mi = np.concatenate([rng.integers(0, M, 2000), np.repeat([0, M - 1], N)])
-    ni = np.concatenate([rng.integers(0, N, 2000), np.tile(np.arange(N), 2)])
-    ref = oracle.linear_points(dY, X, None, dtype=dtype, layout="AT_KN", mi=mi, ni=ni, residual=G, out_dtype=dtype)
-    err = np.max(np.abs(y[mi, ni] - ref)) / np.max(np.abs(ref))
-    assert err <= TOL[dtype], f"{desc}: err {err:.3e}"

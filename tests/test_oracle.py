@@ -254,3 +254,77 @@ def test_gelu_applied_after_bias(oracle_lib):
     b = _store([1.5], "f32")
     out = oracle_lib.linear(X, W, b, gelu=True)
     assert out[0, 0] == oracle_lib.gelu_tanh(1.5)
+
+
+# --- the pass/fail measure: max|y - ref| / max|ref| ----------------------------------------
+# "Writing a CUDA matmul that catches cuBLAS", section "The measurement was nearly
+# wrong": the error is the largest absolute deviation over the output, divided by the
+# largest magnitude of the reference.  Hand-worked values, each chosen so that one
+# plausible slip (a dropped abs, a denominator over the result, a signed maximum,
+# broadcasting) gives a different number.
+
+def test_error_measure_exact_match_is_zero(oracle_lib):
+    ref = np.array([[1.0, -4.0], [2.0, 3.0]])
+    assert oracle_lib.normalized_error(ref.copy(), ref) == 0.0
+
+
+def test_error_measure_hand_values(oracle_lib):
+    ref = np.array([[1.0, -4.0], [2.0, 3.0]])
+    # one element 0.5 too low: |err| = 0.5, max|ref| = 4 (from the negative entry) -> 0.125;
+    # a signed max of ref would give 0.5 / 3, a signed max of (y - ref) would give 0.
+    y = ref.copy()
+    y[1, 0] -= 0.5
+    assert oracle_lib.normalized_error(y, ref) == 0.125
+    # the worst of several deviations counts: 0.25 and -1.0 -> 1.0 / 4
+    y = ref.copy()
+    y[0, 0] += 0.25
+    y[1, 1] -= 1.0
+    assert oracle_lib.normalized_error(y, ref) == 0.25
+    # the denominator is the reference's, not the result's: a result entry of 10 where
+    # the reference holds 2 gives 8 / 4 = 2 (over the result it would be 8 / 10)
+    y = ref.copy()
+    y[1, 0] = 10.0
+    assert oracle_lib.normalized_error(y, ref) == 2.0
+
+
+def test_error_measure_is_relative_to_the_whole_output(oracle_lib):
+    # a deviation of 1e-3 on an entry of size 1e-3 is small against max|ref| = 1000
+    ref = np.array([1e-3, 1000.0])
+    y = np.array([2e-3, 1000.0])
+    assert oracle_lib.normalized_error(y, ref) == pytest.approx(1e-6, rel=1e-12)
+
+
+def test_error_measure_zero_reference_and_empty(oracle_lib):
+    z = np.zeros((3, 3))
+    assert oracle_lib.normalized_error(z, z) == 0.0
+    y = z.copy()
+    y[2, 1] = -1e-30
+    assert oracle_lib.normalized_error(y, z) == float("inf")
+    assert oracle_lib.normalized_error(np.zeros((0, 4)), np.zeros((0, 4))) == 0.0
+
+
+def test_error_measure_nan_fails_every_tolerance(oracle_lib):
+    ref = np.array([1.0, 2.0, 3.0])
+    y = ref.copy()
+    y[1] = np.nan
+    err = oracle_lib.normalized_error(y, ref)
+    assert not err <= 1e-2 and not err <= 1e30
+
+
+def test_error_measure_rejects_shape_mismatch(oracle_lib):
+    ref = np.ones((4, 3))
+    with pytest.raises(ValueError):
+        oracle_lib.normalized_error(np.ones(3), ref)  # would broadcast over the rows
+    with pytest.raises(ValueError):
+        oracle_lib.normalized_error(np.ones((3, 4)), ref)
+
+
+def test_error_measure_is_the_one_the_gpu_tests_use():
+    """The GPU test helpers take the measure from the oracle package instead of keeping a copy."""
+    import ast
+
+    src = open(os.path.join(os.path.dirname(__file__), "gpu_helpers.py")).read()
+    tree = ast.parse(src)
+    assert not any(isinstance(n, ast.FunctionDef) and n.name == "normalized_error" for n in ast.walk(tree))
+    assert any(isinstance(n, ast.ImportFrom) and n.module == "oracle" and
+               any(a.name == "normalized_error" for a in n.names) for n in ast.walk(tree))

@@ -151,36 +151,17 @@ def test_gpt2_layer_m128(dtype):
         _check(c)
 
 
-def _sampled(case, npts=3000, rows=8, seed=0, **force):
-    Y, desc = run_case(case, **force)
-    y = to_f64(Y)
-    rng = np.random.default_rng(seed)
-    mi = rng.integers(0, case.M, npts)
-    ni = rng.integers(0, case.N, npts)
-    # whole first and last rows as well
-    mi = np.concatenate([mi, np.repeat([0, case.M - 1], case.N)])
-    ni = np.concatenate([ni, np.tile(np.arange(case.N), 2)])
-    ref = oracle.linear_points(case.X, case.W, case.b, dtype=case.in_dtype, layout=case.layout, gelu=case.gelu,
-                               mi=mi, ni=ni)
-    err = np.max(np.abs(y[mi, ni] - ref)) / np.max(np.abs(ref))
-    assert err <= TOL[case.in_dtype], f"{desc}: err {err:.3e}"
-    assert np.all(np.isfinite(y))
-    return y, desc
-
-
 def test_tiled_persistent():
     """Persistent workgroups (tile option 10, 128x128x64): a workgroup per resident slot loops over tiles, loading
-    the next tile's first slices while the current one finishes.  1024 or 512 tiles: several per workgroup."""
+    the next tile's first slices while the current one finishes.  1024 or 512 tiles: several per workgroup.
+    Every output is compared, so a tile the loop skips or stores twice cannot go unseen."""
     for (M, N, K), pair, layout, epi, res in [((4096, 4096, 256), ("bf16", "bf16"), "NK", (True, True), False),
                                               ((4096, 2048, 512), ("f16", "f32"), "NK", (True, False), False),
                                               ((2048, 4096, 128), ("bf16", "f32"), "KN", (False, False), False),
                                               ((4096, 4096, 128), ("bf16", "bf16"), "NK", (True, False), True)]:
         c = inputs.random_case(17, M, N, K, pair[0], pair[1], layout, bias=epi[0], gelu=epi[1], residual=res)
         for tile in (10, 11):  # staged; direct loads where the operands allow them
-            if res:  # the sampled check below compares against the oracle with the residual added
-                _, desc = _check(c, variant=tlgemm.VARIANT_TILED, tile=tile)
-            else:
-                _, desc = _sampled(c, npts=2000, variant=tlgemm.VARIANT_TILED, tile=tile)
+            _, desc = _check(c, variant=tlgemm.VARIANT_TILED, tile=tile)
             assert "persistent" in desc, desc
             assert ("load=direct" in desc) == (tile == 11 and layout == "NK"), desc
 
@@ -189,7 +170,7 @@ def test_tiled_persistent_f32():
     """fp32 persistent entries (options 7 and 8: 128x128x16 capped at two per CU, 64x64x16)."""
     for tile, (M, N, K) in [(7, (4096, 4096, 64)), (8, (2048, 2048, 96))]:
         c = inputs.random_case(20, M, N, K, "f32", "f32", "KN" if tile == 7 else "NK", bias=tile == 8, gelu=tile == 8)
-        _, desc = _sampled(c, npts=2000, variant=tlgemm.VARIANT_TILED, tile=tile)
+        _, desc = _check(c, variant=tlgemm.VARIANT_TILED, tile=tile)
         assert "persistent" in desc, desc
 
 
@@ -206,15 +187,18 @@ def test_tiled_persistent_small_and_fallbacks():
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_square_4096(dtype):
+    """All 16.7 M outputs of the square workload against the oracle (the plan the bench times)."""
     c = inputs.workload_square(dtype=dtype)
-    _, desc = _sampled(c)
+    _, desc = _check(c)
     assert "variant=tiled" in desc
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_gpt2_stack_m8192_first_layer(dtype):
-    for c in inputs.workload_gpt2_stack(layers=1, dtype=dtype):
-        _sampled(c, npts=2000)
+@pytest.mark.parametrize("which", range(4), ids=["qkv", "attn_out", "fc", "proj"])
+def test_gpt2_stack_m8192_first_layer(dtype, which):
+    """Every output of each linear of the stack's first layer (8192 rows) against the oracle."""
+    c = inputs.workload_gpt2_stack(layers=1, dtype=dtype)[which]
+    _check(c)
 
 
 # --- exact properties ------------------------------------------------------------------
@@ -279,6 +263,28 @@ def test_stream_argument_and_workspace_reuse():
     s.synchronize()
     for c, y in zip(cases, outs):
         assert normalized_error(to_f64(y), oracle.linear_case(c)) <= 1e-5
+
+
+def test_workspace_shared_between_plan_kinds():
+    """One workspace, zeroed once, serves a tiled split plan (fp32 partials), then a split stream plan
+    (arrival counters), then the tiled plan again: the partials never land on the counters."""
+    tiled_case = inputs.random_case(21, 128, 768, 3072, "f32", bias=True)
+    stream_case = inputs.random_case(22, 16, 768, 3072, "f16", bias=True, gelu=True)
+    tiled = tlgemm.Plan.create(128, 768, 3072, "f32", bias=True, variant=tlgemm.VARIANT_TILED, split_k=8, tile=2)
+    stream = tlgemm.Plan.create(16, 768, 3072, "f16", bias=True, gelu=True, variant=tlgemm.VARIANT_STREAM,
+                                tile=3, split_k=6)
+    try:
+        assert "split=8" in tiled.describe() and "split=6" in stream.describe()
+        ws = torch.zeros(max(tiled.workspace_size, stream.workspace_size), dtype=torch.uint8, device="cuda:0")
+        for c, p in [(tiled_case, tiled), (stream_case, stream), (tiled_case, tiled), (stream_case, stream)]:
+            X, W, b = device_case(c)
+            Y = tlgemm.run(p, X, W, b, workspace=ws)
+            torch.cuda.synchronize()
+            assert normalized_error(to_f64(Y), oracle.linear_case(c)) <= TOL[c.in_dtype], p.describe()
+        assert not torch.any(ws[:65536]), "a completed run left a counter set"
+    finally:
+        tiled.close()
+        stream.close()
 
 
 def test_subnormal_fp16_inputs_not_flushed():
