@@ -230,6 +230,85 @@ __global__ __launch_bounds__(64 * NB * KW) void stream_kernel(const void* __rest
     }
 }
 
+// Narrow 16-bit layers (M <= 16, K a multiple of 512 up to 4096): the 16
+// weight rows of a tile live in LDS for the whole K range.  Timed on the
+// 16×4096×4096 layer with cold weights, this beats streaming the weight into
+// registers by 0.3-0.8 µs of ~9 (probe kernels, rocprofv3 medians on several
+// boxes), for two reasons:
+//  * each direct load (global_load_lds) reads one contiguous KiB of a weight
+//    row, where an MFMA-operand load spreads 64 bytes over each of 16 rows;
+//    the weight is never in registers, so it needs no staging;
+//  * X goes straight to registers in the MFMA operand layout, each wave its
+//    own K range, X and weight loads interleaved: X needs no LDS store and no
+//    barrier of its own, and never waits behind the whole weight stream.
+// Wave w fetches weight rows 2w and 2w+1; instruction (row R, KiB h) lands
+// at LDS row R, bytes [1 KiB·h, 1 KiB·(h+1)), lane l at 16·l.  The lanes
+// fetch the 16-byte chunks of that KiB permuted, chunk c at c ^ (R % 16), so
+// the operand reads of 16 rows at one k hit 16 distinct 4-bank groups.  Wave
+// w then multiplies K range [w·K/8, (w+1)·K/8) and the 8 partials are summed
+// through LDS in wave order, as in the register-streaming kernel.
+// PR: KiB-instructions per weight row (K = 512·PR); a wave issues 2·PR
+// direct loads and 2·PR X loads and runs 2·PR MFMA steps of 32 k, all
+// unrolled with no condition, so every load is issued before the first wait.
+template <int IN, int OUT, uint32_t EPI, int PR>
+__global__ __launch_bounds__(512) void stream_dl_kernel(const void* __restrict__ Xv, const void* __restrict__ Wv,
+                                                       const void* __restrict__ bias, void* __restrict__ Y, int M,
+                                                       int N, int resid) {
+    static_assert(IN != TLG_F32 && PR >= 1 && PR * kStreamDlKStep <= kStreamDlMaxK, "16-bit operands, K in LDS");
+    using S = uint16_t;
+    constexpr int KW = 8, K = PR * kStreamDlKStep, STEPS = 2 * PR, KPW = K / KW;
+    __shared__ __attribute__((aligned(16))) S wl[16 * K];
+    __shared__ float red[KW * 4 * 64];
+    const S* __restrict__ X = static_cast<const S*>(Xv);
+    const S* __restrict__ W = static_cast<const S*>(Wv);
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int r = lane & 15, g = lane >> 4;
+    const int n0 = blockIdx.x * 16;
+    const S* xrow = X + (int64_t)min(r, M - 1) * K + w * KPW + 8 * g;  // rows past M repeat row M-1, never stored
+    u32x4 xr[STEPS];
+#pragma unroll
+    for (int j = 0; j < STEPS; ++j) {
+        xr[j] = ldg16(xrow + 32 * j);
+        const int R = 2 * w + j / PR, h = j % PR;
+        const int c = ((h << 6) + lane) ^ (R & 15);
+        const S* src = W + (int64_t)min(n0 + R, N - 1) * K + 8 * c;  // rows past N repeat row N-1, never stored
+        __builtin_amdgcn_global_load_lds((const void*)src,
+                                         (__attribute__((address_space(3))) void*)(wl + R * K + h * 512), 16, 0,
+                                         2 /* nt: streamed once */);
+    }
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): this wave's X and direct loads have landed
+    __syncthreads();                                   // and every other wave's weight rows
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < STEPS; ++j) {
+        const int c = (w * KPW + 32 * j) / 8 + g;  // 16-byte chunk of weight row r
+        const u32x4 wv = *reinterpret_cast<const u32x4*>(wl + r * K + 8 * (c ^ r));
+        acc = mfma16_16bit<IN>(xr[j], wv, acc);
+    }
+    // wave partials summed in wave order; a 16×16 accumulator holds column
+    // (lane % 16) and rows 4·(lane / 16) + e
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[(w * 4 + e) * 64 + lane] = acc[e];
+    __syncthreads();
+    if (w != 0) return;
+    const int n = n0 + r;
+    float b = 0.0f;
+    if constexpr ((EPI & TLG_EPI_BIAS) != 0)
+        if (n < N) b = load_elem<IN>(bias, n);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        float sum = red[e * 64 + lane];
+#pragma unroll
+        for (int q = 1; q < KW; ++q) sum += red[(q * 4 + e) * 64 + lane];
+        const int m = 4 * g + e;
+        if (m < M && n < N) {
+            float v = epilogue<EPI>(sum, b);
+            if (resid) v += load_elem<OUT>(Y, (int64_t)m * N + n);
+            store_out<OUT>(Y, (int64_t)m * N + n, v);
+        }
+    }
+}
+
 template <int I, int NB, int KW, int LOADS>
 static int launch_stream_cfg(const tlg_plan& p, const void* X, const void* W, const void* bias, void* Y, void* ws,
                              hipStream_t stream) {
@@ -274,12 +353,54 @@ static int launch_stream_cfg(const tlg_plan& p, const void* X, const void* W, co
     });
 }
 
+template <int I>
+static int launch_stream_dl(const tlg_plan& p, const void* X, const void* W, const void* bias, void* Y,
+                            hipStream_t stream) {
+    if constexpr (I == TLG_F32) {
+        set_error("the direct-load stream tile takes 16-bit inputs");
+        return (int)TLG_ERR_UNSUPPORTED;
+    } else {
+        // the planner's conditions, checked again before the launch
+        if (p.M > 16 || p.K % kStreamDlKStep != 0 || p.K > kStreamDlMaxK || p.split != 1 || p.grid_z != 1) {
+            set_error("direct-load stream tile: shape outside its limits");
+            return (int)TLG_ERR_INVALID_ARG;
+        }
+        auto with_out = [&](auto f) {
+            if (p.out_dt == TLG_F32) return f(ic<TLG_F32>{});
+            return f(ic<I>{});
+        };
+        return with_out([&](auto out) {
+            return with_epi(p.epi, [&](auto epi) {
+                constexpr int O = decltype(out)::value;
+                constexpr uint32_t E = (uint32_t)decltype(epi)::value;
+                const int resid = (p.epi & TLG_EPI_RESIDUAL) != 0;
+                auto go = [&](auto pr) {
+                    hipLaunchKernelGGL((stream_dl_kernel<I, O, E, decltype(pr)::value>), dim3((unsigned)p.grid_x),
+                                       dim3(512), 0, stream, X, W, bias, Y, (int)p.M, (int)p.N, resid);
+                    return check_launch("stream_dl_kernel");
+                };
+                static_assert(kStreamDlMaxK == 8 * kStreamDlKStep, "one instantiation per K");
+                switch (p.K / kStreamDlKStep) {
+                case 1: return go(ic<1>{});
+                case 2: return go(ic<2>{});
+                case 3: return go(ic<3>{});
+                case 4: return go(ic<4>{});
+                case 5: return go(ic<5>{});
+                case 6: return go(ic<6>{});
+                case 7: return go(ic<7>{});
+                default: return go(ic<8>{});
+                }
+            });
+        });
+    }
+}
+
 // All stream launches for one input dtype; explicitly instantiated once per
 // dtype in its own translation unit.
 template <int I>
 int launch_stream_in(const tlg_plan& p, const void* X, const void* W, const void* bias, void* Y, void* ws,
                      hipStream_t stream) {
-    static_assert(kNumStream == 5, "stream configurations changed");
+    static_assert(kNumStream == 6 && kStream[5].dl, "stream configurations changed");
 #define TLG_STREAM_CASE(i) \
     case i: return launch_stream_cfg<I, kStream[i].nb, kStream[i].kw, kStream[i].loads>(p, X, W, bias, Y, ws, stream);
     switch (p.tile) {
@@ -288,6 +409,7 @@ int launch_stream_in(const tlg_plan& p, const void* X, const void* W, const void
         TLG_STREAM_CASE(2)
         TLG_STREAM_CASE(3)
         TLG_STREAM_CASE(4)
+    case 5: return launch_stream_dl<I>(p, X, W, bias, Y, stream);
     default: set_error("bad stream tile"); return (int)TLG_ERR_INVALID_ARG;
     }
 #undef TLG_STREAM_CASE

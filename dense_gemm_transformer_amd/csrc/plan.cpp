@@ -116,6 +116,11 @@ static int fill_stream(tlg_plan& p, int tile, int split) {
         return TLG_ERR_INVALID_ARG;
     }
     const StreamCfg& c = kStream[tile];
+    if (c.dl && (p.in_dt == TLG_F32 || p.M > 16 || p.K % kStreamDlKStep != 0 || p.K > kStreamDlMaxK || split > 1)) {
+        set_error("stream configuration %d needs 16-bit inputs, M <= 16, K a multiple of %d up to %d and no split",
+                  tile, kStreamDlKStep, kStreamDlMaxK);
+        return TLG_ERR_UNSUPPORTED;
+    }
     const int rowb = stream_rowb(p.M);
     if (stream_lds_bytes(c, p.in_dt, rowb) > kLdsBytes) {
         set_error("stream configuration %d does not fit in LDS for M=%lld", tile, (long long)p.M);
@@ -143,7 +148,7 @@ static int fill_stream(tlg_plan& p, int tile, int split) {
     p.rowb = rowb;
     p.bm = 16 * rowb;
     p.bn = (int)bn;
-    p.bk = (int)wck;
+    p.bk = c.dl ? (int)p.K : (int)wck;
     p.threads = 64 * c.nb * c.kw;
     p.grid_x = tiles;
     p.grid_y = S;
@@ -166,6 +171,8 @@ static int fill_stream(tlg_plan& p, int tile, int split) {
 static int auto_stream(tlg_plan& p) {
     const int rowb = stream_rowb(p.M);
     if (ceil_div(p.N, 16) * ceil_div(p.M, 16 * rowb) >= kNumCUs / 2) {
+        if (p.in_dt != TLG_F32 && p.M <= 16 && p.K % kStreamDlKStep == 0 && p.K <= kStreamDlMaxK)
+            return fill_stream(p, 5, 1);
         for (int cfg : {0, 1, 4})
             if (stream_lds_bytes(kStream[cfg], p.in_dt, rowb) <= kLdsBytes) return fill_stream(p, cfg, 1);
     }
@@ -396,7 +403,10 @@ int gemm_plan_describe(tlg_plan_t p, char* buf, size_t n) {
                        (p->epi & TLG_EPI_BIAS) ? "bias" : "none", (p->epi & TLG_EPI_GELU_TANH) ? "+gelu" : "",
                        (p->epi & TLG_EPI_RESIDUAL) ? "+res" : "", p->bm, p->bn, p->bk, p->split,
                        p->threads, (long long)p->grid_x, (long long)p->grid_y, (long long)p->grid_z,
-                       p->launches, p->ws_bytes, p->variant == TLG_VARIANT_TILED && p->stages ? " load=direct" : "",
+                       p->launches, p->ws_bytes,
+                       (p->variant == TLG_VARIANT_TILED && p->stages) || (p->variant == TLG_VARIANT_STREAM && kStream[p->tile].dl)
+                           ? " load=direct"
+                           : "",
                        p->variant == TLG_VARIANT_TILED && p->persist ? " persistent" : "");
     if (buf && n) {
         size_t c = (size_t)len < n - 1 ? (size_t)len : n - 1;

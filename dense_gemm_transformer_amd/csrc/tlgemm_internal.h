@@ -79,9 +79,10 @@ constexpr int kNumTiled16 = sizeof(kTiled16) / sizeof(kTiled16[0]);
 // again.  Each wave keeps `loads` 16-byte weight loads per lane in flight per
 // chunk (a chunk is loads·32 fp16/bf16 or loads·16 fp32 elements of K).
 struct StreamCfg {
-    int nb;     // 16-row column blocks per workgroup
-    int kw;     // waves splitting the workgroup's K range
-    int loads;  // 16-byte loads per lane per chunk
+    int nb;      // 16-row column blocks per workgroup
+    int kw;      // waves splitting the workgroup's K range
+    int loads;   // 16-byte loads per lane per chunk
+    int dl = 0;  // the weight tile goes to LDS by direct loads, X to registers (16-bit, M <= 16, no split)
 };
 constexpr StreamCfg kStream[] = {
     {1, 8, 16},  // 0: 16-row tiles over all of K by 8 waves; no inter-workgroup traffic (M <= 16)
@@ -89,7 +90,10 @@ constexpr StreamCfg kStream[] = {
     {8, 1, 16},  // 2: 128-row tiles, K split across workgroups
     {4, 1, 32},  // 3: 64-row tiles, 1024-wide fp16 chunks, K split across workgroups
     {2, 4, 4},   // 4: 32-row tiles, 4-way in-workgroup split
+    {1, 8, 16, 1},  // 5: 16-row tiles, all of the tile's weight rows in LDS (K a multiple of 512, at most 4096)
 };
+// Direct-load stream tile: 16 weight rows of K 16-bit elements resident in LDS.
+constexpr int kStreamDlMaxK = 4096, kStreamDlKStep = 512;
 constexpr int kNumStream = sizeof(kStream) / sizeof(kStream[0]);
 constexpr int kStreamMaxM = 64;      // rows of X one stream workgroup covers (4 blocks of 16)
 constexpr int kStreamMaxRows = 256;  // beyond this the tiled kernel always wins (W re-read per row block)
@@ -99,6 +103,7 @@ constexpr int kLdsBytes = 160 * 1024;
 // LDS of one stream workgroup: the X chunk (16·rowb rows, padded by 16
 // bytes) plus the in-workgroup reduction buffer.  rowb is 1, 2 or 4.
 inline int64_t stream_lds_bytes(const StreamCfg& c, int in_dt, int rowb) {
+    if (c.dl) return 16 * kStreamDlMaxK * 2 + 8 * 4 * 64 * 4;  // weight rows, wave partials
     const int64_t esize = in_dt == 0 ? 4 : 2, epv = 16 / esize;
     const int64_t wck = (int64_t)c.kw * c.loads * 4 * epv;
     const int64_t x = 16 * rowb * (wck + epv) * esize;

@@ -275,3 +275,20 @@ def test_stream_split_counter_block_limit():
     assert e.value.status == t.ERR_UNSUPPORTED and "counters" in str(e.value)
     i = _plan(16, 16385 * 16, 8192, "f16", variant=t.VARIANT_STREAM, tile=1, split_k=1).info  # no split: no counters
     assert i.workspace_bytes == 0
+
+
+def test_stream_weight_rows_in_lds_planning():
+    """The LDS-resident stream tile (option 6): 16-bit, M <= 16, K a multiple of 512 up to 4096, no split;
+    the planner takes it for such narrow layers with enough 16-row tiles to fill the chip."""
+    i = _plan(16, 4096, 2048, "bf16").info
+    assert (i.variant, i.tile_n, i.tile_k, i.split_k, i.workgroups, i.threads) == (t.VARIANT_STREAM, 16, 2048, 1, 256, 512)
+    assert "tile=16x16x2048 " in _plan(16, 4096, 2048, "bf16").describe()
+    assert _plan(16, 4096, 2048, "bf16").describe().endswith(" load=direct")
+    assert "load=direct" not in _plan(16, 4096, 2048, "bf16", variant=t.VARIANT_STREAM, tile=1).describe()
+    for args in [(16, 64, 512, "f32"), (17, 64, 512, "f16"), (16, 64, 520, "f16"), (16, 64, 4608, "bf16")]:
+        with pytest.raises(t.TlgError) as e:
+            _plan(*args, variant=t.VARIANT_STREAM, tile=6)
+        assert e.value.status == t.ERR_UNSUPPORTED
+    with pytest.raises(t.TlgError):
+        _plan(16, 64, 1024, "f16", variant=t.VARIANT_STREAM, tile=6, split_k=2)
+    assert _plan(16, 4096, 4608, "f16").info.tile_k != 4608  # too long for LDS: the register-streaming tile

@@ -67,6 +67,29 @@ def test_stream(pair, epi, tile):
     assert ran >= 2
 
 
+@pytest.mark.parametrize("pair", PAIRS[1:], ids=lambda p: f"{p[0]}->{p[1]}")
+@pytest.mark.parametrize("epi", EPIS, ids=["none", "bias", "gelu", "bias+gelu"])
+def test_stream_weight_rows_in_lds(pair, epi):
+    """Stream option 6: the 16 weight rows of a tile in LDS by direct loads, X in registers (M <= 16,
+    K a multiple of 512 up to 4096), ragged N and M, with and without the residual."""
+    for (M, N, K), res in [((1, 16, 512), False), ((16, 48, 512), True), ((5, 50, 1024), False),
+                           ((16, 4096, 4096), False), ((13, 100, 3584), True), ((16, 264, 2048), False)]:
+        c = inputs.random_case(23, M, N, K, pair[0], pair[1], "NK", bias=epi[0], gelu=epi[1], residual=res)
+        _, desc = _check(c, variant=tlgemm.VARIANT_STREAM, tile=6)
+        assert "variant=stream" in desc and f"tile=16x16x{K} " in desc, desc
+
+
+def test_stream_weight_rows_in_lds_limits():
+    """Shapes outside the LDS-resident tile are refused, not run."""
+    for args in [(16, 64, 512, "f32"), (17, 64, 512, "f16"), (16, 64, 520, "f16"), (16, 64, 4608, "bf16")]:
+        with pytest.raises(tlgemm.TlgError) as e:
+            tlgemm.Plan.create(*args, variant=tlgemm.VARIANT_STREAM, tile=6)
+        assert e.value.status == tlgemm.ERR_UNSUPPORTED
+    with pytest.raises(tlgemm.TlgError) as e:
+        tlgemm.Plan.create(16, 64, 1024, "f16", variant=tlgemm.VARIANT_STREAM, tile=6, split_k=2)
+    assert e.value.status == tlgemm.ERR_UNSUPPORTED
+
+
 @pytest.mark.parametrize("pair", [("f32", "f32"), ("f16", "f16"), ("bf16", "f32")], ids=lambda p: f"{p[0]}->{p[1]}")
 @pytest.mark.parametrize("split", [1, 2, 3, 7])
 def test_stream_forced_split(pair, split):
