@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 
 #include "kernels/common.h"
 #include "tlgemm_internal.h"
@@ -50,6 +51,69 @@ static bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 }  // namespace tlg
 
 using namespace tlg;
+
+// ---- the library's own scratch, for callers that cannot allocate ----------------------
+// One array per device the library runs on, held until the process ends.  Host
+// code never uses its name as an address: the name is a host-side stand-in; the
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The counter block must start at zero; completed runs leave it zero.  A
+// kernel, not a memset, so the first call may sit inside a captured graph.
+__global__ __launch_bounds__(256) void zero_counters_kernel(u32x4* __restrict__ p, int n) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+}  // namespace
+
+// Device address of this device's scratch; its counter block is cleared
+// (on `stream`) the first time a device is seen.
+static int scratch_for_device(void** out, hipStream_t stream) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        set_error("gemm_run_no_alloc: no current device below %d", kMaxDevices);
+        return TLG_ERR_LAUNCH;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) {
+            set_error("gemm_run_no_alloc: hipGetSymbolAddress failed on device %d: %s", dev, hipGetErrorString(e));
+            return TLG_ERR_LAUNCH;
+        }
+        constexpr int n = (int)(kWsCounterBytes / 16);
+        hipLaunchKernelGGL(zero_counters_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, static_cast<u32x4*>(ptr),
+                           n);
+        const int rc = check_launch("zero_counters_kernel");
+        if (rc != TLG_OK) return rc;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return TLG_OK;
+}
+
+extern "C" int gemm_run_no_alloc(tlg_plan_t p, const void* X, const void* W, const void* bias, void* Y, void* stream) {
+    if (!p) {
+        set_error("gemm_run_no_alloc: NULL plan");
+        return TLG_ERR_INVALID_ARG;
+    }
+    if (p->ws_bytes > kScratchBytes) {
+        set_error("gemm_run_no_alloc: the plan needs %zu bytes of scratch, the library holds %zu per device",
+                  p->ws_bytes, (size_t)kScratchBytes);
+        return TLG_ERR_WORKSPACE;
+    }
+    void* ws = nullptr;
+    if (p->ws_bytes) {
+        const int rc = scratch_for_device(&ws, static_cast<hipStream_t>(stream));
+        if (rc != TLG_OK) return rc;
+    }
+    return gemm_run(p, X, W, bias, Y, ws, p->ws_bytes, stream);
+}
 
 extern "C" int gemm_run(tlg_plan_t p, const void* X, const void* W, const void* bias, void* Y,
                         void* workspace, size_t ws_bytes, void* stream) {

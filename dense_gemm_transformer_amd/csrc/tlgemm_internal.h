@@ -146,4 +146,8 @@ int launch_plan(const tlg_plan& p, const void* X, const void* W, const void* bia
 // sequence of plans.
 constexpr size_t kWsCounterBytes = 64 * 1024;
 constexpr int64_t kWsMaxTickets = (int64_t)(kWsCounterBytes / 4);
+// The library-held scratch of gemm_run_no_alloc (per device), laid out as a
+// workspace: counter block, then partials.
+constexpr size_t kScratchBytes = 32u << 20;
+constexpr int kMaxDevices = 64;
 }  // namespace tlg

@@ -36,7 +36,7 @@ DTYPE_CODES = {"f32": F32, "f16": F16, "bf16": BF16}
 LAYOUT_CODES = {"NK": NK, "KN": KN, "AT_NK": AT_NK, "AT_KN": AT_KN}
 
 # Every symbol include/tlgemm.h declares.
-EXPORTS = ("gemm_plan", "gemm_plan_ex", "gemm_workspace_size", "gemm_plan_info", "gemm_run",
+EXPORTS = ("gemm_plan", "gemm_plan_ex", "gemm_workspace_size", "gemm_plan_info", "gemm_run", "gemm_run_no_alloc",
            "gemm_destroy", "gemm_plan_describe", "gemm_status_string", "gemm_last_error")
 
 
@@ -75,6 +75,8 @@ def _load() -> ctypes.CDLL:
     lib.gemm_plan_info.restype = ci
     lib.gemm_run.argtypes = [vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gemm_run.restype = ci
+    lib.gemm_run_no_alloc.argtypes = [vp, vp, vp, vp, vp, vp]
+    lib.gemm_run_no_alloc.restype = ci
     lib.gemm_destroy.argtypes = [vp]
     lib.gemm_destroy.restype = ci
     lib.gemm_plan_describe.argtypes = [vp, ctypes.c_char_p, sz]
@@ -147,6 +149,11 @@ def gemm_plan_describe(handle) -> str:
     buf = ctypes.create_string_buffer(need + 1)
     _lib.gemm_plan_describe(handle, buf, need + 1)
     return buf.value.decode()
+
+
+def gemm_run_no_alloc(handle, X, W, bias, Y, stream=0) -> None:
+    """gemm_run with the library's own per-device scratch in place of a workspace."""
+    _check(_lib.gemm_run_no_alloc(handle, X, W, bias or None, Y, stream or None))
 
 
 def gemm_run(handle, X, W, bias, Y, workspace=0, ws_bytes=0, stream=0) -> None:

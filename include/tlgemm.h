@@ -150,6 +150,23 @@ int gemm_plan_info(tlg_plan_t p, tlg_plan_info* info);
 int gemm_run(tlg_plan_t p, const void* X, const void* W, const void* bias, void* Y,
              void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * gemm_run_no_alloc — gemm_run for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, checks and result as gemm_run, without the
+ * workspace: split plans use a scratch array the library keeps in device
+ * memory, 32 MiB per device, held from the first call on a device until the
+ * process ends.  A plan whose gemm_workspace_size exceeds 32 MiB is refused
+ * with TLG_ERR_WORKSPACE before any launch.  Nothing is allocated or freed:
+ * the first call on a device looks up that device's array and clears its
+ * counter block with a kernel on `stream`; every completed run leaves the
+ * counters zero again.  All calls on one device share its array, so calls
+ * that can overlap on one device (other streams, or work not yet finished on
+ * another stream) race and must be serialised by the caller; calls on one
+ * stream are ordered by the stream.
+ */
+int gemm_run_no_alloc(tlg_plan_t p, const void* X, const void* W, const void* bias, void* Y, void* stream);
+
 /* Free a plan.  NULL is a no-op. */
 int gemm_destroy(tlg_plan_t p);
 
