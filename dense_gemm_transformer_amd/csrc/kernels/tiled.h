@@ -446,12 +446,20 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) 
     constexpr int SV = HALF / NVM > 0 ? HALF / NVM : 1;
     constexpr int SR = MPK / FR > 0 ? MPK / FR : 1;
     constexpr int SW = HALF / NDW > 0 ? HALF / NDW : 1;
+    // 16-bit tiles whose last k-step has an MFMA for every LDS store keep the
+    // stores out of the earlier k-steps: LDS operations complete in order, so
+    // a fragment read issued after a store cannot be waited for without the
+    // store, and stores mixed into the k-steps that still read fragments
+    // stall their MFMAs.  (Square bf16 256×256×64: 2-3 % faster.)  Other
+    // tiles spread the stores over the second half of the MFMAs.
+    constexpr bool LATE_ST = !F32 && NDW <= MPK;
+    constexpr int ST0 = LATE_ST ? (NKQ - 1) * MPK : HALF, SW0 = LATE_ST ? MPK / NDW : SW;
     auto slot = [&](int m, bool loads, bool stores) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
         if (loads && m % SV == 0 && m / SV < NVM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         if (m / MPK < NKQ - 1 && (m % MPK) % SR == 0 && (m % MPK) / SR < FR)
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // next k-step's operand read
-        if (stores && m >= HALF && (m - HALF) % SW == 0 && (m - HALF) / SW < NDW)
+        if (stores && m >= ST0 && (m - ST0) % SW0 == 0 && (m - ST0) / SW0 < NDW)
             __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS stores: A's first, then the weight's
     };
     auto whole_phase = [&]() {

@@ -121,7 +121,7 @@ static int fill_stream(tlg_plan& p, int tile, int split) {
                   tile, kStreamDlKStep, kStreamDlMaxK);
         return TLG_ERR_UNSUPPORTED;
     }
-    const int rowb = stream_rowb(p.M);
+    const int rowb = c.rb ? c.rb : stream_rowb(p.M);
     if (stream_lds_bytes(c, p.in_dt, rowb) > kLdsBytes) {
         set_error("stream configuration %d does not fit in LDS for M=%lld", tile, (long long)p.M);
         return TLG_ERR_UNSUPPORTED;
