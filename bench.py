@@ -52,17 +52,18 @@ METRIC = "TFLOP/s (% MFMA peak) @4096³ fp32; µs + HBM GB/s @16×4096×4096 fp1
 
 # Bytes each kernel moved between L2 and memory per launch, from rocprofv3
 # FETCH_SIZE and WRITE_SIZE passes over `bench.py --steps 3 --warmup 1
-# --narrow-launches 32 --no-cpu-baseline --no-parity` (profiles/hbm_traffic_mi355x.md).
+# --narrow-launches 32 --no-cpu-baseline --no-parity --no-extra`, summarised
+# by `bench.py --pmc-summary` (the HBM-traffic profile under profiles/).
 # FETCH_SIZE is scaled by 1.998 and WRITE_SIZE by 1.0: the factors that make
-# the same counters read 32 MiB for a 32 MiB device-to-device copy.  Each
-# entry holds the hash of the kernel sources and the tile it was taken on;
+# the same counters read 32 MiB for the run's 32 MiB device-to-device copies.
+# Each entry holds the hash of the kernel sources and the tile it was taken on;
 # after a change to either the figure no longer applies and the bench reports null.
 FETCH_SCALE, WRITE_SCALE = 1.998, 1.0
 TRAFFIC = {
-    "tiled_f32": {"sources": ("common.h", "tiled.h"), "sha": "2cc92c535ee242f3",
-                  "tile": "256x256x16", "fetch_kib": 196688.1, "write_kib": 65536.0},
-    "stream_f16": {"sources": ("common.h", "stream.h"), "sha": "93e64e0b9b70f86b",
-                   "tile": "16x16x4096", "fetch_kib": 16929.5, "write_kib": 128.0},
+    "tiled_f32": {"sources": ("common.h", "tiled.h"), "sha": "681d253f3b2fd783",
+                  "tile": "256x256x16", "fetch_kib": 196687.0, "write_kib": 65536.0},
+    "stream_f16": {"sources": ("common.h", "stream.h"), "sha": "8ce0548efe2ee6ec",
+                   "tile": "16x16x4096", "fetch_kib": 16920.5, "write_kib": 128.0},
 }
 
 
@@ -664,7 +665,8 @@ def rocprof_summary(outdir: str, segments: list[str]) -> str:
 
     One row per (kernel, launch grid in workgroups): launches, median, p10,
     p90 and minimum duration, so that kernels of one template with different
-    tiles or grids are never pooled.  ``segments`` entries ``NAME@GRID=n1,n2,...``
+    tiles or grids are never pooled.  The library's kernels and the ceiling
+    probes only: torch's and the HIP runtime's own kernels are left out.  ``segments`` entries ``NAME@GRID=n1,n2,...``
     split that row's launches, in dispatch order, into consecutive runs of
     n1, n2, ... launches (for example the parity call, the cold launches and
     the warm launches of one kernel), each summarised on its own.
@@ -684,11 +686,19 @@ def rocprof_summary(outdir: str, segments: list[str]) -> str:
                 key = (row["Kernel_Name"], "x".join(map(str, grid)))
                 dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
                 groups.setdefault(key, []).append((int(row["Dispatch_Id"]), dur))
+    def short(name: str) -> str:  # the template arguments identify a kernel; drop its parameter list
+        return name[:name.rindex("(")] if name.endswith(")") and "(" in name else name
+
+    def ours(name: str) -> bool:  # the library's kernels and the ceiling probes, not torch's or the runtime's
+        return not (name.startswith("void at::") or name.startswith("at::") or name.startswith("__amd_rocclr"))
+
     lines = ["| kernel | grid (workgroups) | launches | median µs | p10 µs | p90 µs | min µs |",
              "|---|---|---|---|---|---|---|"]
     for (name, grid), v in sorted(groups.items(), key=lambda kv: -sum(d for _, d in kv[1])):
+        if not ours(name):
+            continue
         d = np.array([x for _, x in v])
-        lines.append(f"| `{name}` | {grid} | {len(d)} | {np.median(d):.2f} | {np.percentile(d, 10):.2f} | "
+        lines.append(f"| `{short(name)}` | {grid} | {len(d)} | {np.median(d):.2f} | {np.percentile(d, 10):.2f} | "
                      f"{np.percentile(d, 90):.2f} | {d.min():.2f} |")
     out = ["Per launch configuration (kernel begin to end, from the kernel trace):", "", *lines, ""]
     for spec in segments:
@@ -698,7 +708,7 @@ def rocprof_summary(outdir: str, segments: list[str]) -> str:
         sizes = [int(c) for c in counts.split(",")]
         if sum(sizes) != len(v):
             raise SystemExit(f"{name}@{grid}: {len(v)} launches in the trace, segments sum to {sum(sizes)}")
-        out += [f"`{name}` at grid {grid}, launches in dispatch order split into runs of {counts}:", "",
+        out += [f"`{short(name)}` at grid {grid}, launches in dispatch order split into runs of {counts}:", "",
                 "| run | launches | median µs | p10 µs | p90 µs |", "|---|---|---|---|---|"]
         i = 0
         for k, n in enumerate(sizes):
@@ -712,10 +722,59 @@ def rocprof_summary(outdir: str, segments: list[str]) -> str:
         out += [f"rocprofv3 `--stats` ({os.path.basename(path)}):", "",
                 "| kernel | calls | average µs | min µs | max µs |", "|---|---|---|---|---|"]
         for r in rows:
-            out.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+            if not ours(r["Name"]):
+                continue
+            out.append(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                        f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
         out.append("")
     return "\n".join(out)
+
+
+def pmc_summary(fetch_dir: str, write_dir: str, kernels: list[str]) -> str:
+    """Markdown table of HBM bytes per launch from two ``rocprofv3 --pmc`` runs (FETCH_SIZE, WRITE_SIZE).
+
+    Both counters read KiB per dispatch.  Each is scaled by the factor that
+    makes it read the true size of the runtime's device-to-device copies in
+    the same run (``__amd_rocclr_copyBuffer`` of one 32 MiB weight copy).
+    ``kernels`` entries ``NAME@GRID=ALGORITHMIC_BYTES`` name the rows to report.
+    """
+    import csv
+
+    def per_kernel(d: str, counter: str):
+        out: dict = {}
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path, newline="") as f:
+                for row in csv.DictReader(f):
+                    if row["Counter_Name"] != counter:
+                        continue
+                    wg = max(int(row["Workgroup_Size"]), 1)
+                    key = (row["Kernel_Name"], f"{int(row['Grid_Size']) // wg}x1x1")
+                    out.setdefault(key, []).append(float(row["Counter_Value"]))
+        return out
+
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    copy = [k for k in fetch if k[0].startswith("__amd_rocclr_copyBuffer") and k[1] == "256x1x1"]
+    if not copy:
+        raise SystemExit("no 32 MiB device copy in the FETCH_SIZE run to calibrate against")
+    kib = 32 * 1024.0
+    f_scale = kib / float(np.median(fetch[copy[0]]))
+    w_scale = kib / float(np.median(write[copy[0]]))
+    lines = [f"Calibration: the 32 MiB device copies read FETCH_SIZE {kib / f_scale:.1f} KiB and WRITE_SIZE "
+             f"{kib / w_scale:.1f} KiB, so FETCH_SIZE is scaled by {f_scale:.3f} and WRITE_SIZE by {w_scale:.3f}.", "",
+             "| kernel | grid | launches | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled bytes per launch | algorithmic bytes | ratio |",
+             "|---|---|---|---|---|---|---|---|"]
+    for spec in kernels:
+        key, alg = spec.rsplit("=", 1)
+        name, grid = key.rsplit("@", 1)
+        fk = [k for k in fetch if k[0].startswith(name) and k[1] == grid]
+        if len(fk) != 1:
+            raise SystemExit(f"{name}@{grid}: {len(fk)} matching kernels in the FETCH_SIZE run")
+        fv, wv = float(np.median(fetch[fk[0]])), float(np.median(write.get(fk[0], [0.0])))
+        tot = fv * 1024 * f_scale + wv * 1024 * w_scale
+        shown = fk[0][0][:fk[0][0].rindex("(")] if fk[0][0].endswith(")") else fk[0][0]
+        lines.append(f"| `{shown}` | {grid} | {len(fetch[fk[0]])} | {fv:.1f} | {wv:.1f} | {tot:.0f} | {alg} | "
+                     f"{tot / float(alg):.2f} |")
+    return "\n".join(lines)
 
 
 def main(argv=None) -> int:
@@ -732,8 +791,15 @@ def main(argv=None) -> int:
                     help="print a markdown summary of a rocprofv3 kernel-trace run under DIR and exit (no GPU)")
     ap.add_argument("--segment", action="append", default=[], metavar="NAME@GRID=n1,n2,...",
                     help="with --rocprof-summary: split one kernel's launches into consecutive runs")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print HBM bytes per launch from FETCH_SIZE / WRITE_SIZE rocprofv3 runs and exit (no GPU)")
+    ap.add_argument("--kernel", action="append", default=[], metavar="NAME@GRID=BYTES",
+                    help="with --pmc-summary: a kernel row to report, with its algorithmic bytes per launch")
     args = ap.parse_args(argv)
 
+    if args.pmc_summary:
+        print(pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.kernel))
+        return 0
     if args.rocprof_summary:
         print(rocprof_summary(args.rocprof_summary, args.segment))
         return 0
@@ -903,8 +969,9 @@ def main(argv=None) -> int:
                         "roofline": {"bound": "hbm", "achieved": round(n_gbs, 1), "peak": PEAK_HBM_GBS,
                                      "unit": "GB/s", "frac": round(n_gbs / PEAK_HBM_GBS, 4),
                                      "traffic": measured_traffic("stream_f16", tile_str(nplan)),
-                                     "kernel": f"stream_kernel fp16 {nplan.info.tile_m}x{nplan.info.tile_n}, "
-                                               f"{nplan.info.threads // 64} waves over K",
+                                     "kernel": f"stream kernel fp16 {nplan.info.tile_m}x{nplan.info.tile_n}, "
+                                               f"{nplan.info.threads // 64} waves over K"
+                                               + (", weight rows in LDS" if "load=direct" in nplan.describe() else ""),
                                      "algorithmic_bytes_per_launch": n_bytes},
                         "timing": "HIP events over back-to-back launches (includes launch gaps)",
                         "plan": nplan.describe()},
