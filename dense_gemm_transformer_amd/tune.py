@@ -87,7 +87,7 @@ def candidates(case, tlgemm):
     out = []
     opts = []
     if case.layout == "NK" and case.M <= 256:
-        for tile in range(1, 10):
+        for tile in range(1, 11):
             opts += [(tlgemm.VARIANT_STREAM, tile, 0), (tlgemm.VARIANT_STREAM, tile, 1)]
     for tile in range(1, 12):  # past the dtype's tile list the planner refuses, and the option is skipped
         for split in (1, 2, 4, 8):

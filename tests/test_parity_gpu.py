@@ -51,7 +51,7 @@ def test_generic(pair, layout, epi):
 
 @pytest.mark.parametrize("pair", PAIRS, ids=lambda p: f"{p[0]}->{p[1]}")
 @pytest.mark.parametrize("epi", EPIS, ids=["none", "bias", "gelu", "bias+gelu"])
-@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4, 5, 7, 8, 9])
+@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4, 5, 7, 8, 9, 10])
 def test_stream(pair, epi, tile):
     ran = 0
     for M, N, K in [(1, 16, 8), (16, 48, 512), (5, 50, 520), (17, 36, 1032), (40, 100, 264), (64, 16, 4096),
