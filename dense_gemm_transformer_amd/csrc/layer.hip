@@ -124,186 +124,188 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const void* __restrict__
 }
 
 // ---- fused causal attention ------------------------------------------------------------
-// One workgroup per (batch, head) with four waves; each wave takes 32 query
-// rows at a time.  The head's keys and values are converted to fp32 into LDS
-// once.  For each block of 32 keys up to the wave's last row (causality as a
-// loop bound):
-//  * S = Q Kᵀ with fp32 MFMA (Q in registers, pre-scaled by log2(e)/sqrt(64);
-//    16-byte key fragments from LDS) lands in the accumulator layout, where a
-//    lane holds one key column of 16 rows;
-//  * the wave passes S through its LDS tile into the operand layout, where a
-//    lane holds 16 keys of one row: masking, the row maximum (16 local
-//    maxima and one exchange between the two half-waves), the rescaling
-//    factor exp2(m_old - m_new), P = exp2(S - m_new) and the lane's partial
-//    row sum are all per-lane work, and P is already the A operand of P V;
-//  * the 32 rescaling factors return through the tile to the accumulator
-//    layout of the output, which is rescaled before O += P V.
+// One workgroup per (batch, head) with four waves.  The head's keys and
+// values go to LDS once (values transposed, [dimension][key]).  Queries come
+// in blocks of 16 rows; with causality block q needs q + 1 key blocks of 16,
+// so wave w takes blocks w and 7 - w of every group of eight: 9 key blocks
+// per wave at T = 128, the same on every wave (and on every SIMD).  For each
+// key block up to the query block (causality as a loop bound):
+//  * S = Q Kᵀ on v_mfma_f32_16x16x4_f32: lane group kk holds dimensions
+//    16kk .. 16kk+15 of its query row (in registers, pre-scaled by
+//    log2(e)/sqrt(64)) and of its key row (four 16-byte LDS reads); the same
+//    permutation of the dimensions on both sides leaves each dot product
+//    unchanged.  Two accumulators take alternate steps, summed at the end;
+//  * S passes through the wave's 16×16 LDS tile into the A-operand layout of
+//    P V, where lane (row i, group kk) holds keys 4kk .. 4kk+3 of row i:
+//    masking, the row maximum (four local values and two exchanges), the
+//    rescaling factor exp2(m_old - m_new), P = exp2(S - m_new) and the lane's
+//    part of the row sum are per-lane work;
+//  * the four output tiles (dimensions in blocks of 16, accumulator layout:
+//    lane (dimension d, group g) holds rows 4g..4g+3) are rescaled with the
+//    factors of their rows, fetched by lane exchange, then O += P V with the
+//    values read four keys at a time from the transposed copy.
 // The row sums meet at the end the same way.
 //
-// LDS layouts, XOR-swizzled so that the reads are conflict-free without
-// padding (keys, values and four 32x32 tiles fill exactly 80 KiB, two
-// workgroups per CU at T <= 128): key row j holds its sixteen 16-byte
-// chunks at chunk ^ (j % 16); value (j, d) sits at column d ^ 32 for rows
-// with bit 4 of j set; tile (m, n) at column n ^ 4 (m % 8).
+// LDS layouts, XOR-swizzled so that the reads are conflict-free: key row j
+// holds its sixteen 16-byte chunks at chunk ^ (j % 16); transposed value
+// row d holds its four-key chunks at chunk ^ (d % 16); the score tile has a
+// row stride of 20 floats.  Value columns past T (up to the next multiple of
+// 16) are zero, so masked keys (p = 0) multiply finite values.
 constexpr int kHeadSize = 64, kKeyBlock = 32;
 
 // 16-byte loads each thread keeps in flight while filling the key and value tiles.
 constexpr int kLoadGroup = 8;
 
 __device__ inline int k_at(int j, int chunk) { return j * kHeadSize + ((chunk ^ (j & 15)) << 2); }
-__device__ inline int v_at(int j, int d) { return j * kHeadSize + (d ^ (((j >> 4) & 1) << 5)); }
 __device__ inline int p_at(int m, int n) { return m * 32 + (n ^ ((m & 7) << 2)); }
+template <int TMAX> __device__ inline int vt_at(int d, int key) {
+    return d * TMAX + ((((key >> 2) ^ (d & 15)) << 2) | (key & 3));
+}
+constexpr int kTile16 = 20;  // row stride of the 16×16 score tile (floats)
 
 template <int DT, bool CAUSAL, int TMAX>
 __global__ __launch_bounds__(256) void attention_kernel(const void* __restrict__ qkv, void* __restrict__ out,
                                                         float* __restrict__ lse, int T, int NH) {
     constexpr int HS = kHeadSize;
     constexpr int EPV = Elem<DT>::per16;  // elements per 16-byte vector
+    static_assert(EPV == 4, "the fp32 kernel");
     __shared__ __attribute__((aligned(16))) float Ks[TMAX * HS];
-    __shared__ __attribute__((aligned(16))) float Vs[TMAX * HS];
-    __shared__ __attribute__((aligned(16))) float Ps[4 * 32 * 32];
+    __shared__ __attribute__((aligned(16))) float Vt[HS * TMAX];
+    __shared__ __attribute__((aligned(16))) float Ps[4 * 16 * kTile16];
     const int bh = blockIdx.x, b = bh / NH, h = bh % NH;
     const int64_t C = (int64_t)NH * HS, C3 = 3 * C;
     const int64_t head = (int64_t)b * T * C3 + (int64_t)h * HS;  // q of row 0 of this head
 
     // Keys and values, 16-byte vectors: each thread has kLoadGroup loads in
     // flight before it stores any of them (one load, wait, store per vector
-    // would chain the memory latency kLoadGroup times).
+    // would chain the memory latency kLoadGroup times).  Value columns T ..
+    // Tz-1 of the transposed copy are written as zeros.
     constexpr int VPR = HS / EPV;  // 16-byte vectors per row
-    const int nvec = 2 * T * VPR;
+    const int Tz = (T + 15) / 16 * 16;
+    const int nvec = (T + Tz) * VPR;
     for (int base = threadIdx.x; base < nvec; base += 256 * kLoadGroup) {
         float f[kLoadGroup][EPV];
 #pragma unroll
         for (int i = 0; i < kLoadGroup; ++i) {
             const int idx = base + 256 * i;
-            if (idx < nvec) {
-                const int which = idx / (T * VPR), rem = idx % (T * VPR), j = rem / VPR, c0 = (rem % VPR) * EPV;
-                load_vec<DT, EPV>(qkv, head + (int64_t)j * C3 + (which + 1) * C + c0, f[i]);
-            }
+            const bool isv = idx >= T * VPR;
+            const int rem = isv ? idx - T * VPR : idx, j = rem / VPR, c0 = (rem % VPR) * EPV;
+#pragma unroll
+            for (int u = 0; u < EPV; ++u) f[i][u] = 0.0f;
+            if (idx < nvec && j < T)
+                load_vec<DT, EPV>(qkv, head + (int64_t)j * C3 + (isv ? 2 : 1) * C + c0, f[i]);
         }
 #pragma unroll
         for (int i = 0; i < kLoadGroup; ++i) {
             const int idx = base + 256 * i;
-            if (idx < nvec) {
-                const int which = idx / (T * VPR), rem = idx % (T * VPR), j = rem / VPR, c0 = (rem % VPR) * EPV;
+            if (idx >= nvec) continue;
+            const bool isv = idx >= T * VPR;
+            const int rem = isv ? idx - T * VPR : idx, j = rem / VPR, c0 = (rem % VPR) * EPV;
+            if (isv) {
 #pragma unroll
-                for (int u = 0; u < EPV; u += 4) {
-                    const f32x4 x = {f[i][u], f[i][u + 1], f[i][u + 2], f[i][u + 3]};
-                    float* dst = which ? Vs + v_at(j, c0 + u) : Ks + k_at(j, (c0 + u) >> 2);
-                    *reinterpret_cast<f32x4*>(dst) = x;
-                }
+                for (int u = 0; u < EPV; ++u) Vt[vt_at<TMAX>(c0 + u, j)] = f[i][u];
+            } else {
+                *reinterpret_cast<f32x4*>(Ks + k_at(j, c0 >> 2)) = f32x4{f[i][0], f[i][1], f[i][2], f[i][3]};
             }
         }
     }
     __syncthreads();
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, r = lane & 31, g = lane >> 5;
-    float* P = Ps + wave * 1024;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, c16 = lane & 15, kk = lane >> 4;
+    float* P = Ps + wave * 16 * kTile16;
     const float qscale = 1.4426950408889634f / 8.0f;  // log2(e) / sqrt(64)
-    // the 16 accumulator rows of this lane: 8q + 4g + i, read from a tile row as four 16-byte runs
-    auto gather_rows = [&](float (&dst)[16]) {
+    const int nqb = (T + 15) / 16;
+    for (int group = 0; group < nqb; group += 8) {
+        for (int half = 0; half < 2; ++half) {
+            const int qblk = group + (half ? 7 - wave : wave);
+            if (qblk >= nqb) continue;  // wave-uniform
+            const int q0 = qblk * 16;
+            const int myrow = q0 + c16;  // this lane's row in the operand layout
+            float q[16];                 // dimensions 16kk .. 16kk+15 of row myrow
 #pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {
-            const f32x4 x = *reinterpret_cast<const f32x4*>(P + p_at(0, 8 * qd + 4 * g));
-            dst[4 * qd] = x[0], dst[4 * qd + 1] = x[1], dst[4 * qd + 2] = x[2], dst[4 * qd + 3] = x[3];
-        }
-    };
-    for (int qb = 0; qb < T; qb += 128) {
-        const int row0 = qb + wave * 32;
-        if (row0 >= T) break;  // wave-uniform
-        const int myrow = row0 + r;  // the row this lane holds in the operand layout
-        // A operand of S: row myrow, head dimensions g*32 .. g*32+31
-        float q[32];
+            for (int c = 0; c < 16; c += EPV)
+                load_vec<DT, EPV>(qkv, head + (int64_t)min(myrow, T - 1) * C3 + 16 * kk + c, q + c);
 #pragma unroll
-        for (int c = 0; c < 32; c += EPV)
-            load_vec<DT, EPV>(qkv, head + (int64_t)min(myrow, T - 1) * C3 + g * 32 + c, q + c);
+            for (int c = 0; c < 16; ++c) q[c] *= qscale;
+            f32x4 o[4];
 #pragma unroll
-        for (int c = 0; c < 32; ++c) q[c] *= qscale;
-        f32x16 o0, o1;
+            for (int dt = 0; dt < 4; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            float m = -INFINITY, lp = 0.0f;  // running maximum and this lane's part of the row sum
+            const int kend = CAUSAL ? min(T, q0 + 16) : T;
+            for (int j0 = 0; j0 < kend; j0 += 16) {
+                // S: key row j0 + c16 (rows past T hold stale values; their scores are masked below)
+                const int kr = j0 + c16;
+                f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 16; ++e) o0[e] = o1[e] = 0.0f;
-        float m = -INFINITY, lp = 0.0f;  // running maximum and this lane's part of the row sum
-        const int kend = CAUSAL ? min(T, row0 + 32) : T;
-        for (int j0 = 0; j0 < kend; j0 += kKeyBlock) {
-            const int kr = min(j0 + r, T - 1);
-            f32x16 sacc;
+                for (int t = 0; t < 4; ++t) {
+                    const f32x4 kv = *reinterpret_cast<const f32x4*>(Ks + k_at(kr, 4 * kk + t));
+                    s0 = mfma16_f32(q[4 * t], kv[0], s0);
+                    s1 = mfma16_f32(q[4 * t + 1], kv[1], s1);
+                    s0 = mfma16_f32(q[4 * t + 2], kv[2], s0);
+                    s1 = mfma16_f32(q[4 * t + 3], kv[3], s1);
+                }
+                // accumulator layout (key c16, rows 4kk + e) -> operand layout (row c16, keys 4kk ..
+                // 4kk+3).  LDS operations of one wave complete in issue order; the empty asm
+                // statements keep the compiler from reordering these accesses across each other.
+                asm volatile("" ::: "memory");
 #pragma unroll
-            for (int e = 0; e < 16; ++e) sacc[e] = 0.0f;
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const f32x4 kv = *reinterpret_cast<const f32x4*>(Ks + k_at(kr, g * 8 + t));
-#pragma unroll
-                for (int u = 0; u < 4; ++u) sacc = mfma32_f32(q[4 * t + u], kv[u], sacc);
-            }
-            // accumulator layout -> operand layout through the wave's tile.  The tile is reused for the
-            // rescaling factors; LDS operations of one wave complete in issue order, and the empty asm
-            // statements keep the compiler from reordering these accesses across each other.
-            asm volatile("" ::: "memory");
-#pragma unroll
-            for (int e = 0; e < 16; ++e) P[p_at(8 * (e >> 2) + 4 * g + (e & 3), r)] = sacc[e];
-            float p[16];
-#pragma unroll
-            for (int k4 = 0; k4 < 4; ++k4) {
-                const f32x4 x = *reinterpret_cast<const f32x4*>(P + p_at(r, g * 16 + 4 * k4));
-                p[4 * k4] = x[0], p[4 * k4 + 1] = x[1], p[4 * k4 + 2] = x[2], p[4 * k4 + 3] = x[3];
-            }
-            float bm = -INFINITY;
-#pragma unroll
-            for (int c = 0; c < 16; ++c) {
-                const int key = j0 + g * 16 + c;
-                const bool keep = key < T && myrow < T && (!CAUSAL || key <= myrow);
-                p[c] = keep ? p[c] : -INFINITY;
-                bm = fmaxf(bm, p[c]);
-            }
-            bm = fmaxf(bm, __shfl_xor(bm, 32, 64));  // the other half of the row
-            const float mn = fmaxf(m, bm);
-            const float ms = mn == -INFINITY ? 0.0f : mn;  // a row with nothing visible yet stays at zero
-            const float corr = __builtin_amdgcn_exp2f(m - ms);
-            m = mn;
-            float ps = 0.0f;
-#pragma unroll
-            for (int c = 0; c < 16; ++c) {
-                p[c] = __builtin_amdgcn_exp2f(p[c] - ms);
-                ps += p[c];
-            }
-            lp = lp * corr + ps;
-            // rescaling factors back to the accumulator rows
-            asm volatile("" ::: "memory");
-            if (g == 0) P[p_at(0, r)] = corr;
-            asm volatile("" ::: "memory");
-            float cr[16];
-            gather_rows(cr);
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                o0[e] *= cr[e];
-                o1[e] *= cr[e];
-            }
-            // O += P V: keys g*16 + 4 k4 + u of this block
-#pragma unroll
-            for (int k4 = 0; k4 < 4; ++k4)
+                for (int e = 0; e < 4; ++e) P[(4 * kk + e) * kTile16 + c16] = s0[e] + s1[e];
+                const f32x4 sv = *reinterpret_cast<const f32x4*>(P + c16 * kTile16 + 4 * kk);
+                asm volatile("" ::: "memory");
+                float p[4] = {sv[0], sv[1], sv[2], sv[3]};
+                float bm = -INFINITY;
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    const int vr = min(j0 + g * 16 + 4 * k4 + u, T - 1);  // masked keys carry p = 0
-                    o0 = mfma32_f32(p[4 * k4 + u], Vs[v_at(vr, r)], o0);
-                    o1 = mfma32_f32(p[4 * k4 + u], Vs[v_at(vr, 32 + r)], o1);
+                    const int key = j0 + 4 * kk + u;
+                    const bool keep = key < T && myrow < T && (!CAUSAL || key <= myrow);
+                    p[u] = keep ? p[u] : -INFINITY;
+                    bm = fmaxf(bm, p[u]);
                 }
-        }
-        const float l = lp + __shfl_xor(lp, 32, 64);
-        if (g == 0 && lse && myrow < T)
-            lse[((int64_t)b * NH + h) * T + myrow] = (m + __builtin_amdgcn_logf(l)) * 0.6931471805599453f;
-        asm volatile("" ::: "memory");
-        if (g == 0) P[p_at(0, r)] = 1.0f / l;
-        asm volatile("" ::: "memory");
-        float inv[16];
-        gather_rows(inv);
+                bm = fmaxf(bm, __shfl_xor(bm, 16, 64));  // the row's other key groups
+                bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+                const float mn = fmaxf(m, bm);
+                const float ms = mn == -INFINITY ? 0.0f : mn;  // a row with nothing visible yet stays at zero
+                const float corr = __builtin_amdgcn_exp2f(m - ms);
+                m = mn;
+                float ps = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int row = row0 + 8 * (e >> 2) + 4 * g + (e & 3);
-            if (row < T) {
-                const int64_t orow = ((int64_t)b * T + row) * C + (int64_t)h * HS;
-                const float y0 = o0[e] * inv[e], y1 = o1[e] * inv[e];
-                store_vec<DT, 1>(out, orow + r, &y0);
-                store_vec<DT, 1>(out, orow + 32 + r, &y1);
+                for (int u = 0; u < 4; ++u) {
+                    p[u] = __builtin_amdgcn_exp2f(p[u] - ms);
+                    ps += p[u];
+                }
+                lp = lp * corr + ps;
+                // rescaling factors of the accumulator rows 4kk + e (held by lanes 4kk + e of group 0)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float ce = __shfl(corr, 4 * kk + e, 64);
+#pragma unroll
+                    for (int dt = 0; dt < 4; ++dt) o[dt][e] *= ce;
+                }
+                // O += P V: keys j0 + 4kk + u, dimensions 16dt + c16 of the value tile
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) {
+                    const f32x4 vv = *reinterpret_cast<const f32x4*>(Vt + vt_at<TMAX>(16 * dt + c16, j0 + 4 * kk));
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) o[dt] = mfma16_f32(p[u], vv[u], o[dt]);
+                }
+            }
+            float l = lp + __shfl_xor(lp, 16, 64);
+            l += __shfl_xor(l, 32, 64);
+            if (kk == 0 && lse && myrow < T)
+                lse[((int64_t)b * NH + h) * T + myrow] = (m + __builtin_amdgcn_logf(l)) * 0.6931471805599453f;
+            const float inv = 1.0f / l;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float ie = __shfl(inv, 4 * kk + e, 64);
+                const int row = q0 + 4 * kk + e;
+                if (row < T) {
+                    const int64_t orow = ((int64_t)b * T + row) * C + (int64_t)h * HS;
+#pragma unroll
+                    for (int dt = 0; dt < 4; ++dt) {
+                        const float y = o[dt][e] * ie;
+                        store_vec<DT, 1>(out, orow + 16 * dt + c16, &y);
+                    }
+                }
             }
         }
     }
