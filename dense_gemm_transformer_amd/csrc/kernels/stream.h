@@ -230,82 +230,134 @@ __global__ __launch_bounds__(64 * NB * KW) void stream_kernel(const void* __rest
     }
 }
 
-// Narrow 16-bit layers (M <= 16, K a multiple of 512 up to 4096): the 16
-// weight rows of a tile live in LDS for the whole K range.  Timed on the
-// 16×4096×4096 layer with cold weights, this beats streaming the weight into
-// registers by 0.3-0.8 µs of ~9 (probe kernels, rocprofv3 medians on several
-// boxes), for two reasons:
-//  * each direct load (global_load_lds) reads one contiguous KiB of a weight
-//    row, where an MFMA-operand load spreads 64 bytes over each of 16 rows;
-//    the weight is never in registers, so it needs no staging;
-//  * X goes straight to registers in the MFMA operand layout, each wave its
-//    own K range, X and weight loads interleaved: X needs no LDS store and no
-//    barrier of its own, and never waits behind the whole weight stream.
-// Wave w fetches weight rows 2w and 2w+1; instruction (row R, KiB h) lands
-// at LDS row R, bytes [1 KiB·h, 1 KiB·(h+1)), lane l at 16·l.  The lanes
-// fetch the 16-byte chunks of that KiB permuted, chunk c at c ^ (R % 16), so
-// the operand reads of 16 rows at one k hit 16 distinct 4-bank groups.  Wave
-// w then multiplies K range [w·K/8, (w+1)·K/8) and the 8 partials are summed
-// through LDS in wave order, as in the register-streaming kernel.
-// PR: KiB-instructions per weight row (K = 512·PR); a wave issues 2·PR
-// direct loads and 2·PR X loads and runs 2·PR MFMA steps of 32 k, all
-// unrolled with no condition, so every load is issued before the first wait.
+// Wait until at most N vector-memory operations of this wave are in flight
+// (direct loads to LDS included).  The scheduling barriers keep the LDS reads
+// of the phase this wait covers below it.
+template <int N> __device__ inline void wait_vmem() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Narrow 16-bit layers (M <= 16, K a multiple of 512 up to 4096): wave w
+// owns K range [w·K/8, (w+1)·K/8) and fetches exactly the weights it
+// multiplies, all 16 rows of the tile over that range, into an LDS region of
+// its own by direct loads (global_load_lds); X goes straight to registers in
+// the MFMA operand layout.  Timed on the 16×4096×4096 layer with cold
+// weights (probe kernels, rocprofv3 medians), against the alternatives:
+//  * streaming the weight into registers costs 1.5-2 µs more of ~9: an
+//    MFMA-operand load spreads 64 bytes over each of 16 rows, where a direct
+//    load here reads 128-byte runs of 8 rows;
+//  * fetching whole rows per wave and multiplying after one workgroup
+//    barrier (no product starts before the last weight byte of the tile has
+//    landed) measured 8.6-8.8 against 8.2 µs at K = 4096, and 0.2-0.7 µs
+//    more at every K from 512 to 3584 but one: at K = 2048 it was 0.5 µs
+//    faster (6.1 against 6.7 µs), a case no tuned workload has.
+// The wave's range is fetched in PR phases of 64 columns.  A phase is two X
+// loads and two direct loads of 8 rows × 128 bytes (lane l: row 8i + l/8,
+// 16-byte chunk l%8), and each phase has an LDS array of its own, so the wait
+// before a phase's reads covers that phase's loads only (with one array for
+// all of them the compiler waits for every load of the wave).  Products start
+// as soon as the first phase has landed, with no barrier.  Chunk c of row R
+// sits at position c ^ ((R/2) % 8) of its 128-byte slot, so the 16 lanes
+// reading one k of 16 rows (two rows per 256 bytes) hit 16 distinct 4-bank
+// groups.  The 8 wave partials are summed through LDS in wave order; waves
+// 0-3 each finish one of the four accumulator rows.
+// PR: 512-column steps of K (K = 512·PR); a wave issues 4·PR loads up front
+// and runs 2·PR MFMA steps of 32 k, all unrolled.
 template <int IN, int OUT, uint32_t EPI, int PR>
 __global__ __launch_bounds__(512) void stream_dl_kernel(const void* __restrict__ Xv, const void* __restrict__ Wv,
                                                        const void* __restrict__ bias, void* __restrict__ Y, int M,
                                                        int N, int resid) {
     static_assert(IN != TLG_F32 && PR >= 1 && PR * kStreamDlKStep <= kStreamDlMaxK, "16-bit operands, K in LDS");
+    static_assert(kStreamDlMaxK / kStreamDlKStep <= 8, "one LDS array per phase, at most 8");
     using S = uint16_t;
-    constexpr int KW = 8, K = PR * kStreamDlKStep, STEPS = 2 * PR, KPW = K / KW;
-    __shared__ __attribute__((aligned(16))) S wl[16 * K];
+    constexpr int KW = 8, K = PR * kStreamDlKStep, KPW = K / KW;  // KPW = 64·PR: PR phases of 64 columns
+    constexpr int PH = KW * 16 * 64;                             // one phase of every wave
+    __shared__ __attribute__((aligned(16))) S ph0[PH];
+    __shared__ __attribute__((aligned(16))) S ph1[PR > 1 ? PH : 8];
+    __shared__ __attribute__((aligned(16))) S ph2[PR > 2 ? PH : 8];
+    __shared__ __attribute__((aligned(16))) S ph3[PR > 3 ? PH : 8];
+    __shared__ __attribute__((aligned(16))) S ph4[PR > 4 ? PH : 8];
+    __shared__ __attribute__((aligned(16))) S ph5[PR > 5 ? PH : 8];
+    __shared__ __attribute__((aligned(16))) S ph6[PR > 6 ? PH : 8];
+    __shared__ __attribute__((aligned(16))) S ph7[PR > 7 ? PH : 8];
     __shared__ float red[KW * 4 * 64];
     const S* __restrict__ X = static_cast<const S*>(Xv);
     const S* __restrict__ W = static_cast<const S*>(Wv);
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int r = lane & 15, g = lane >> 4;
     const int n0 = blockIdx.x * 16;
+    // this wave's part of phase p: two 1 KiB blocks of 8 rows × 64 columns
+    auto region = [&](auto pc) -> S* {
+        constexpr int p = decltype(pc)::value;
+        S* a = p == 0 ? ph0 : p == 1 ? ph1 : p == 2 ? ph2 : p == 3 ? ph3 : p == 4 ? ph4 : p == 5 ? ph5 : p == 6 ? ph6 : ph7;
+        return a + w * (16 * 64);
+    };
     const S* xrow = X + (int64_t)min(r, M - 1) * K + w * KPW + 8 * g;  // rows past M repeat row M-1, never stored
-    u32x4 xr[STEPS];
+    const int lr = lane >> 3, lc = lane & 7;
+    u32x4 xr[2 * PR];
+    auto issue = [&](auto pc) {
+        constexpr int p = decltype(pc)::value;
+        S* dst = region(pc);
+        xr[2 * p] = ldg16(xrow + 64 * p);
+        xr[2 * p + 1] = ldg16(xrow + 64 * p + 32);
 #pragma unroll
-    for (int j = 0; j < STEPS; ++j) {
-        xr[j] = ldg16(xrow + 32 * j);
-        const int R = 2 * w + j / PR, h = j % PR;
-        const int c = ((h << 6) + lane) ^ (R & 15);
-        const S* src = W + (int64_t)min(n0 + R, N - 1) * K + 8 * c;  // rows past N repeat row N-1, never stored
-        __builtin_amdgcn_global_load_lds((const void*)src,
-                                         (__attribute__((address_space(3))) void*)(wl + R * K + h * 512), 16, 0,
-                                         2 /* nt: streamed once */);
-    }
-    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): this wave's X and direct loads have landed
-    __syncthreads();                                   // and every other wave's weight rows
+        for (int i = 0; i < 2; ++i) {
+            const int R = 8 * i + lr;
+            const S* src = W + (int64_t)min(n0 + R, N - 1) * K + w * KPW + 64 * p + 8 * (lc ^ ((R >> 1) & 7));
+            __builtin_amdgcn_global_load_lds((const void*)src,  // rows past N repeat row N-1, never stored
+                                             (__attribute__((address_space(3))) void*)(dst + 512 * i), 16, 0,
+                                             2 /* nt: streamed once */);
+        }
+    };
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const int rd = 512 * (r >> 3) + 64 * (r & 7), sw = (r >> 1) & 7;
+    auto multiply = [&](auto pc) {
+        constexpr int p = decltype(pc)::value;
+        wait_vmem<4 * (PR - p - 1)>();  // this phase's X and weight loads have landed
+        const S* src = region(pc) + rd;
 #pragma unroll
-    for (int j = 0; j < STEPS; ++j) {
-        const int c = (w * KPW + 32 * j) / 8 + g;  // 16-byte chunk of weight row r
-        const u32x4 wv = *reinterpret_cast<const u32x4*>(wl + r * K + 8 * (c ^ r));
-        acc = mfma16_16bit<IN>(xr[j], wv, acc);
-    }
+        for (int i = 0; i < 2; ++i) {
+            const u32x4 wv = *reinterpret_cast<const u32x4*>(src + 8 * ((4 * i + g) ^ sw));
+            acc = mfma16_16bit<IN>(xr[2 * p + i], wv, acc);
+        }
+    };
+    using std::integral_constant;
+    issue(integral_constant<int, 0>{});
+    if constexpr (PR > 1) issue(integral_constant<int, 1>{});
+    if constexpr (PR > 2) issue(integral_constant<int, 2>{});
+    if constexpr (PR > 3) issue(integral_constant<int, 3>{});
+    if constexpr (PR > 4) issue(integral_constant<int, 4>{});
+    if constexpr (PR > 5) issue(integral_constant<int, 5>{});
+    if constexpr (PR > 6) issue(integral_constant<int, 6>{});
+    if constexpr (PR > 7) issue(integral_constant<int, 7>{});
+    multiply(integral_constant<int, 0>{});
+    if constexpr (PR > 1) multiply(integral_constant<int, 1>{});
+    if constexpr (PR > 2) multiply(integral_constant<int, 2>{});
+    if constexpr (PR > 3) multiply(integral_constant<int, 3>{});
+    if constexpr (PR > 4) multiply(integral_constant<int, 4>{});
+    if constexpr (PR > 5) multiply(integral_constant<int, 5>{});
+    if constexpr (PR > 6) multiply(integral_constant<int, 6>{});
+    if constexpr (PR > 7) multiply(integral_constant<int, 7>{});
     // wave partials summed in wave order; a 16×16 accumulator holds column
     // (lane % 16) and rows 4·(lane / 16) + e
 #pragma unroll
     for (int e = 0; e < 4; ++e) red[(w * 4 + e) * 64 + lane] = acc[e];
     __syncthreads();
-    if (w != 0) return;
-    const int n = n0 + r;
-    float b = 0.0f;
-    if constexpr ((EPI & TLG_EPI_BIAS) != 0)
-        if (n < N) b = load_elem<IN>(bias, n);
+    if (w >= 4) return;
+    float sum = red[w * 64 + lane];  // wave w < 4 finishes accumulator row e = w
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        float sum = red[e * 64 + lane];
-#pragma unroll
-        for (int q = 1; q < KW; ++q) sum += red[(q * 4 + e) * 64 + lane];
-        const int m = 4 * g + e;
-        if (m < M && n < N) {
-            float v = epilogue<EPI>(sum, b);
-            if (resid) v += load_elem<OUT>(Y, (int64_t)m * N + n);
-            store_out<OUT>(Y, (int64_t)m * N + n, v);
-        }
+    for (int q = 1; q < KW; ++q) sum += red[(q * 4 + w) * 64 + lane];
+    const int m = 4 * g + w, n = n0 + r;
+    if (m < M && n < N) {
+        float b = 0.0f;
+        if constexpr ((EPI & TLG_EPI_BIAS) != 0) b = load_elem<IN>(bias, n);
+        float v = epilogue<EPI>(sum, b);
+        if (resid) v += load_elem<OUT>(Y, (int64_t)m * N + n);
+        store_out<OUT>(Y, (int64_t)m * N + n, v);
     }
 }
 
