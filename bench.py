@@ -62,8 +62,8 @@ FETCH_SCALE, WRITE_SCALE = 1.998, 1.0
 TRAFFIC = {
     "tiled_f32": {"sources": ("common.h", "tiled.h"), "sha": "681d253f3b2fd783",
                   "tile": "256x256x16", "fetch_kib": 196687.0, "write_kib": 65536.0},
-    "stream_f16": {"sources": ("common.h", "stream.h"), "sha": "8ce0548efe2ee6ec",
-                   "tile": "16x16x4096", "fetch_kib": 16920.5, "write_kib": 128.0},
+    "stream_f16": {"sources": ("common.h", "stream.h"), "sha": "95153d19377ba2f0",
+                   "tile": "16x16x4096", "fetch_kib": 16918.5, "write_kib": 128.0},
 }
 
 
@@ -971,7 +971,7 @@ def main(argv=None) -> int:
                                      "traffic": measured_traffic("stream_f16", tile_str(nplan)),
                                      "kernel": f"stream kernel fp16 {nplan.info.tile_m}x{nplan.info.tile_n}, "
                                                f"{nplan.info.threads // 64} waves over K"
-                                               + (", weight rows in LDS" if "load=direct" in nplan.describe() else ""),
+                                               + (", each wave's K range of the weight rows in LDS" if "load=direct" in nplan.describe() else ""),
                                      "algorithmic_bytes_per_launch": n_bytes},
                         "timing": "HIP events over back-to-back launches (includes launch gaps)",
                         "plan": nplan.describe()},
