@@ -525,9 +525,14 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) 
     constexpr int CPR = WTN / EPC;                             // 16-byte runs per staged row
     // Stage the accumulators through this wave's strip stg, then apply bias,
     // GELU and the residual and store (generic, so that it is instantiated
-    // only where it is used).
+    // only where it is used).  A half-strip holds 16·CPR runs.  Where CPR
+    // divides 64 a lane keeps one column set for all its runs (bias loaded
+    // once); otherwise (wave tiles 96 or 192 columns wide) the lanes take
+    // runs 64 apart with a guard on the last round, and each run's columns
+    // and bias are its own.
+    constexpr bool EVEN_RUNS = 64 % CPR == 0 && (16 * CPR) % 64 == 0;
+    constexpr int NRUN = (16 * CPR + 63) / 64;
     auto store_staged = [&](auto* stg) {
-        static_assert(64 % CPR == 0 && (16 * CPR) % 64 == 0, "runs divide evenly over the lanes");
         // Opaque copy of the lane index: everything the epilogue derives from
         // it is computed here, after the loop, instead of being hoisted in
         // front of it and held in registers through it (which spilled the
@@ -540,7 +545,7 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) 
 #pragma unroll
         for (int q = 0; q < EPC; ++q) {
             bcol[q] = 0.0f;
-            if constexpr (!SPLIT && (EPI & TLG_EPI_BIAS) != 0) bcol[q] = load_elem<IN>(bias, ncol + q);
+            if constexpr (EVEN_RUNS && !SPLIT && (EPI & TLG_EPI_BIAS) != 0) bcol[q] = load_elem<IN>(bias, ncol + q);
         }
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
@@ -554,9 +559,20 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) 
                 // LDS operations of one wave complete in order: the reads
                 // below see these writes, and the next half's writes follow them.
 #pragma unroll
-                for (int q = 0; q < (16 * CPR) / 64; ++q) {
-                    const int row = (el + 64 * q) / CPR;
-                    const float* src = stg + row * SROW + col;
+                for (int q = 0; q < NRUN; ++q) {
+                    const int run = el + 64 * q;
+                    if (!EVEN_RUNS && run >= 16 * CPR) break;
+                    const int row = run / CPR;
+                    const int rcol = EVEN_RUNS ? col : (run % CPR) * EPC;  // this run's first column in the strip
+                    const int nrun = n0 + wn0 + rcol;
+                    float brun[EPC];
+#pragma unroll
+                    for (int u = 0; u < EPC; ++u) {
+                        brun[u] = bcol[u];
+                        if constexpr (!EVEN_RUNS && !SPLIT && (EPI & TLG_EPI_BIAS) != 0)
+                            brun[u] = load_elem<IN>(bias, nrun + u);
+                    }
+                    const float* src = stg + row * SROW + rcol;
                     float v[EPC];
 #pragma unroll
                     for (int u = 0; u < EPC; u += 4) {
@@ -568,11 +584,11 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_occupancy<BM, BN, WM, WN>())) 
                     if constexpr (SPLIT) {
 #pragma unroll
                         for (int u = 0; u < 4; ++u) out[u] = __float_as_uint(v[u]);
-                        *reinterpret_cast<u32x4*>(ws + ((int64_t)z * M + m) * N + ncol) = out;
+                        *reinterpret_cast<u32x4*>(ws + ((int64_t)z * M + m) * N + nrun) = out;
                     } else {
 #pragma unroll
-                        for (int u = 0; u < EPC; ++u) v[u] = epilogue<EPI>(v[u], bcol[u]);
-                        u32x4* dst = reinterpret_cast<u32x4*>(static_cast<char*>(Y) + (m * N + ncol) * OB);
+                        for (int u = 0; u < EPC; ++u) v[u] = epilogue<EPI>(v[u], brun[u]);
+                        u32x4* dst = reinterpret_cast<u32x4*>(static_cast<char*>(Y) + (m * N + nrun) * OB);
                         if (resid) {
                             float rv[EPC];
                             unpack16<OUT>(*dst, rv);
@@ -924,13 +940,14 @@ int launch_tiled_in(const tlg_plan& p, const void* X, const void* W, const void*
                 constexpr uint32_t E = (uint32_t)decltype(epi)::value;
                 constexpr const TileCfg* T = I == TLG_F32 ? kTiledF32 : kTiled16;
                 constexpr int count = I == TLG_F32 ? kNumTiledF32 : kNumTiled16;
-                static_assert(kNumTiledF32 == 8 && kNumTiled16 == 11, "tile lists changed");
+                static_assert(kNumTiledF32 == 8 && kNumTiled16 == 13, "tile lists changed");
 #define TLG_TILED_CASE(i)                                                                                     \
     case i:                                                                                                   \
         if constexpr (i < count) {                                                                            \
             constexpr TileCfg c = T[i];                                                                       \
-            return launch_tiled_cfg<I, O, L, E, c.bm, c.bn, c.bk, c.wm, c.wn, c.cap, c.dl, c.pers>(p, X, W, bias, Y, \
-                                                                                                   wsf, stream);   \
+            if constexpr (tile_fits_layout(c, I, L))                                                          \
+                return launch_tiled_cfg<I, O, L, E, c.bm, c.bn, c.bk, c.wm, c.wn, c.cap, c.dl, c.pers>(       \
+                    p, X, W, bias, Y, wsf, stream);                                                           \
         }                                                                                                     \
         break;
                 switch (p.tile) {
@@ -945,6 +962,8 @@ int launch_tiled_in(const tlg_plan& p, const void* X, const void* W, const void*
                     TLG_TILED_CASE(8)
                     TLG_TILED_CASE(9)
                     TLG_TILED_CASE(10)
+                    TLG_TILED_CASE(11)
+                    TLG_TILED_CASE(12)
                 default: break;
                 }
                 set_error("bad tiled tile");

@@ -190,6 +190,11 @@ static int fill_tiled(tlg_plan& p, int tile, int split) {
         return TLG_ERR_INVALID_ARG;
     }
     const TileCfg& c = tiled_cfg(p.in_dt, tile);
+    if (!tile_fits_layout(c, p.in_dt, p.layout)) {
+        set_error("tiled tile %dx%d does not take layout %d (its loads do not divide over its threads)", c.bm, c.bn,
+                  p.layout);
+        return TLG_ERR_UNSUPPORTED;
+    }
     const int64_t ksteps = ceil_div(p.K, c.bk);
     if (split < 0 || split > ksteps) {
         set_error("split_k=%d must be in 1..%lld for K=%lld", split, (long long)ksteps, (long long)p.K);

@@ -70,7 +70,29 @@ constexpr TileCfg kTiled16[] = {
     {128, 128, 32, 2, 2, 0, 4},   // 8: direct loads, four 32-deep stages (three slices in flight)
     {128, 128, 64, 2, 2, 0, 0, 1},  // 9: persistent, the next tile's first slices loaded during this one's end
     {128, 128, 64, 2, 2, 0, 2, 1},  // 10: persistent with direct loads (warm-fast, slower in a cold pass of GPT-2 layers)
+    // 128×192 tiles (64×96 per wave): at 8192 rows the GPT-2 widths 768 and 2304
+    // make 256 or 768 of them, whole rounds of the 256 CUs where 128×128 makes
+    // 1.5 or 4.5.  Warm probe, bf16 with bias: proj 8192×768×3072 54.3 → 42.9 µs
+    // (11), qkv 8192×2304×768 39.8 → 38.1 µs (12, against entry 10).
+    {128, 192, 64, 2, 2, 0, 0, 1},  // 11: persistent, staged
+    {128, 192, 64, 2, 2, 0, 2, 1},  // 12: persistent with direct loads (80 KiB: two per CU)
 };
+// Whether a tile's operand loads divide evenly over its threads for a
+// layout: every thread issues the same whole number of 16-byte loads of each
+// operand, and a thread's loads of an [K][N] or [K][M] operand (stored
+// n- or m-contiguous in LDS) share one lane offset, so the row width in
+// 16-byte vectors divides the thread count.  The tiled kernel asserts the same
+// at compile time; the planner refuses the rest (the 128×192 tiles take no
+// [K][N] weight: 24 vectors per row against 256 threads).
+constexpr bool tile_fits_layout(const TileCfg& c, int in_dt, int layout) {
+    const int threads = 64 * c.wm * c.wn, epv = in_dt == TLG_F32 ? 4 : 8;
+    const int vpr = c.bk / epv, mv = c.bm / epv, nv = c.bn / epv;
+    const bool at = layout_a_transposed(layout), kn = layout_b_kn(layout);
+    const int a_vec = at ? c.bk * mv : c.bm * vpr, b_vec = kn ? c.bk * nv : c.bn * vpr;
+    return threads % vpr == 0 && (!kn || threads % nv == 0) && (!at || threads % mv == 0) &&
+           a_vec >= threads && a_vec % threads == 0 && b_vec >= threads && b_vec % threads == 0;
+}
+
 constexpr int kNumTiledF32 = sizeof(kTiledF32) / sizeof(kTiledF32[0]);
 constexpr int kNumTiled16 = sizeof(kTiled16) / sizeof(kTiled16[0]);
 

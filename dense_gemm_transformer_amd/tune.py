@@ -46,6 +46,10 @@ from . import inputs, search
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 TABLE = os.path.join(HERE, "csrc", "dispatch_table.inc")
+# Length of each variant's tile list (for 16-bit inputs, the longer tiled list):
+# the options a search walks.  A CPU test checks them against the planner.
+STREAM_OPTIONS = 10
+TILED_OPTIONS = 13
 
 
 def workload_cases():
@@ -87,9 +91,9 @@ def candidates(case, tlgemm):
     out = []
     opts = []
     if case.layout == "NK" and case.M <= 256:
-        for tile in range(1, 11):
+        for tile in range(1, STREAM_OPTIONS + 1):
             opts += [(tlgemm.VARIANT_STREAM, tile, 0), (tlgemm.VARIANT_STREAM, tile, 1)]
-    for tile in range(1, 12):  # past the dtype's tile list the planner refuses, and the option is skipped
+    for tile in range(1, TILED_OPTIONS + 1):  # past the dtype's tile list the planner refuses, and the option is skipped
         for split in (1, 2, 4, 8):
             opts.append((tlgemm.VARIANT_TILED, tile, split))
     for v, tile, split in opts:
@@ -297,7 +301,7 @@ def table_tile(plan) -> int:
     from . import tlgemm
 
     i = plan.info
-    for t in range(1, 12):
+    for t in range(1, max(TILED_OPTIONS, STREAM_OPTIONS) + 1):
         try:
             q = tlgemm.Plan.create(plan.M, plan.N, plan.K, plan.in_dtype, plan.out_dtype, plan.layout,
                                    bool(plan.epi_flags & 1), bool(plan.epi_flags & 2), i.variant, max(i.split_k, 1)

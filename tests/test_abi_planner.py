@@ -292,3 +292,46 @@ def test_stream_weight_rows_in_lds_planning():
     with pytest.raises(t.TlgError):
         _plan(16, 64, 1024, "f16", variant=t.VARIANT_STREAM, tile=6, split_k=2)
     assert _plan(16, 4096, 4608, "f16").info.tile_k != 4608  # too long for LDS: the register-streaming tile
+
+
+def test_search_walks_every_tile_option():
+    """The option counts the measured search walks match the planner's tile lists: the last option of each
+    list plans, the one past it is refused (16-bit tiled list; fp32's is shorter)."""
+    from dense_gemm_transformer_amd import tune
+
+    p = t.Plan.create(16, 4096, 4096, "f16", "f16", "NK", variant=t.VARIANT_STREAM, tile=tune.STREAM_OPTIONS)
+    p.close()
+    with pytest.raises(t.TlgError):
+        t.Plan.create(16, 4096, 4096, "f16", "f16", "NK", variant=t.VARIANT_STREAM, tile=tune.STREAM_OPTIONS + 1)
+    p = t.Plan.create(512, 576, 768, "bf16", "bf16", "NK", variant=t.VARIANT_TILED, tile=tune.TILED_OPTIONS)
+    p.close()
+    with pytest.raises(t.TlgError):
+        t.Plan.create(512, 576, 768, "bf16", "bf16", "NK", variant=t.VARIANT_TILED, tile=tune.TILED_OPTIONS + 1)
+    with pytest.raises(t.TlgError):
+        t.Plan.create(512, 512, 512, "f32", "f32", "NK", variant=t.VARIANT_TILED, tile=9)
+
+
+def test_wide_128x192_tiles_plan():
+    """Tiled options 12 and 13 (128×192, persistent; staged and direct-load): exact fits at the GPT-2 widths
+    plan persistent, the direct-load entry fills LDS by direct loads where the operands allow it."""
+    p = t.Plan.create(8192, 768, 3072, "bf16", "bf16", "NK", bias=True, variant=t.VARIANT_TILED, tile=12)
+    i = p.info
+    assert (i.tile_m, i.tile_n, i.tile_k, i.threads) == (128, 192, 64, 256)
+    assert "persistent" in p.describe() and "load=direct" not in p.describe()
+    p.close()
+    p = t.Plan.create(8192, 2304, 768, "bf16", "bf16", "NK", bias=True, variant=t.VARIANT_TILED, tile=13)
+    assert "persistent" in p.describe() and "load=direct" in p.describe(), p.describe()
+    p.close()
+    # a transposed first operand keeps staged loads; [K][N] weights are refused (24 vectors per row of the
+    # tile against 256 threads); a split or a ragged N is not persistent
+    p = t.Plan.create(2048, 768, 768, "bf16", "bf16", "AT_NK", variant=t.VARIANT_TILED, tile=13)
+    assert "persistent" in p.describe() and "load=direct" not in p.describe(), p.describe()
+    p.close()
+    for layout in ("KN", "AT_KN"):
+        with pytest.raises(t.TlgError) as e:
+            t.Plan.create(2048, 768, 768, "bf16", "bf16", layout, variant=t.VARIANT_TILED, tile=12)
+        assert e.value.status == t.ERR_UNSUPPORTED
+    for (M, N, K), split in [((512, 576, 1536), 2), ((512, 500, 768), 1)]:
+        p = t.Plan.create(M, N, K, "bf16", "bf16", "NK", variant=t.VARIANT_TILED, tile=12, split_k=split)
+        assert "persistent" not in p.describe(), p.describe()
+        p.close()

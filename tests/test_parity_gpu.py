@@ -112,7 +112,11 @@ def test_stream_forced_split(pair, split):
 @pytest.mark.parametrize("layout", ["NK", "KN"])
 @pytest.mark.parametrize("epi", EPIS, ids=["none", "bias", "gelu", "bias+gelu"])
 def test_tiled(pair, layout, epi):
-    for tile in range(1, 9 if pair[0] == "f32" else 12):
+    for tile in range(1, 9 if pair[0] == "f32" else 14):
+        if layout == "KN" and tile >= 12:  # 128×192 takes no [K][N] weight: the planner refuses it
+            with pytest.raises(tlgemm.TlgError):
+                tlgemm.Plan.create(256, 384, 64, pair[0], pair[1], layout, variant=tlgemm.VARIANT_TILED, tile=tile)
+            continue
         for (M, N, K), split in [((130, 136, 72), 1), ((256, 256, 256), 1), ((64, 64, 32), 1),
                                  ((200, 264, 400), 3), ((33, 520, 1024), 4)]:
             c = _case(3, M, N, K, pair, layout, epi)
@@ -187,6 +191,27 @@ def test_tiled_persistent():
             _, desc = _check(c, variant=tlgemm.VARIANT_TILED, tile=tile)
             assert "persistent" in desc, desc
             assert ("load=direct" in desc) == (tile == 11 and layout == "NK"), desc
+
+
+def test_tiled_128x192():
+    """Tiled options 12 and 13 (128×192, 64×96 per wave): the staged epilogue's rows hold 12 (16-bit out) or
+    24 (fp32 out) 16-byte runs, which the lanes take 64 apart with a guard.  Persistent grids of several
+    rounds (staged, and direct loads at two per CU), a transposed first operand, the residual, split partials
+    through the same epilogue, and an odd slice count (no persistence).  Every output is compared with the oracle."""
+    for (M, N, K), pair, layout, epi, res, tile, split, want in [
+            ((4096, 3072, 256), ("bf16", "bf16"), "NK", (True, True), False, 12, 1, "persistent"),
+            ((4096, 4608, 128), ("bf16", "bf16"), "NK", (True, False), False, 13, 1, "load=direct persistent"),
+            ((2048, 1536, 256), ("f16", "f32"), "AT_NK", (False, False), True, 12, 1, "persistent"),
+            ((4096, 2304, 128), ("bf16", "bf16"), "NK", (False, False), True, 13, 1, "persistent"),
+            ((512, 576, 1536), ("f16", "f32"), "NK", (True, True), False, 12, 2, "split=2"),
+            ((512, 576, 1536), ("bf16", "bf16"), "NK", (False, True), True, 13, 2, "split=2"),
+            ((256, 384, 192), ("bf16", "bf16"), "NK", (True, True), False, 12, 1, "tile=128x192x64")]:
+        c = inputs.random_case(21, M, N, K, pair[0], pair[1], layout, bias=epi[0], gelu=epi[1], residual=res)
+        _, desc = _check(c, variant=tlgemm.VARIANT_TILED, tile=tile, split_k=split)
+        assert want in desc, desc
+        assert "tile=128x192x64" in desc, desc
+        if split > 1 or K // 64 % 2:
+            assert "persistent" not in desc, desc
 
 
 def test_tiled_persistent_f32():
