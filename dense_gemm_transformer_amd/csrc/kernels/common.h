@@ -127,6 +127,14 @@ __device__ inline u32x4 ldg16(const void* p) { return *static_cast<const u32x4*>
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 __device__ u32x4 buffer_load16(i32x4 rsrc, uint32_t voffset, int soffset, int aux) __asm(
     "llvm.amdgcn.raw.buffer.load.v4i32");
+__device__ void buffer_store16(u32x4 v, i32x4 rsrc, uint32_t voffset, int soffset, int aux) __asm(
+    "llvm.amdgcn.raw.buffer.store.v4i32");
+// Cache-policy operand of the buffer accesses: device scope (sc1).  A store
+// with it writes through this XCD's L2, and a load with it does not take a
+// line this XCD's L2 may hold from before, so the two exchange data between
+// workgroups on different XCDs without an L2 write-back or invalidate (the
+// access form of a relaxed device-scope atomic on gfx950).
+constexpr int kAuxDevice = 16;
 // Descriptor for the bytes [p, p + bytes), bytes < 2^31: every field is read
 // from the first lane (the arguments are uniform by construction, and this
 // keeps the descriptor in scalar registers), stride 0, 32-bit data format.

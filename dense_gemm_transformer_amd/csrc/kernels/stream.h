@@ -26,7 +26,13 @@
 //    tile, and the last to arrive sums the S partials in split order.  Both
 //    sums run in a fixed order, so results are bitwise reproducible (the
 //    rule of "Optimizing a GPT-2-class transformer on a GPU", Act I).  One
-//    launch, no atomics on data.
+//    launch, no atomics on data.  The partials cross XCDs, whose L2s are not
+//    kept coherent with one another; they are written and read with
+//    device-scope accesses (written through the writer's L2, read past the
+//    reader's), and the writer waits for its stores to complete before it
+//    takes the ticket.  A device-scope release and acquire would write back
+//    and invalidate whole L2s instead: measured on a 16-row probe, 13-17 µs
+//    against 10.2 µs for this form and 8.2 µs with no reduction at all.
 //
 // Rows of X past M and rows of W past N are clamped to valid rows (their
 // outputs are never stored); K past the split's range loads as zero.
@@ -183,23 +189,26 @@ __global__ __launch_bounds__(64 * NB * KW) void stream_kernel(const void* __rest
     } else {
         // Partials in fragment order [split][tile][nb][rb][lane] (one
         // 16-byte store per lane); the reducing workgroup reads the same order.
-        f32x4* frag = reinterpret_cast<f32x4*>(ws);
+        // The host keeps the partial region below 2^31 bytes (one buffer
+        // descriptor covers it).
         const int64_t tiles = (int64_t)gridDim.x * gridDim.z;
         const int64_t tid = (int64_t)blockIdx.z * gridDim.x + tile;  // ticket of this (row block, tile)
         const int64_t per_split = tiles * NB * ROWB * 64;
         const int64_t base = ((tid * NB + nb) * ROWB) * 64 + lane;
+        const i32x4 prs = buffer_rsrc(ws, (int64_t)gridDim.y * per_split * 16);
         if (kw == 0)
 #pragma unroll
-            for (int rb = 0; rb < ROWB; ++rb) frag[split * per_split + base + rb * 64] = acc[rb];
-        // Release this workgroup's partials at device scope (one fence after
-        // the workgroup barrier covers every wave), then take the tile's ticket.
+            for (int rb = 0; rb < ROWB; ++rb)
+                buffer_store16(__builtin_bit_cast(u32x4, acc[rb]), prs,
+                               (uint32_t)((split * per_split + base + rb * 64) * 16), 0, kAuxDevice);
+        // Every store of this wave has completed (written through its L2)
+        // before the workgroup barrier, and so before the ticket is taken.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         __shared__ unsigned last;
-        if (t == 0) {
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-            last = atomicAdd(&tickets[tid], 1u) == gridDim.y - 1;
-            if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        }
+        if (t == 0)
+            last = __hip_atomic_fetch_add(&tickets[tid], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                   gridDim.y - 1;
         __syncthreads();
         if (!last || kw != 0) return;
         const int splits = gridDim.y;
@@ -211,7 +220,10 @@ __global__ __launch_bounds__(64 * NB * KW) void stream_kernel(const void* __rest
             f32x4 part[kStreamMaxSplit];  // every split's fragment in flight, then the ordered sum
 #pragma unroll
             for (int z = 0; z < kStreamMaxSplit; ++z)
-                part[z] = z < splits ? frag[z * per_split + base + rb * 64] : f32x4{0.f, 0.f, 0.f, 0.f};
+                part[z] = z < splits ? __builtin_bit_cast(f32x4, buffer_load16(prs, (uint32_t)((z * per_split + base +
+                                                                                              rb * 64) * 16), 0,
+                                                                               kAuxDevice))
+                                     : f32x4{0.f, 0.f, 0.f, 0.f};
             f32x4 s4 = part[0];
 #pragma unroll
             for (int z = 1; z < kStreamMaxSplit; ++z)

@@ -160,7 +160,12 @@ static int fill_stream(tlg_plan& p, int tile, int split) {
                   (long long)slots, (long long)kWsMaxTickets);
         return TLG_ERR_UNSUPPORTED;
     }
-    p.ws_bytes = S > 1 ? kWsCounterBytes + (size_t)S * slots * bn * 16 * rowb * sizeof(float) : 0;
+    const int64_t part_bytes = S > 1 ? (int64_t)S * slots * bn * 16 * rowb * (int64_t)sizeof(float) : 0;
+    if (part_bytes >= INT32_MAX) {  // the kernel addresses its partials through one buffer descriptor
+        set_error("stream split-K: %lld bytes of partials exceed 2 GiB", (long long)part_bytes);
+        return TLG_ERR_UNSUPPORTED;
+    }
+    p.ws_bytes = S > 1 ? kWsCounterBytes + (size_t)part_bytes : 0;
     return TLG_OK;
 }
 
