@@ -940,7 +940,7 @@ int launch_tiled_in(const tlg_plan& p, const void* X, const void* W, const void*
                 constexpr uint32_t E = (uint32_t)decltype(epi)::value;
                 constexpr const TileCfg* T = I == TLG_F32 ? kTiledF32 : kTiled16;
                 constexpr int count = I == TLG_F32 ? kNumTiledF32 : kNumTiled16;
-                static_assert(kNumTiledF32 == 8 && kNumTiled16 == 13, "tile lists changed");
+                static_assert(kNumTiledF32 == 10 && kNumTiled16 == 13, "tile lists changed");
 #define TLG_TILED_CASE(i)                                                                                     \
     case i:                                                                                                   \
         if constexpr (i < count) {                                                                            \

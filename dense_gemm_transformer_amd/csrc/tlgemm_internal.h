@@ -47,6 +47,10 @@ constexpr TileCfg kTiledF32[] = {
     {256, 256, 16, 2, 4},  // 5: eight waves, two per SIMD, 128×64 wave tiles
     {128, 128, 16, 2, 2, 2, 0, 1},  // 6: entry 0 with persistent workgroups
     {64, 64, 16, 2, 2, 0, 0, 1},    // 7: entry 1 with persistent workgroups
+    // 128×192 (64×96 per wave): whole rounds at the GPT-2 widths (768 → 256
+    // tiles at 8192 rows, so proj needs no K split), as for 16-bit inputs.
+    {128, 192, 16, 2, 2},           // 8
+    {128, 192, 32, 2, 2, 0, 0, 1},  // 9: persistent (32-deep slices leave a staging strip for every wave)
 };
 // 16-bit operands: v_mfma_f32_32x32x16_{f16,bf16}.  A slice of 32 elements
 // is only 256 MFMA cycles per wave, too short to hide one slice of load

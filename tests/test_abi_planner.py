@@ -307,8 +307,10 @@ def test_search_walks_every_tile_option():
     p.close()
     with pytest.raises(t.TlgError):
         t.Plan.create(512, 576, 768, "bf16", "bf16", "NK", variant=t.VARIANT_TILED, tile=tune.TILED_OPTIONS + 1)
+    p = t.Plan.create(512, 576, 768, "f32", "f32", "NK", variant=t.VARIANT_TILED, tile=10)  # fp32's last entry
+    p.close()
     with pytest.raises(t.TlgError):
-        t.Plan.create(512, 512, 512, "f32", "f32", "NK", variant=t.VARIANT_TILED, tile=9)
+        t.Plan.create(512, 576, 768, "f32", "f32", "NK", variant=t.VARIANT_TILED, tile=11)
 
 
 def test_wide_128x192_tiles_plan():

@@ -112,8 +112,8 @@ def test_stream_forced_split(pair, split):
 @pytest.mark.parametrize("layout", ["NK", "KN"])
 @pytest.mark.parametrize("epi", EPIS, ids=["none", "bias", "gelu", "bias+gelu"])
 def test_tiled(pair, layout, epi):
-    for tile in range(1, 9 if pair[0] == "f32" else 14):
-        if layout == "KN" and tile >= 12:  # 128×192 takes no [K][N] weight: the planner refuses it
+    for tile in range(1, 11 if pair[0] == "f32" else 14):
+        if layout == "KN" and tile >= (9 if pair[0] == "f32" else 12):  # 128×192 takes no [K][N] weight
             with pytest.raises(tlgemm.TlgError):
                 tlgemm.Plan.create(256, 384, 64, pair[0], pair[1], layout, variant=tlgemm.VARIANT_TILED, tile=tile)
             continue
@@ -212,11 +212,19 @@ def test_tiled_128x192():
         assert "tile=128x192x64" in desc, desc
         if split > 1 or K // 64 % 2:
             assert "persistent" not in desc, desc
+    # fp32 options 9 and 10 (128×192×16, and ×32 persistent): 24 runs per staged row
+    for (M, N, K), epi, res, tile, split in [((512, 576, 384), (True, True), False, 9, 1),
+                                             ((512, 576, 768), (True, False), True, 9, 2),
+                                             ((2048, 1536, 256), (True, True), False, 10, 1)]:
+        c = inputs.random_case(22, M, N, K, "f32", "f32", "NK", bias=epi[0], gelu=epi[1], residual=res)
+        _, desc = _check(c, variant=tlgemm.VARIANT_TILED, tile=tile, split_k=split)
+        assert "tile=128x192x" in desc and (("persistent" in desc) == (tile == 10)), desc
 
 
 def test_tiled_persistent_f32():
-    """fp32 persistent entries (options 7 and 8: 128x128x16 capped at two per CU, 64x64x16)."""
-    for tile, (M, N, K) in [(7, (4096, 4096, 64)), (8, (2048, 2048, 96))]:
+    """fp32 persistent entries (options 7 and 8: 128x128x16 capped at two per CU, 64x64x16; option 10:
+    128x192x32, whose staged epilogue rows hold 24 16-byte runs)."""
+    for tile, (M, N, K) in [(7, (4096, 4096, 64)), (8, (2048, 2048, 96)), (10, (4096, 3072, 128))]:
         c = inputs.random_case(20, M, N, K, "f32", "f32", "KN" if tile == 7 else "NK", bias=tile == 8, gelu=tile == 8)
         _, desc = _check(c, variant=tlgemm.VARIANT_TILED, tile=tile)
         assert "persistent" in desc, desc
