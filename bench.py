@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the transformer linear-layer GEMM on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--ramp-ms R] [--no-cpu-baseline]
 
 A step is one call of the library on the square fp32 GEMM C = A·B with
 M = N = K = 4096 and row-major A and B (warm operands).  Its throughput in
@@ -25,6 +25,12 @@ GPT-2-small layer at 8192 tokens (dX with the [K][N] weight layout, dW with the
 transposed first operand accumulated onto the previous gradient); LayerNorm and
 fused causal attention at GPT-2-small size; and the GPT-2-small forward through
 12 blocks composed from all of them (tokens/s).
+
+Every timed region is preceded by R milliseconds (default 300) of untimed
+back-to-back launches of its own work, then (for the square GEMMs) the W
+warmup steps: from idle the core clock needs tens of milliseconds of load to
+come up, and the bench measures the loaded clock (``clock_ramp_ms`` in the
+output line).
 
 The oracle (plain C, double accumulation) is timed on this host's cores on
 a bounded row sample of the square workload and reported as
@@ -52,7 +58,7 @@ METRIC = "TFLOP/s (% MFMA peak) @4096³ fp32; µs + HBM GB/s @16×4096×4096 fp1
 
 # Bytes each kernel moved between L2 and memory per launch, from rocprofv3
 # FETCH_SIZE and WRITE_SIZE passes over `bench.py --steps 3 --warmup 1
-# --narrow-launches 32 --no-cpu-baseline --no-parity --no-extra`, summarised
+# --narrow-launches 32 --no-cpu-baseline --no-parity --no-extra --ramp-ms 0`, summarised
 # by `bench.py --pmc-summary` (the HBM-traffic profile under profiles/).
 # FETCH_SIZE is scaled by 1.998 and WRITE_SIZE by 1.0: the factors that make
 # the same counters read 32 MiB for the run's 32 MiB device-to-device copies.
@@ -60,8 +66,8 @@ METRIC = "TFLOP/s (% MFMA peak) @4096³ fp32; µs + HBM GB/s @16×4096×4096 fp1
 # after a change to either the figure no longer applies and the bench reports null.
 FETCH_SCALE, WRITE_SCALE = 1.998, 1.0
 TRAFFIC = {
-    "tiled_f32": {"sources": ("common.h", "tiled.h"), "sha": "ed7fc7931b9ec7ca",
-                  "tile": "256x256x16", "fetch_kib": 196687.0, "write_kib": 65536.0},
+    "tiled_f32": {"sources": ("common.h", "tiled.h"), "sha": "bc1d84a98f036bd5",
+                  "tile": "256x256x16", "fetch_kib": 196685.0, "write_kib": 65536.0},
     "stream_f16": {"sources": ("common.h", "stream.h"), "sha": "24a261f043cb0dae",
                    "tile": "16x16x4096", "fetch_kib": 16916.5, "write_kib": 128.0},
 }
@@ -114,6 +120,36 @@ def read_clocks(torch):
     except Exception:
         return None
     return None
+
+
+RAMP_MS = 300.0  # default --ramp-ms
+
+
+def ramp(fn, stream, min_ms: float = None) -> float:
+    """Run ``fn(i)`` back to back, untimed, until at least ``min_ms`` of GPU time has passed; returns that time.
+
+    From idle (the host generating inputs, the oracle checking a sample) the
+    core clock takes tens of milliseconds of load to come up: the square bf16
+    4096³ GEMM measured 133–137 µs per launch after 10 launches from a
+    second of idle and 112 µs after 400 (fp32: 936–945 against 915–918 µs).
+    Every timed region of this bench is preceded by such a ramp of its own
+    work, so that it measures the loaded clock, as a busy GPU runs.
+    """
+    import torch
+
+    min_ms = RAMP_MS if min_ms is None else min_ms
+    spent, n, i = 0.0, 1, 0
+    while spent < min_ms:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            fn(i)
+            i += 1
+        b.record(stream)
+        torch.cuda.synchronize()
+        spent += a.elapsed_time(b)
+        n = min(2 * n, 4096)
+    return spent
 
 
 def time_launches(fn, n: int, stream) -> float:
@@ -299,8 +335,7 @@ def bench_ceilings(torch, dev, stream, cold_bufs):
     def read(buf):
         ok(lib.tlg_ceil_read(vp(buf.data_ptr()), ctypes.c_size_t(nbytes), vp(sink.data_ptr()), s))
 
-    for i in range(4 * len(cold_bufs)):
-        read(cold_bufs[i % len(cold_bufs)])
+    ramp(lambda i: read(cold_bufs[i % len(cold_bufs)]), stream)
     cold_ms = time_launches(lambda i: read(cold_bufs[i % len(cold_bufs)]), 2000, stream)
     warm_ms = time_launches(lambda i: read(cold_bufs[0]), 2000, stream)
     mfma, clock_mhz = {}, {}
@@ -309,7 +344,7 @@ def bench_ceilings(torch, dev, stream, cold_bufs):
     ok(lib.tlg_ceil_wall_clock_khz(ctypes.byref(khz)))
     for name, bf16, iters, flop in (("f32", 0, 2000, 4096), ("bf16", 1, 4000, 32768)):
         call = lambda i: ok(lib.tlg_ceil_mfma_clock(bf16, 256, iters, vp(sink.data_ptr()), vp(stamps.data_ptr()), s))
-        call(0)
+        ramp(call, stream)
         ms = time_launches(call, 10, stream)
         mfma[name] = 256 * 4 * iters * 16 * flop / (ms * 1e-3) / 1e12
         st = stamps.view(256, 4).cpu().numpy().astype(np.float64)  # the last launch's counters
@@ -347,8 +382,7 @@ def bench_c1(torch, dev, stream, no_parity: bool):
     if not no_parity:
         ref = oracle.linear_case(c)
         err = float(np.max(np.abs(host_f64(torch, Y) - ref)) / np.max(np.abs(ref)))
-    for i in range(256):
-        run(copies[i % len(copies)])
+    ramp(lambda i: run(copies[i % len(copies)]), stream)
     cold = time_launches(lambda i: run(copies[i % len(copies)]), 1024, stream)
     warm = time_launches(lambda i: run(W0), 1024, stream)
     return {"workload": "fp32 linear Y=X.W^T+b, M=128, K=768, N=768, W out x in, N(0,1)/N(0,0.02)",
@@ -386,6 +420,7 @@ def bench_c3(torch, dev, stream, no_parity: bool, copies: int = 12):
     torch.cuda.synchronize()
     for g in gemms:
         c = g["case"]
+        ramp(lambda i: run(g, g["Ws"][0]), stream)
         err = None
         if not no_parity:
             ref = oracle.linear_case(c)
@@ -400,8 +435,7 @@ def bench_c3(torch, dev, stream, no_parity: bool, copies: int = 12):
         for g in gemms:
             run(g, g["Ws"][l % copies])
 
-    for l in range(2 * copies):
-        layer(l)
+    ramp(layer, stream)
     warm = time_launches(lambda i: layer(0), 256, stream)
     cold = time_launches(lambda i: layer(i), 256, stream)
     flops = sum(g["case"].flops for g in gemms)
@@ -459,8 +493,7 @@ def bench_c5(torch, dev, stream, dtype: str, no_parity: bool, layers: int = 12, 
             case = inputs.LinearCase(name, M, N, K, dtype, dtype, "NK", True, gelu,
                                      inputs.gpt2_activation(w, 0, g, M, dtype), Wh, bh)
             errs[name] = sampled_parity(case, host_f64(torch, ys[g]), npts=1000)
-    for _ in range(3):
-        one_pass()
+    ramp(lambda i: one_pass(), stream)
     ms = median_span_ms(torch, one_pass, reps, stream)
     graph_ms, graph_same = graph_span_ms(torch, one_pass, reps, ys)
     flops = layers * sum(2 * M * N * K for _, N, K, _ in inputs.GPT2_LINEARS)
@@ -526,8 +559,7 @@ def bench_backward(torch, dev, stream, dtype: str, no_parity: bool, reps: int = 
                 errs[f"{name}.{key}"] = float(np.max(np.abs(y[mi, ni] - ref)) / np.max(np.abs(ref)))
         for name, dx, dw, d, outs, wss, _ in jobs:  # back to the initial gradients for timing
             outs["dW"].copy_(d["G"])
-    for _ in range(2):
-        one_pass()
+    ramp(lambda i: one_pass(), stream)
     ms = median_span_ms(torch, one_pass, reps, stream)
     flops = sum(2 * 2 * T * N * K for _, N, K, _ in inputs.GPT2_LINEARS)
     return {"workload": f"GPT-2-small backward GEMMs at {T} tokens, one layer: dX = dY.W ([K][N] weight) and "
@@ -566,6 +598,7 @@ def bench_layer_ops(torch, dev, stream, dtype: str, no_parity: bool, reps: int =
             ("attention_b64_t128_h12", att, B * T * 4 * NH * HS * es, 4 * B * NH * HS * T * (T + 1) // 2)):
         fn()
         torch.cuda.synchronize()
+        ramp(lambda i: fn(), stream)
         us = time_launches(lambda i: fn(), reps, stream) * 1e3
         r = {"us": round(us, 3), "GB/s": round(nbytes / us / 1e3, 1),
              "roofline": {"bound": "hbm", "achieved": round(nbytes / us / 1e3, 1), "peak": PEAK_HBM_GBS,
@@ -632,8 +665,7 @@ def bench_gpt2_forward(torch, dev, stream, dtype: str, no_parity: bool, layers: 
         for blk in blocks:
             blk.forward(x, stream.cuda_stream)
 
-    for _ in range(2):
-        one_pass()
+    ramp(lambda i: one_pass(), stream)
     ms = median_span_ms(torch, one_pass, reps, stream)
     # the same pass captured once in a HIP graph, starting from a device copy of the input
     xin = dev_tensor(torch, x0, dtype, dev)
@@ -668,8 +700,10 @@ def rocprof_summary(outdir: str, segments: list[str]) -> str:
     tiles or grids are never pooled.  The library's kernels and the ceiling
     probes only: torch's and the HIP runtime's own kernels are left out.  ``segments`` entries ``NAME@GRID=n1,n2,...``
     split that row's launches, in dispatch order, into consecutive runs of
-    n1, n2, ... launches (for example the parity call, the cold launches and
-    the warm launches of one kernel), each summarised on its own.
+    n1, n2, ... launches (for example the parity call, the clock ramp, the
+    cold launches and the warm launches of one kernel), each summarised on its
+    own; one ``*`` stands for however many launches the other runs leave (the
+    ramp's count depends on the clock).
     """
     import csv
 
@@ -705,8 +739,12 @@ def rocprof_summary(outdir: str, segments: list[str]) -> str:
         key, counts = spec.rsplit("=", 1)
         name, grid = key.rsplit("@", 1)
         v = sorted(groups.get((name, grid), []))
-        sizes = [int(c) for c in counts.split(",")]
-        if sum(sizes) != len(v):
+        parts = counts.split(",")
+        if parts.count("*") > 1:
+            raise SystemExit(f"{spec}: at most one '*' run")
+        fixed = sum(int(c) for c in parts if c != "*")
+        sizes = [len(v) - fixed if c == "*" else int(c) for c in parts]  # '*': the launches the others leave
+        if sum(sizes) != len(v) or min(sizes) < 0:
             raise SystemExit(f"{name}@{grid}: {len(v)} launches in the trace, segments sum to {sum(sizes)}")
         out += [f"`{short(name)}` at grid {grid}, launches in dispatch order split into runs of {counts}:", "",
                 "| run | launches | median µs | p10 µs | p90 µs |", "|---|---|---|---|---|"]
@@ -777,11 +815,75 @@ def pmc_summary(fetch_dir: str, write_dir: str, kernels: list[str]) -> str:
     return "\n".join(lines)
 
 
+def counter_summary(dirs: list[str], kernels: list[str]) -> str:
+    """Markdown table of per-dispatch counter medians from ``rocprofv3 --pmc`` runs (any counters).
+
+    ``kernels`` entries ``NAME@GRID`` name the rows.  GRBM_GUI_ACTIVE reads
+    the busy cycles of the 8 XCDs summed: over 8 it is the kernel's length in
+    core-clock cycles, and over the kernel's median duration in the same run's
+    kernel trace, its core clock.  Where the run holds them, derived columns
+    follow: that clock; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES over the 1024
+    SIMDs times the kernel's cycles; the LDS bank-conflict share =
+    SQ_LDS_BANK_CONFLICT over SQ_LDS_IDX_ACTIVE.
+    """
+    import csv
+
+    vals: dict = {}
+    durs: dict = {}
+    for d in dirs:
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path, newline="") as f:
+                for row in csv.DictReader(f):
+                    wg = max(int(row["Workgroup_Size"]), 1)
+                    key = (row["Kernel_Name"], f"{int(row['Grid_Size']) // wg}x1x1")
+                    vals.setdefault(key, {}).setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+        for path in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+            with open(path, newline="") as f:
+                for row in csv.DictReader(f):
+                    key = (row["Kernel_Name"], f"{row['Grid_Size_X']}x{row['Grid_Size_Y']}x{row['Grid_Size_Z']}")
+                    wg = (max(int(row["Workgroup_Size_X"]), 1), max(int(row["Workgroup_Size_Y"]), 1),
+                          max(int(row["Workgroup_Size_Z"]), 1))
+                    grid = tuple(int(row[f"Grid_Size_{a}"]) // w for a, w in zip("XYZ", wg))
+                    if grid[1:] == (1, 1):
+                        durs.setdefault((row["Kernel_Name"], f"{grid[0]}x1x1"), []).append(
+                            (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) * 1e-9)
+    names = sorted({c for v in vals.values() for c in v})
+    xcds, simds = 8, 1024
+    derived = []
+    if "GRBM_GUI_ACTIVE" in names:
+        derived.append(("core MHz", lambda m, t: m["GRBM_GUI_ACTIVE"] / xcds / t / 1e6 if t else float("nan")))
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in names and "GRBM_GUI_ACTIVE" in names:
+        derived.append(("MFMA busy",
+                        lambda m, t: m["SQ_VALU_MFMA_BUSY_CYCLES"] / (m["GRBM_GUI_ACTIVE"] / xcds * simds)))
+    if "SQ_LDS_BANK_CONFLICT" in names and "SQ_LDS_IDX_ACTIVE" in names:
+        derived.append(("LDS conflict share",
+                        lambda m, t: m["SQ_LDS_BANK_CONFLICT"] / max(m["SQ_LDS_IDX_ACTIVE"], 1.0)))
+    lines = ["| kernel | grid | dispatches | median µs | " + " | ".join(names + [d[0] for d in derived]) + " |",
+             "|---|---|---|---|" + "---|" * (len(names) + len(derived))]
+    for spec in kernels:
+        name, grid = spec.rsplit("@", 1)
+        ks = [k for k in vals if k[0].startswith(name) and k[1] == grid]
+        if len(ks) != 1:
+            raise SystemExit(f"{name}@{grid}: {len(ks)} matching kernels in the counter runs")
+        v = vals[ks[0]]
+        med = {c: float(np.median(v[c])) for c in v}
+        shown = ks[0][0][:ks[0][0].rindex("(")] if ks[0][0].endswith(")") else ks[0][0]
+        t = float(np.median(durs[ks[0]])) if ks[0] in durs else 0.0
+        cells = [f"{med[c]:.4g}" if c in med else "" for c in names]
+        cells += [f"{fn(med, t):.3f}" if all(c in med for c in names) else "" for _, fn in derived]
+        lines.append(f"| `{shown}` | {grid} | {max(len(x) for x in v.values())} | {t * 1e6:.2f} | "
+                     + " | ".join(cells) + " |")
+    return "\n".join(lines)
+
+
 def main(argv=None) -> int:
+    global RAMP_MS
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50, help="timed square-GEMM steps")
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--ramp-ms", type=float, default=RAMP_MS,
+                    help="untimed back-to-back work before each timed region, in GPU milliseconds (clock ramp)")
     ap.add_argument("--narrow-launches", type=int, default=2000, help="timed cold narrow launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
@@ -789,16 +891,23 @@ def main(argv=None) -> int:
                     help="skip the ceiling probes and the 128-row layer and M=8192 stack workloads")
     ap.add_argument("--rocprof-summary", metavar="DIR",
                     help="print a markdown summary of a rocprofv3 kernel-trace run under DIR and exit (no GPU)")
+    ap.add_argument("--counter-summary", nargs="+", metavar="DIR",
+                    help="print per-dispatch counter medians of rocprofv3 --pmc runs under the DIRs and exit (no GPU)")
     ap.add_argument("--segment", action="append", default=[], metavar="NAME@GRID=n1,n2,...",
                     help="with --rocprof-summary: split one kernel's launches into consecutive runs")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print HBM bytes per launch from FETCH_SIZE / WRITE_SIZE rocprofv3 runs and exit (no GPU)")
     ap.add_argument("--kernel", action="append", default=[], metavar="NAME@GRID=BYTES",
-                    help="with --pmc-summary: a kernel row to report, with its algorithmic bytes per launch")
+                    help="with --pmc-summary: a kernel row to report, with its algorithmic bytes per launch; "
+                         "with --counter-summary: NAME@GRID")
     args = ap.parse_args(argv)
+    RAMP_MS = args.ramp_ms
 
     if args.pmc_summary:
         print(pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.kernel))
+        return 0
+    if args.counter_summary:
+        print(counter_summary(args.counter_summary, args.kernel))
         return 0
     if args.rocprof_summary:
         print(rocprof_summary(args.rocprof_summary, args.segment))
@@ -842,6 +951,7 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     sq_err = None if args.no_parity else sampled_parity(sq, to_f64(C))
     log(f"square fp32: {plan.describe()} parity {sq_err}")
+    ramp(run_sq, stream, args.ramp_ms)
     for i in range(args.warmup):
         run_sq(i)
     ms = time_launches(run_sq, args.steps, stream)
@@ -856,6 +966,7 @@ def main(argv=None) -> int:
     run_sqb(0)
     torch.cuda.synchronize()
     sqb_err = None if args.no_parity else sampled_parity(sqb, to_f64(C))
+    ramp(run_sqb, stream, args.ramp_ms)
     for i in range(args.warmup):
         run_sqb(i)
     msb = time_launches(run_sqb, args.steps, stream)
@@ -877,8 +988,7 @@ def main(argv=None) -> int:
     run_n(0)
     torch.cuda.synchronize()
     n_err = None if args.no_parity else sampled_parity(nc, to_f64(Y))
-    for i in range(COLD_COPIES * 4):
-        run_n(i)
+    ramp(run_n, stream, args.ramp_ms)
     n_ms = time_launches(run_n, args.narrow_launches, stream)
     warm_ms = time_launches(lambda i: run_n(0), args.narrow_launches, stream)
     n_bytes = nc.M * nc.K * 2 + nc.N * nc.K * 2 + nc.M * nc.N * 2
@@ -936,6 +1046,7 @@ def main(argv=None) -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_ramp_ms": args.ramp_ms,
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
