@@ -66,12 +66,15 @@ __device__ inline float wave_sum(float x) {
 // over the values, one read of the row); no LDS, no barrier.
 constexpr int kLnMaxPerLane = 64;  // values a lane holds: C <= 64 * 64
 
-template <int DT, int VE, int R>
+// NVMAX: VE-wide vectors a lane holds per row, the smallest of the
+// instantiated counts that covers C (the host picks it), so that the row and
+// the gamma and beta vectors stay in registers at full occupancy.
+template <int DT, int VE, int R, int NVMAX>
 __global__ __launch_bounds__(256) void layernorm_kernel(const void* __restrict__ X, const void* __restrict__ gamma,
                                                         const void* __restrict__ beta, void* __restrict__ Y,
                                                         float* __restrict__ mean_out, float* __restrict__ rstd_out,
                                                         int64_t rows, int C, float eps) {
-    constexpr int NVMAX = kLnMaxPerLane / (VE * R);
+    static_assert(NVMAX * VE * R <= kLnMaxPerLane, "values a lane holds");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t row0 = ((int64_t)blockIdx.x * 4 + wave) * R;
     float v[R][NVMAX][VE];
@@ -82,6 +85,17 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const void* __restrict__
             const int e = (lane + 64 * j) * VE;
             if (row0 + r < rows && e < C) load_vec<DT, VE>(X, (row0 + r) * C + e, v[r][j]);
         }
+    // gamma and beta do not depend on the row: their loads go out with the
+    // rows', not after the statistics (a second memory round trip)
+    float gv[NVMAX][VE], bv[NVMAX][VE];
+#pragma unroll
+    for (int j = 0; j < NVMAX; ++j) {
+        const int e = (lane + 64 * j) * VE;
+        if (e < C) {
+            load_vec<DT, VE>(gamma, e, gv[j]);
+            load_vec<DT, VE>(beta, e, bv[j]);
+        }
+    }
     const float inv_c = 1.0f / (float)C;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -108,11 +122,9 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const void* __restrict__
         for (int j = 0; j < NVMAX; ++j) {
             const int e = (lane + 64 * j) * VE;
             if (e < C) {
-                float g[VE], b[VE], y[VE];
-                load_vec<DT, VE>(gamma, e, g);
-                load_vec<DT, VE>(beta, e, b);
+                float y[VE];
 #pragma unroll
-                for (int u = 0; u < VE; ++u) y[u] = (v[r][j][u] - mu) * rs * g[u] + b[u];
+                for (int u = 0; u < VE; ++u) y[u] = (v[r][j][u] - mu) * rs * gv[j][u] + bv[j][u];
                 store_vec<DT, VE>(Y, row * C + e, y);
             }
         }
@@ -480,24 +492,43 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     return x < y + nb && y < x + na;
 }
 
-template <int DT, int VE, int R>
+template <int DT, int VE, int R, int NV>
 int launch_layernorm(const void* X, const void* g, const void* b, void* Y, float* mean, float* rstd, int64_t rows,
                      int C, float eps, hipStream_t s) {
     const int64_t grid = (rows + 4 * R - 1) / (4 * R);
-    hipLaunchKernelGGL((layernorm_kernel<DT, VE, R>), dim3((unsigned)grid), dim3(256), 0, s, X, g, b, Y, mean, rstd,
-                       rows, C, eps);
+    hipLaunchKernelGGL((layernorm_kernel<DT, VE, R, NV>), dim3((unsigned)grid), dim3(256), 0, s, X, g, b, Y, mean,
+                       rstd, rows, C, eps);
     return check_launch("layernorm_kernel");
 }
 
-// Rows per wave: two where the 64 values a lane holds allow it.  Measured at
+// Rows per wave: two where the values a lane holds allow it.  Measured at
 // 8192 x 768: one row per wave 10.2 / 9.4 us (fp32 / bf16), two 9.8 / 8.6 us,
 // four 11.1 / 10.7 us (more loads in flight per wave, but half the waves).
+// Vectors per lane per row: the smallest of 1, 2, 3, 4, 8, 16, 32, 64 that
+// covers the row.
 template <int DT, int VE>
 int layernorm_ve(const void* X, const void* g, const void* b, void* Y, float* mean, float* rstd, int64_t rows, int C,
                  float eps, hipStream_t s) {
-    const int per_row = (C + 64 * VE - 1) / (64 * VE) * VE;  // values per lane per row
-    if (per_row * 2 <= kLnMaxPerLane) return launch_layernorm<DT, VE, 2>(X, g, b, Y, mean, rstd, rows, C, eps, s);
-    return launch_layernorm<DT, VE, 1>(X, g, b, Y, mean, rstd, rows, C, eps, s);
+    const int need = (C + 64 * VE - 1) / (64 * VE);  // vectors per lane per row
+    auto go = [&](auto nvc) -> int {
+        constexpr int NV = decltype(nvc)::value;
+        if constexpr (NV * VE > kLnMaxPerLane) {
+            return (int)TLG_ERR_UNSUPPORTED;  // not reached: C <= 64 * kLnMaxPerLane is checked by the caller
+        } else {
+            if constexpr (2 * NV * VE <= kLnMaxPerLane)
+                return launch_layernorm<DT, VE, 2, NV>(X, g, b, Y, mean, rstd, rows, C, eps, s);
+            else
+                return launch_layernorm<DT, VE, 1, NV>(X, g, b, Y, mean, rstd, rows, C, eps, s);
+        }
+    };
+    if (need <= 1) return go(std::integral_constant<int, 1>{});
+    if (need <= 2) return go(std::integral_constant<int, 2>{});
+    if (need <= 3) return go(std::integral_constant<int, 3>{});
+    if (need <= 4) return go(std::integral_constant<int, 4>{});
+    if (need <= 8) return go(std::integral_constant<int, 8>{});
+    if (need <= 16) return go(std::integral_constant<int, 16>{});
+    if (need <= 32) return go(std::integral_constant<int, 32>{});
+    return go(std::integral_constant<int, 64>{});
 }
 
 template <int DT>
