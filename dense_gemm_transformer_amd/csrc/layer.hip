@@ -136,12 +136,17 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const void* __restrict__
 }
 
 // ---- fused causal attention ------------------------------------------------------------
-// One workgroup per (batch, head) with four waves.  The head's keys and
-// values go to LDS once (values transposed, [dimension][key]).  Queries come
-// in blocks of 16 rows; with causality block q needs q + 1 key blocks of 16,
-// so wave w takes blocks w and 7 - w of every group of eight: 9 key blocks
-// per wave at T = 128, the same on every wave (and on every SIMD).  For each
-// key block up to the query block (causality as a loop bound):
+// One workgroup per (batch, head) with four waves.  Queries come in blocks of
+// 16 rows; with causality block q needs q + 1 key blocks of 16, so wave w
+// takes blocks w and 7 - w of every group of eight: 9 key blocks per wave at
+// T = 128, the same on every wave (and on every SIMD).  The head's keys and
+// values pass through LDS in chunks of 64 keys (values transposed,
+// [dimension][key]); each wave keeps the running state of both its query
+// blocks in registers across the chunks.  The chunk keeps a workgroup's LDS
+// at 37 KiB whatever T is, so three workgroups share a CU and the 768 heads
+// of B 64 × 12 run in one round (with the head's whole K and V resident, 69
+// KiB, two fitted and they took one and a half).  For each key block up to
+// the query block (causality as a loop bound), in key order:
 //  * S = Q Kᵀ on v_mfma_f32_16x16x4_f32: lane group kk holds dimensions
 //    16kk .. 16kk+15 of its query row (in registers, pre-scaled by
 //    log2(e)/sqrt(64)) and of its key row (four 16-byte LDS reads); the same
@@ -159,11 +164,11 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const void* __restrict__
 // The row sums meet at the end the same way.
 //
 // LDS layouts, XOR-swizzled so that the reads are conflict-free: key row j
-// holds its sixteen 16-byte chunks at chunk ^ (j % 16); transposed value
-// row d holds its four-key chunks at chunk ^ (d % 16); the score tile has a
-// row stride of 20 floats.  Value columns past T (up to the next multiple of
-// 16) are zero, so masked keys (p = 0) multiply finite values.
-constexpr int kHeadSize = 64, kKeyBlock = 32;
+// of a chunk holds its sixteen 16-byte chunks at chunk ^ (j % 16); transposed
+// value row d holds its four-key chunks at chunk ^ (d % 16); the score tile
+// has a row stride of 20 floats.  Keys and values past T are loaded as zero,
+// so masked keys (p = 0) multiply finite values.
+constexpr int kHeadSize = 64, kKeyBlock = 32, kKeyChunk = 64;
 
 // 16-byte loads each thread keeps in flight while filling the key and value tiles.
 constexpr int kLoadGroup = 8;
@@ -175,146 +180,181 @@ template <int TMAX> __device__ inline int vt_at(int d, int key) {
 }
 constexpr int kTile16 = 20;  // row stride of the 16×16 score tile (floats)
 
+// The running state of one 16-row query block (its query rows are re-read
+// from memory, an L2 hit, for each chunk: holding both blocks' would spill).
+struct QBlock {
+    f32x4 o[4];   // output tiles, dimensions 16dt .. 16dt+15
+    float m, lp;  // running maximum and this lane's part of the row sum
+    int q0, myrow;
+    bool on;      // the block exists (wave-uniform)
+};
+
 template <int DT, bool CAUSAL, int TMAX>
-__global__ __launch_bounds__(256) void attention_kernel(const void* __restrict__ qkv, void* __restrict__ out,
-                                                        float* __restrict__ lse, int T, int NH) {
-    constexpr int HS = kHeadSize;
+__global__ __launch_bounds__(256, TMAX <= 128 ? 3 : 1) void attention_kernel(const void* __restrict__ qkv,
+                                                                            void* __restrict__ out,
+                                                                            float* __restrict__ lse, int T, int NH) {
+    // Up to 128 keys, chunks of 64 (three workgroups per CU); beyond, the
+    // whole head stays resident: with few heads per CU there is no occupancy
+    // to win, and chunks there measured slower (B 16, T 256: 50.9 vs 43.6 µs).
+    constexpr int HS = kHeadSize, KC = TMAX <= 128 ? kKeyChunk : TMAX;
     constexpr int EPV = Elem<DT>::per16;  // elements per 16-byte vector
     static_assert(EPV == 4, "the fp32 kernel");
-    __shared__ __attribute__((aligned(16))) float Ks[TMAX * HS];
-    __shared__ __attribute__((aligned(16))) float Vt[HS * TMAX];
+    static_assert(TMAX % KC == 0, "whole chunks");
+    constexpr int VPR = HS / EPV;  // 16-byte vectors per row
+    static_assert((2 * KC * VPR) % (256 * kLoadGroup) == 0, "whole rounds of loads fill a chunk");
+    __shared__ __attribute__((aligned(16))) float Ks[KC * HS];
+    __shared__ __attribute__((aligned(16))) float Vt[HS * KC];
     __shared__ __attribute__((aligned(16))) float Ps[4 * 16 * kTile16];
     const int bh = blockIdx.x, b = bh / NH, h = bh % NH;
     const int64_t C = (int64_t)NH * HS, C3 = 3 * C;
     const int64_t head = (int64_t)b * T * C3 + (int64_t)h * HS;  // q of row 0 of this head
-
-    // Keys and values, 16-byte vectors: each thread has kLoadGroup loads in
-    // flight before it stores any of them (one load, wait, store per vector
-    // would chain the memory latency kLoadGroup times).  Value columns T ..
-    // Tz-1 of the transposed copy are written as zeros.
-    constexpr int VPR = HS / EPV;  // 16-byte vectors per row
-    const int Tz = (T + 15) / 16 * 16;
-    const int nvec = (T + Tz) * VPR;
-    for (int base = threadIdx.x; base < nvec; base += 256 * kLoadGroup) {
-        float f[kLoadGroup][EPV];
-#pragma unroll
-        for (int i = 0; i < kLoadGroup; ++i) {
-            const int idx = base + 256 * i;
-            const bool isv = idx >= T * VPR;
-            const int rem = isv ? idx - T * VPR : idx, j = rem / VPR, c0 = (rem % VPR) * EPV;
-#pragma unroll
-            for (int u = 0; u < EPV; ++u) f[i][u] = 0.0f;
-            if (idx < nvec && j < T)
-                load_vec<DT, EPV>(qkv, head + (int64_t)j * C3 + (isv ? 2 : 1) * C + c0, f[i]);
-        }
-#pragma unroll
-        for (int i = 0; i < kLoadGroup; ++i) {
-            const int idx = base + 256 * i;
-            if (idx >= nvec) continue;
-            const bool isv = idx >= T * VPR;
-            const int rem = isv ? idx - T * VPR : idx, j = rem / VPR, c0 = (rem % VPR) * EPV;
-            if (isv) {
-#pragma unroll
-                for (int u = 0; u < EPV; ++u) Vt[vt_at<TMAX>(c0 + u, j)] = f[i][u];
-            } else {
-                *reinterpret_cast<f32x4*>(Ks + k_at(j, c0 >> 2)) = f32x4{f[i][0], f[i][1], f[i][2], f[i][3]};
-            }
-        }
-    }
-    __syncthreads();
-
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, c16 = lane & 15, kk = lane >> 4;
     float* P = Ps + wave * 16 * kTile16;
     const float qscale = 1.4426950408889634f / 8.0f;  // log2(e) / sqrt(64)
     const int nqb = (T + 15) / 16;
+
+    // One key block of 16 (keys j0 .. j0+15, the chunk starting at key c0) into a query block's state.
+    auto step = [&](QBlock& st, const float* q, int j0, int c0) {
+        // S: key row j0 + c16 (rows past T are zero; their scores are masked below)
+        const int kl = j0 - c0 + c16;
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const f32x4 kv = *reinterpret_cast<const f32x4*>(Ks + k_at(kl, 4 * kk + t));
+            s0 = mfma16_f32(q[4 * t], kv[0], s0);
+            s1 = mfma16_f32(q[4 * t + 1], kv[1], s1);
+            s0 = mfma16_f32(q[4 * t + 2], kv[2], s0);
+            s1 = mfma16_f32(q[4 * t + 3], kv[3], s1);
+        }
+        // accumulator layout (key c16, rows 4kk + e) -> operand layout (row c16, keys 4kk ..
+        // 4kk+3).  LDS operations of one wave complete in issue order; the empty asm
+        // statements keep the compiler from reordering these accesses across each other.
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int e = 0; e < 4; ++e) P[(4 * kk + e) * kTile16 + c16] = s0[e] + s1[e];
+        const f32x4 sv = *reinterpret_cast<const f32x4*>(P + c16 * kTile16 + 4 * kk);
+        asm volatile("" ::: "memory");
+        float p[4] = {sv[0], sv[1], sv[2], sv[3]};
+        float bm = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int key = j0 + 4 * kk + u;
+            const bool keep = key < T && st.myrow < T && (!CAUSAL || key <= st.myrow);
+            p[u] = keep ? p[u] : -INFINITY;
+            bm = fmaxf(bm, p[u]);
+        }
+        bm = fmaxf(bm, __shfl_xor(bm, 16, 64));  // the row's other key groups
+        bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+        const float mn = fmaxf(st.m, bm);
+        const float ms = mn == -INFINITY ? 0.0f : mn;  // a row with nothing visible yet stays at zero
+        const float corr = __builtin_amdgcn_exp2f(st.m - ms);
+        st.m = mn;
+        float ps = 0.0f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            p[u] = __builtin_amdgcn_exp2f(p[u] - ms);
+            ps += p[u];
+        }
+        st.lp = st.lp * corr + ps;
+        // rescaling factors of the accumulator rows 4kk + e (held by lanes 4kk + e of group 0)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float ce = __shfl(corr, 4 * kk + e, 64);
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) st.o[dt][e] *= ce;
+        }
+        // O += P V: keys j0 + 4kk + u, dimensions 16dt + c16 of the value tile
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+            const f32x4 vv = *reinterpret_cast<const f32x4*>(Vt + vt_at<KC>(16 * dt + c16, j0 - c0 + 4 * kk));
+#pragma unroll
+            for (int u = 0; u < 4; ++u) st.o[dt] = mfma16_f32(p[u], vv[u], st.o[dt]);
+        }
+    };
+
+    QBlock blk[2];
+    int resident = -1;  // first key of the chunk in LDS
     for (int group = 0; group < nqb; group += 8) {
+#pragma unroll
         for (int half = 0; half < 2; ++half) {
+            QBlock& st = blk[half];
             const int qblk = group + (half ? 7 - wave : wave);
-            if (qblk >= nqb) continue;  // wave-uniform
-            const int q0 = qblk * 16;
-            const int myrow = q0 + c16;  // this lane's row in the operand layout
-            float q[16];                 // dimensions 16kk .. 16kk+15 of row myrow
+            st.on = qblk < nqb;
+            st.q0 = qblk * 16;
+            st.myrow = st.q0 + c16;  // this lane's row in the operand layout
 #pragma unroll
-            for (int c = 0; c < 16; c += EPV)
-                load_vec<DT, EPV>(qkv, head + (int64_t)min(myrow, T - 1) * C3 + 16 * kk + c, q + c);
+            for (int dt = 0; dt < 4; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            st.m = -INFINITY;
+            st.lp = 0.0f;
+        }
+        // keys the group needs (workgroup-uniform, so every wave meets every barrier)
+        const int gend = CAUSAL ? min(T, (group + 8) * 16) : T;
+        for (int c0 = 0; c0 < gend; c0 += KC) {
+            if (c0 != resident) {  // workgroup-uniform: a chunk that holds all of T is loaded once
+                __syncthreads();  // the previous chunk's reads are done
+                for (int base = threadIdx.x; base < 2 * KC * VPR; base += 256 * kLoadGroup) {
+                    // keys c0 .. c0+KC-1 and their values, 16-byte vectors: each thread has its kLoadGroup
+                    // loads in flight before it stores any of them
+                    float f[kLoadGroup][EPV];
 #pragma unroll
-            for (int c = 0; c < 16; ++c) q[c] *= qscale;
-            f32x4 o[4];
+                    for (int i = 0; i < kLoadGroup; ++i) {
+                        const int idx = base + 256 * i;
+                        const bool isv = idx >= KC * VPR;
+                        const int rem = isv ? idx - KC * VPR : idx, j = rem / VPR, c = (rem % VPR) * EPV;
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            float m = -INFINITY, lp = 0.0f;  // running maximum and this lane's part of the row sum
-            const int kend = CAUSAL ? min(T, q0 + 16) : T;
-            for (int j0 = 0; j0 < kend; j0 += 16) {
-                // S: key row j0 + c16 (rows past T hold stale values; their scores are masked below)
-                const int kr = j0 + c16;
-                f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+                        for (int u = 0; u < EPV; ++u) f[i][u] = 0.0f;
+                        if (c0 + j < T)
+                            load_vec<DT, EPV>(qkv, head + (int64_t)(c0 + j) * C3 + (isv ? 2 : 1) * C + c, f[i]);
+                    }
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const f32x4 kv = *reinterpret_cast<const f32x4*>(Ks + k_at(kr, 4 * kk + t));
-                    s0 = mfma16_f32(q[4 * t], kv[0], s0);
-                    s1 = mfma16_f32(q[4 * t + 1], kv[1], s1);
-                    s0 = mfma16_f32(q[4 * t + 2], kv[2], s0);
-                    s1 = mfma16_f32(q[4 * t + 3], kv[3], s1);
+                    for (int i = 0; i < kLoadGroup; ++i) {
+                        const int idx = base + 256 * i;
+                        const bool isv = idx >= KC * VPR;
+                        const int rem = isv ? idx - KC * VPR : idx, j = rem / VPR, c = (rem % VPR) * EPV;
+                        if (isv) {
+#pragma unroll
+                            for (int u = 0; u < EPV; ++u) Vt[vt_at<KC>(c + u, j)] = f[i][u];
+                        } else {
+                            *reinterpret_cast<f32x4*>(Ks + k_at(j, c >> 2)) = f32x4{f[i][0], f[i][1], f[i][2], f[i][3]};
+                        }
+                    }
                 }
-                // accumulator layout (key c16, rows 4kk + e) -> operand layout (row c16, keys 4kk ..
-                // 4kk+3).  LDS operations of one wave complete in issue order; the empty asm
-                // statements keep the compiler from reordering these accesses across each other.
-                asm volatile("" ::: "memory");
-#pragma unroll
-                for (int e = 0; e < 4; ++e) P[(4 * kk + e) * kTile16 + c16] = s0[e] + s1[e];
-                const f32x4 sv = *reinterpret_cast<const f32x4*>(P + c16 * kTile16 + 4 * kk);
-                asm volatile("" ::: "memory");
-                float p[4] = {sv[0], sv[1], sv[2], sv[3]};
-                float bm = -INFINITY;
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int key = j0 + 4 * kk + u;
-                    const bool keep = key < T && myrow < T && (!CAUSAL || key <= myrow);
-                    p[u] = keep ? p[u] : -INFINITY;
-                    bm = fmaxf(bm, p[u]);
-                }
-                bm = fmaxf(bm, __shfl_xor(bm, 16, 64));  // the row's other key groups
-                bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-                const float mn = fmaxf(m, bm);
-                const float ms = mn == -INFINITY ? 0.0f : mn;  // a row with nothing visible yet stays at zero
-                const float corr = __builtin_amdgcn_exp2f(m - ms);
-                m = mn;
-                float ps = 0.0f;
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    p[u] = __builtin_amdgcn_exp2f(p[u] - ms);
-                    ps += p[u];
-                }
-                lp = lp * corr + ps;
-                // rescaling factors of the accumulator rows 4kk + e (held by lanes 4kk + e of group 0)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float ce = __shfl(corr, 4 * kk + e, 64);
-#pragma unroll
-                    for (int dt = 0; dt < 4; ++dt) o[dt][e] *= ce;
-                }
-                // O += P V: keys j0 + 4kk + u, dimensions 16dt + c16 of the value tile
-#pragma unroll
-                for (int dt = 0; dt < 4; ++dt) {
-                    const f32x4 vv = *reinterpret_cast<const f32x4*>(Vt + vt_at<TMAX>(16 * dt + c16, j0 + 4 * kk));
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) o[dt] = mfma16_f32(p[u], vv[u], o[dt]);
-                }
+                __syncthreads();
+                resident = c0;
             }
-            float l = lp + __shfl_xor(lp, 16, 64);
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                QBlock& st = blk[half];
+                if (!st.on) continue;  // wave-uniform
+                const int kend = min(CAUSAL ? min(T, st.q0 + 16) : T, c0 + KC);
+                if (c0 >= kend) continue;
+                float q[16];  // dimensions 16kk .. 16kk+15 of row myrow, pre-scaled
+#pragma unroll
+                for (int c = 0; c < 16; c += EPV)
+                    load_vec<DT, EPV>(qkv, head + (int64_t)min(st.myrow, T - 1) * C3 + 16 * kk + c, q + c);
+#pragma unroll
+                for (int c = 0; c < 16; ++c) q[c] *= qscale;
+                for (int j0 = c0; j0 < kend; j0 += 16) step(st, q, j0, c0);
+            }
+        }
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            QBlock& st = blk[half];
+            if (!st.on) continue;
+            float l = st.lp + __shfl_xor(st.lp, 16, 64);
             l += __shfl_xor(l, 32, 64);
-            if (kk == 0 && lse && myrow < T)
-                lse[((int64_t)b * NH + h) * T + myrow] = (m + __builtin_amdgcn_logf(l)) * 0.6931471805599453f;
+            if (kk == 0 && lse && st.myrow < T)
+                lse[((int64_t)b * NH + h) * T + st.myrow] = (st.m + __builtin_amdgcn_logf(l)) * 0.6931471805599453f;
             const float inv = 1.0f / l;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float ie = __shfl(inv, 4 * kk + e, 64);
-                const int row = q0 + 4 * kk + e;
+                const int row = st.q0 + 4 * kk + e;
                 if (row < T) {
                     const int64_t orow = ((int64_t)b * T + row) * C + (int64_t)h * HS;
 #pragma unroll
                     for (int dt = 0; dt < 4; ++dt) {
-                        const float y = o[dt][e] * ie;
+                        const float y = st.o[dt][e] * ie;
                         store_vec<DT, 1>(out, orow + 16 * dt + c16, &y);
                     }
                 }
