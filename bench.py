@@ -152,6 +152,20 @@ def ramp(fn, stream, min_ms: float = None) -> float:
     return spent
 
 
+def l2_roofline(ceil, plan, case, ms: float) -> dict:
+    """The square GEMM against the on-chip read rate: every workgroup streams a BM-row panel of A and a BN-column
+    panel of B through its CU, so one launch moves es·K·(M·N/BN + N·M/BM) bytes from L2 to the CUs; that over
+    the launch time, against the rate of the ceiling probe that re-reads L2-resident blocks on every CU."""
+    if not ceil or "read_l2_GB/s" not in ceil:
+        return {}
+    i = plan.info
+    es = 4 if case.in_dtype == "f32" else 2
+    nbytes = es * case.K * (case.M * case.N // i.tile_n + case.N * case.M // i.tile_m)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"l2_to_cu": {"bytes_per_launch": nbytes, "GB/s": round(gbs, 1), "ceiling_GB/s": ceil["read_l2_GB/s"],
+                         "frac": round(gbs / ceil["read_l2_GB/s"], 4)}}
+
+
 def time_launches(fn, n: int, stream) -> float:
     """Average ms per call of ``fn(i)`` over n back-to-back calls, HIP events on ``stream``."""
     import torch
@@ -338,6 +352,14 @@ def bench_ceilings(torch, dev, stream, cold_bufs):
     ramp(lambda i: read(cold_bufs[i % len(cold_bufs)]), stream)
     cold_ms = time_launches(lambda i: read(cold_bufs[i % len(cold_bufs)]), 2000, stream)
     warm_ms = time_launches(lambda i: read(cold_bufs[0]), 2000, stream)
+    # on-chip read rate: 256 workgroups re-reading their own 96 KiB blocks of 24 MiB (L2-resident)
+    l2buf = torch.zeros(24 << 20, dtype=torch.uint8, device=dev)
+    l2_reps = 256
+    l2_call = lambda i: ok(lib.tlg_ceil_read_l2(vp(l2buf.data_ptr()), l2_reps, vp(sink.data_ptr()), s))
+    ramp(l2_call, stream)
+    l2_ms = time_launches(l2_call, 20, stream)
+    l2_bytes = (24 << 20) * l2_reps
+    del l2buf
     mfma, clock_mhz = {}, {}
     stamps = torch.zeros(4 * 256, dtype=torch.int64, device=dev)
     khz = ctypes.c_int(0)
@@ -352,12 +374,15 @@ def bench_ceilings(torch, dev, stream, cold_bufs):
     return {"empty_kernel_event_us": round(empty_ms * 1e3, 3),
             "read_cold_us": round(cold_ms * 1e3, 3), "read_cold_GB/s": round(nbytes / (cold_ms * 1e-3) / 1e9, 1),
             "read_warm_us": round(warm_ms * 1e3, 3), "read_bytes": nbytes,
+            "read_l2_GB/s": round(l2_bytes / (l2_ms * 1e-3) / 1e9, 1), "read_l2_bytes_per_launch": l2_bytes,
             "mfma_f32_TFLOP/s": round(mfma["f32"], 1), "mfma_bf16_TFLOP/s": round(mfma["bf16"], 1),
             "sclk_MHz_under_mfma_f32": round(clock_mhz["f32"], 1),
             "sclk_MHz_under_mfma_bf16": round(clock_mhz["bf16"], 1),
             "method": "HIP events over back-to-back launches of the probes in libtlgceil.so: empty kernel "
                       "(256 workgroups), plain read of 32 MiB (256 workgroups x 8 waves x 16 loads of 16 B, "
-                      f"cold = rotating {len(cold_bufs)} buffers), 16 independent 32x32 MFMA chains per wave "
+                      f"cold = rotating {len(cold_bufs)} buffers), on-chip read (256 workgroups re-reading their "
+                      f"own 96 KiB blocks of 24 MiB {l2_reps} times, each block in flight at once), "
+                      "16 independent 32x32 MFMA chains per wave "
                       "on all CUs; sclk = median over workgroups of shader-clock ticks / constant-rate ticks "
                       "(s_memtime / s_memrealtime) across the MFMA loop, times the constant rate"}
 
@@ -1072,6 +1097,7 @@ def main(argv=None) -> int:
                         "frac_mfma_peak": round(sqb.flops / (msb * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                         **clock_adjusted(extra.get("ceilings"), sqb.flops / (msb * 1e-3) / 1e12, PEAK_BF16_TFLOPS,
                                          "bf16"),
+                        **l2_roofline(extra.get("ceilings"), planb, sqb, msb),
                         "plan": planb.describe()},
         "narrow_fp16": {"workload": "fp16 linear Y=X.W^T, M=16, K=4096, N=4096, W out x in, fp16 out, cold W "
                                     f"({COLD_COPIES} rotated copies)",

@@ -30,6 +30,38 @@ __global__ void empty_kernel(int* flag) {
 constexpr int kReadLoads = 16, kReadWaves = 8;
 constexpr size_t kReadBlock = (size_t)kReadWaves * kReadLoads * 1024;
 
+// On-chip read rate: 256 workgroups of 8 waves, workgroup b re-reading its
+// own 96 KiB block (3 MiB per XCD, within its 4 MB L2) `reps` times.  Every
+// pass a lane issues 12 loads of 16 bytes, 6 into each half of the block,
+// before it uses the first (each load instruction of a wave covers 1 KiB of
+// consecutive bytes): 96 KiB per workgroup in flight, more than the CU's L1
+// holds, so the data comes from L2.  Each half takes its offset through an empty asm
+// statement of its own every pass, so the compiler cannot keep one pass's
+// data for the next, and the data is summed.
+constexpr size_t kL2Block = 96 * 1024;
+constexpr int kL2Grid = 256;
+__global__ __launch_bounds__(64 * kReadWaves) void read_l2_kernel(const char* __restrict__ base, int reps,
+                                                                  float* __restrict__ sink) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    constexpr int kLoads = 12, kPerHalf = kLoads / 2;
+    constexpr size_t kHalf = kL2Block / 2, kWave = kHalf / kReadWaves;  // 6 KiB per wave and half
+    static_assert(kWave == kPerHalf * 1024, "a wave's loads tile its part of each half");
+    const uint32_t off = (uint32_t)(blockIdx.x * kL2Block + (size_t)w * kWave + lane * 16);
+    uint32_t x = 0;
+    for (int r = 0; r < reps; ++r) {
+        uint32_t o[2] = {off, (uint32_t)(off + kHalf)};
+        asm volatile("" : "+v"(o[0]));
+        asm volatile("" : "+v"(o[1]));
+        u32x4 v[kLoads];
+#pragma unroll
+        for (int j = 0; j < kLoads; ++j)
+            v[j] = *reinterpret_cast<const u32x4*>(base + o[j / kPerHalf] + (j % kPerHalf) * 1024);
+#pragma unroll
+        for (int j = 0; j < kLoads; ++j) x += v[j][0] + v[j][1] + v[j][2] + v[j][3];
+    }
+    if (x == 0x9e3779b9u) sink[threadIdx.x] = 1.0f;
+}
+
 __global__ __launch_bounds__(64 * kReadWaves) void read_kernel(const char* __restrict__ base, float* __restrict__ sink) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const char* p = base + (size_t)blockIdx.x * kReadBlock;
@@ -111,6 +143,14 @@ int tlg_ceil_read(const void* p, size_t bytes, float* sink, void* stream) {
     if (!p || !sink || bytes == 0 || bytes % kReadBlock != 0 || reinterpret_cast<uintptr_t>(p) % 16 != 0) return -1;
     hipLaunchKernelGGL(read_kernel, dim3((unsigned)(bytes / kReadBlock)), dim3(64 * kReadWaves), 0,
                        (hipStream_t)stream, static_cast<const char*>(p), sink);
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+// Re-read a 24 MiB buffer's 96 KiB blocks `reps` times (one workgroup per block).
+int tlg_ceil_read_l2(const void* p, int reps, float* sink, void* stream) {
+    if (!p || !sink || reps <= 0 || reinterpret_cast<uintptr_t>(p) % 16 != 0) return -1;
+    hipLaunchKernelGGL(read_l2_kernel, dim3(kL2Grid), dim3(64 * kReadWaves), 0, (hipStream_t)stream,
+                       static_cast<const char*>(p), reps, sink);
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 

@@ -28,6 +28,13 @@ int tlg_ceil_empty(int grid, int* flag, void* stream);
  * written only for a data pattern that does not occur in practice. */
 int tlg_ceil_read(const void* p, size_t bytes, float* sink, void* stream);
 
+/* On-chip read rate: `p` (16-byte aligned) holds 24 MiB; 256 workgroups of 8
+ * waves each re-read their own 96 KiB block `reps` (> 0) times, the whole
+ * block in flight per pass, so after the first pass the data comes from each
+ * XCD's L2 (3 MiB per XCD): 24 MiB per pass in all.  `sink` holds 512 floats,
+ * written like `tlg_ceil_read`'s. */
+int tlg_ceil_read_l2(const void* p, int reps, float* sink, void* stream);
+
 /* MFMA issue rate: `grid` (> 0) workgroups of 4 waves, each wave issuing
  * 16·`iters` (> 0) independent MFMAs with no memory traffic: 32x32x16 bf16
  * (32768 flop each) when `bf16` is non-zero, else 32x32x2 fp32 (4096 flop

@@ -31,7 +31,7 @@ def test_ceiling_probe_library_exports_its_header():
     text = re.sub(r"/\*.*?\*/", "", open(hdr).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(tlg_ceil_\w+)\s*\(", text)))
     assert names == ["tlg_ceil_empty", "tlg_ceil_mfma", "tlg_ceil_mfma_clock", "tlg_ceil_read",
-                     "tlg_ceil_wall_clock_khz"]
+                     "tlg_ceil_read_l2", "tlg_ceil_wall_clock_khz"]
     lib = ctypes.CDLL(os.path.join(os.path.dirname(t.LIB_PATH), "libtlgceil.so"))
     for name in names:
         assert hasattr(lib, name), name
