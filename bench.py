@@ -181,6 +181,12 @@ def time_launches(fn, n: int, stream) -> float:
     return start.elapsed_time(end) / n
 
 
+def vendor_entry(call: str, vendor_ms: float, ours_ms: float) -> dict:
+    """One row of the vendor-library context: its time beside this library's on the same inputs and stream."""
+    return {"call": call, "us": round(vendor_ms * 1e3, 2), "ours_us": round(ours_ms * 1e3, 2),
+            "ours_speedup": round(vendor_ms / ours_ms, 3)}
+
+
 def sampled_parity(case, y64, npts=2000, seed=0):
     """max|err|/max|ref| over sampled outputs plus the first and last rows."""
     import oracle
@@ -478,7 +484,8 @@ def bench_c3(torch, dev, stream, no_parity: bool, copies: int = 12):
     return out
 
 
-def bench_c5(torch, dev, stream, dtype: str, no_parity: bool, layers: int = 12, reps: int = 20):
+def bench_c5(torch, dev, stream, dtype: str, no_parity: bool, layers: int = 12, reps: int = 20,
+             vendor: bool = True):
     """Batched GPT-2-small stack at M=8192: one pass = 12 layers x 4 linears, 48 launches on one stream."""
     from dense_gemm_transformer_amd import inputs, tlgemm
 
@@ -523,6 +530,23 @@ def bench_c5(torch, dev, stream, dtype: str, no_parity: bool, layers: int = 12, 
     graph_ms, graph_same = graph_span_ms(torch, one_pass, reps, ys)
     flops = layers * sum(2 * M * N * K for _, N, K, _ in inputs.GPT2_LINEARS)
     tol = 1e-5 if dtype == "f32" else 1e-2
+    vend = None
+    if vendor:  # the same 48 products through the vendor library (GELU a kernel of its own), same inputs
+
+        def vendor_pass():
+            for l in range(layers):
+                for g in range(4):
+                    W, b = wb[l][g]
+                    y = torch.nn.functional.linear(xs[g][l], W, b)
+                    if inputs.GPT2_LINEARS[g][3]:
+                        torch.nn.functional.gelu(y, approximate="tanh")
+
+        tf32 = torch.backends.cuda.matmul.allow_tf32
+        torch.backends.cuda.matmul.allow_tf32 = False
+        ramp(lambda i: vendor_pass(), stream)
+        vend = vendor_entry("F.linear(x, W, b) per product, then F.gelu(tanh) on fc; TF32 off",
+                            median_span_ms(torch, vendor_pass, reps, stream), ms)
+        torch.backends.cuda.matmul.allow_tf32 = tf32
     return {"workload": f"GPT-2-small stack, M=8192 (64 x 128 tokens), {layers} layers x "
                         "{qkv, attn-out, fc+GELU, proj}, bias on all, " + dtype + " in and out",
             "pass_ms": round(ms, 4), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2),
@@ -533,6 +557,7 @@ def bench_c5(torch, dev, stream, dtype: str, no_parity: bool, layers: int = 12, 
             "parity_err_layer0": errs or None,
             "parity_pass": None if not errs else all(e <= tol for e in errs.values()),
             "plans": [p.describe() for p in plans],
+            "vendor_library": vend,
             "timing": f"median over {reps} passes of the HIP-event span of one pass (48 launches, one stream); "
                       "12 distinct weight sets, activations of later layers are row-rotated copies of layer 0's; "
                       "pass_ms_graph: the same 48 launches captured once in a HIP graph, median replay span"}
@@ -912,6 +937,8 @@ def main(argv=None) -> int:
     ap.add_argument("--narrow-launches", type=int, default=2000, help="timed cold narrow launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--no-vendor", action="store_true",
+                    help="skip the vendor-library context (torch.mm / F.linear, i.e. hipBLASLt or rocBLAS)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the ceiling probes and the 128-row layer and M=8192 stack workloads")
     ap.add_argument("--rocprof-summary", metavar="DIR",
@@ -996,6 +1023,25 @@ def main(argv=None) -> int:
         run_sqb(i)
     msb = time_launches(run_sqb, args.steps, stream)
     log(f"square bf16: {msb * 1e3:.1f} us, {sqb.flops / (msb * 1e-3) / 1e12:.1f} TFLOP/s, parity {sqb_err}")
+    # The vendor library (torch.mm: hipBLASLt or rocBLAS) on the same inputs, for context: the same ramp, the
+    # same event timing, fp32 arithmetic (TF32 off) and fp32 output for both squares.
+    vendor = {}
+    if not args.no_vendor:
+        tf32 = torch.backends.cuda.matmul.allow_tf32
+        torch.backends.cuda.matmul.allow_tf32 = False
+        vf = lambda i: torch.mm(A, B, out=C)
+        ramp(vf, stream, args.ramp_ms)
+        vendor["square_4096_f32"] = vendor_entry("torch.mm(A, B, out=C), fp32, TF32 off",
+                                                 time_launches(vf, args.steps, stream), ms)
+        try:
+            vb = lambda i: torch.mm(Ab, Bb, out_dtype=torch.float32)
+            ramp(vb, stream, args.ramp_ms)
+            vendor["square_4096_bf16"] = vendor_entry("torch.mm(A, B, out_dtype=torch.float32), bf16 in",
+                                                      time_launches(vb, args.steps, stream), msb)
+        except (TypeError, RuntimeError) as e:  # out_dtype is not in every torch build
+            vendor["square_4096_bf16"] = {"error": str(e)[:160]}
+        torch.backends.cuda.matmul.allow_tf32 = tf32
+        log(f"vendor squares: {vendor}")
     del Ab, Bb
 
     # ---- narrow fp16 linear 16×4096×4096, cold weights -----------------------------------
@@ -1020,6 +1066,12 @@ def main(argv=None) -> int:
     n_gbs = n_bytes / (n_ms * 1e-3) / 1e9
     log(f"narrow fp16: {nplan.describe()} cold {n_ms * 1e3:.2f} us ({n_gbs:.0f} GB/s), warm {warm_ms * 1e3:.2f} us, "
         f"parity {n_err}")
+    if not args.no_vendor:
+        vn = lambda i: torch.nn.functional.linear(X, Ws[i % COLD_COPIES])
+        ramp(vn, stream, args.ramp_ms)
+        vendor["narrow_16x4096x4096_f16"] = vendor_entry(
+            f"F.linear(X, W) over the same {COLD_COPIES} rotated weight copies",
+            time_launches(vn, args.narrow_launches, stream), n_ms)
 
     extra = {}
     if not args.no_extra:
@@ -1032,7 +1084,10 @@ def main(argv=None) -> int:
         extra["gpt2_layer_m128_f32"] = bench_c3(torch, dev, stream, args.no_parity)
         for dt in ("f32", "bf16"):
             log(f"GPT-2 stack at M=8192, {dt}")
-            extra[f"gpt2_stack_m8192_{dt}"] = bench_c5(torch, dev, stream, dt, args.no_parity)
+            extra[f"gpt2_stack_m8192_{dt}"] = bench_c5(torch, dev, stream, dt, args.no_parity,
+                                                       vendor=not args.no_vendor)
+            if not args.no_vendor:
+                vendor[f"gpt2_stack_m8192_{dt}"] = extra[f"gpt2_stack_m8192_{dt}"]["vendor_library"]
             torch.cuda.empty_cache()
         for dt in ("f32", "bf16"):
             log(f"GPT-2-small forward, 12 blocks, {dt}")
@@ -1112,6 +1167,9 @@ def main(argv=None) -> int:
                                      "algorithmic_bytes_per_launch": n_bytes},
                         "timing": "HIP events over back-to-back launches (includes launch gaps)",
                         "plan": nplan.describe()},
+        "vendor_library": {"note": "context, not a baseline: the same workloads through torch (hipBLASLt or "
+                                   "rocBLAS) on this GPU, timed like this library's; ours_speedup = vendor time / "
+                                   "ours", **vendor} if vendor else None,
         "clocks": {"before": clocks_before, "after": clocks_after,
                    "state": "UNPINNED" + (" (changed during the run)" if clocks_before != clocks_after else "")},
     }

@@ -252,6 +252,14 @@ static int auto_plan(tlg_plan& p) {
     // every tile re-read X, and the tiled kernel with split-K wins.
     if (p.layout == TLG_NK && p.M <= kStreamMaxRows && ceil_div(p.N, 16) * ceil_div(p.M, 32) <= kNumCUs)
         return auto_stream(p);
+    // Outputs that fill every CU with 256×256 tiles take them: half the
+    // operand bytes per flop of 128×128 (square 4096 bf16 → bf16 on MI355X:
+    // 145 µs with 128×128, ~111 µs with 256×256).
+    const int huge = p.in_dt == TLG_F32 ? 5 : 4;
+    const TileCfg& ch = tiled_cfg(p.in_dt, huge);
+    if (p.M % ch.bm == 0 && p.N % ch.bn == 0 && ceil_div(p.M, ch.bm) * ceil_div(p.N, ch.bn) >= kNumCUs &&
+        fill_tiled(p, huge, 1) == TLG_OK)
+        return TLG_OK;
     const int big = 0, small = 1;
     const TileCfg& cb = tiled_cfg(p.in_dt, big);
     const int64_t tiles_big = ceil_div(p.M, cb.bm) * ceil_div(p.N, cb.bn);

@@ -100,6 +100,13 @@ def test_square_fp32_goes_to_tiled():
     # an unlisted square shape falls back to the fill rule's 128×128 tiles
     i = _plan(2048, 2048, 2048, "f32", "f32", "KN").info
     assert (i.tile_m, i.tile_n, i.workgroups) == (128, 128, 256)
+    # outputs that 256×256 tiles alone spread over every CU take them
+    i = _plan(4096, 4096, 4096, "bf16", "bf16", "KN").info  # no table row for bf16 output
+    assert (i.tile_m, i.tile_n, i.workgroups, i.split_k) == (256, 256, 256, 1)
+    i = _plan(8192, 4096, 1024, "f32", "f32", "NK").info
+    assert (i.tile_m, i.tile_n, i.workgroups, i.threads) == (256, 256, 512, 512)
+    i = _plan(4096, 4096 + 128, 4096, "bf16", "bf16", "KN").info  # ragged: the fill rule
+    assert (i.tile_m, i.tile_n) == (128, 128)
 
 
 def test_dispatch_table_rows_are_exact_shape_matches():
