@@ -890,7 +890,6 @@ def counter_summary(dirs: list[str], kernels: list[str]) -> str:
         for path in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
             with open(path, newline="") as f:
                 for row in csv.DictReader(f):
-                    key = (row["Kernel_Name"], f"{row['Grid_Size_X']}x{row['Grid_Size_Y']}x{row['Grid_Size_Z']}")
                     wg = (max(int(row["Workgroup_Size_X"]), 1), max(int(row["Workgroup_Size_Y"]), 1),
                           max(int(row["Workgroup_Size_Z"]), 1))
                     grid = tuple(int(row[f"Grid_Size_{a}"]) // w for a, w in zip("XYZ", wg))
