@@ -416,12 +416,19 @@ def bench_c1(torch, dev, stream, no_parity: bool):
     ramp(lambda i: run(copies[i % len(copies)]), stream)
     cold = time_launches(lambda i: run(copies[i % len(copies)]), 1024, stream)
     warm = time_launches(lambda i: run(W0), 1024, stream)
+    # the same launches replayed from HIP graphs: no host work between them
+    pX, pb, pY, pw = X.data_ptr(), b.data_ptr(), Y.data_ptr(), ws.data_ptr() if ws_bytes else 0
+    g_launch = lambda sh, ws_: [plan.run_ptrs(pX, w.data_ptr(), pb, pY, pw, ws_bytes, sh) for w in ws_]
+    g_warm, _ = graph_span_ms(torch, lambda sh: g_launch(sh, [W0] * 32), 20, [Y])
+    g_cold, _ = graph_span_ms(torch, lambda sh: g_launch(sh, copies), 20, [Y])
     return {"workload": "fp32 linear Y=X.W^T+b, M=128, K=768, N=768, W out x in, N(0,1)/N(0,0.02)",
             "warm_us": round(warm * 1e3, 3), "cold_us": round(cold * 1e3, 3),
+            "warm_graph_us": round(g_warm / 32 * 1e3, 3), "cold_graph_us": round(g_cold / len(copies) * 1e3, 3),
             "TFLOP/s_warm": round(c.flops / (warm * 1e-3) / 1e12, 2),
             "floor_us": round(c.flops / (PEAK_F32_TFLOPS * 1e12) * 1e6, 3),
             "parity_err": err, "parity_pass": None if err is None else err <= 1e-5, "plan": plan.describe(),
-            "timing": "HIP events over back-to-back launches (includes launch gaps)"}
+            "timing": "HIP events over back-to-back launches (includes launch gaps); *_graph_us: median replay "
+                      "of a HIP graph of 32 (warm) or 128 (cold, one per weight copy) launches, per launch"}
 
 
 def bench_c3(torch, dev, stream, no_parity: bool, copies: int = 12):
@@ -634,23 +641,30 @@ def bench_layer_ops(torch, dev, stream, dtype: str, no_parity: bool, reps: int =
     rows, C = X.shape
     dX, dg, db = (dev_tensor(torch, a, dtype, dev) for a in (X, g, b))
     dY = torch.empty_like(dX)
-    ln = lambda: layer.tlg_layernorm(dX.data_ptr(), dg.data_ptr(), db.data_ptr(), dY.data_ptr(), 0, 0, rows, C,
-                                     1e-5, dtype, stream.cuda_stream)
+    pX, pg, pb, pY = dX.data_ptr(), dg.data_ptr(), db.data_ptr(), dY.data_ptr()
+    ln = lambda sh: layer.tlg_layernorm(pX, pg, pb, pY, 0, 0, rows, C, 1e-5, dtype, sh)
     B, T, NH, HS = 64, 128, 12, 64
     qkv = inputs.workload_gpt2_attention(B=B, T=T, n_head=NH, head_size=HS, dtype=dtype)
     dqkv = dev_tensor(torch, qkv, dtype, dev)
     dout = torch.empty((B, T, NH * HS), dtype=dqkv.dtype, device=dev)
-    att = lambda: layer.tlg_attention(dqkv.data_ptr(), dout.data_ptr(), 0, B, T, NH, HS, dtype, True,
-                                      stream.cuda_stream)
+    pq, po = dqkv.data_ptr(), dout.data_ptr()
+    att = lambda sh: layer.tlg_attention(pq, po, 0, B, T, NH, HS, dtype, True, sh)
     res = {}
-    for name, fn, nbytes, flops in (
-            ("layernorm_8192x768", ln, rows * C * 2 * es + 2 * C * es, None),
-            ("attention_b64_t128_h12", att, B * T * 4 * NH * HS * es, 4 * B * NH * HS * T * (T + 1) // 2)):
-        fn()
+    per_graph = 32  # launches captured in one graph
+    for name, fn, out, nbytes, flops in (
+            ("layernorm_8192x768", ln, dY, rows * C * 2 * es + 2 * C * es, None),
+            ("attention_b64_t128_h12", att, dout, B * T * 4 * NH * HS * es, 4 * B * NH * HS * T * (T + 1) // 2)):
+        fn(stream.cuda_stream)
         torch.cuda.synchronize()
-        ramp(lambda i: fn(), stream)
-        us = time_launches(lambda i: fn(), reps, stream) * 1e3
-        r = {"us": round(us, 3), "GB/s": round(nbytes / us / 1e3, 1),
+        ramp(lambda i: fn(stream.cuda_stream), stream)
+        us_eager = time_launches(lambda i: fn(stream.cuda_stream), reps, stream) * 1e3
+        # The host issues a launch through the Python binding in about as long as these kernels run, so
+        # back-to-back eager launches can measure the host: the primary figure replays per_graph launches
+        # captured in one HIP graph (no host work between them), per launch.
+        g_ms, g_same = graph_span_ms(torch, lambda sh: [fn(sh) for _ in range(per_graph)], reps, [out])
+        us = g_ms / per_graph * 1e3
+        r = {"us": round(us, 3), "us_eager": round(us_eager, 3), "graph_bitwise_equal": g_same,
+             "GB/s": round(nbytes / us / 1e3, 1),
              "roofline": {"bound": "hbm", "achieved": round(nbytes / us / 1e3, 1), "peak": PEAK_HBM_GBS,
                           "unit": "GB/s", "frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4),
                           "algorithmic_bytes_per_launch": nbytes}}
@@ -667,7 +681,9 @@ def bench_layer_ops(torch, dev, stream, dtype: str, no_parity: bool, reps: int =
         tol = 1e-5 if dtype == "f32" else 1e-2
         for k in res:
             res[k]["parity_pass"] = res[k]["parity_err"] <= tol
-    res["timing"] = f"HIP events over {reps} back-to-back launches on one stream (includes launch gaps)"
+    res["timing"] = (f"us: median over {reps} replays of a HIP graph of {per_graph} back-to-back launches, per "
+                     f"launch; us_eager: HIP events over {reps} launches from Python on one stream (host-bound "
+                     "where the binding's call takes longer than the kernel)")
     res["workload"] = (f"GPT-2-small layer ops, {dtype}: LayerNorm of X [{rows}][{C}] (gamma, beta), fused causal "
                        f"attention over qkv [{B}][{T}][{3 * NH * HS}] ({NH} heads of {HS}), no lse")
     return res
