@@ -789,8 +789,9 @@ def rocprof_summary(outdir: str, segments: list[str]) -> str:
     def short(name: str) -> str:  # the template arguments identify a kernel; drop its parameter list
         return name[:name.rindex("(")] if name.endswith(")") and "(" in name else name
 
-    def ours(name: str) -> bool:  # the library's kernels and the ceiling probes, not torch's or the runtime's
-        return not (name.startswith("void at::") or name.startswith("at::") or name.startswith("__amd_rocclr"))
+    def ours(name: str) -> bool:  # the library's kernels and the ceiling probes, not torch's, BLAS's or the runtime's
+        return not name.startswith(("void at::", "at::", "__amd_rocclr", "Cijk_", "Custom_Cijk", "rocblas",
+                                    "void rocblas", "void hipblaslt"))
 
     lines = ["| kernel | grid (workgroups) | launches | median µs | p10 µs | p90 µs | min µs |",
              "|---|---|---|---|---|---|---|"]
@@ -831,6 +832,15 @@ def rocprof_summary(outdir: str, segments: list[str]) -> str:
             out.append(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                        f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
         out.append("")
+        # the vendor GEMMs of the bench's context leg, by the macro tile and MFMA tokens their names carry
+        vend = [r for r in rows if r["Name"].startswith(("Cijk_", "Custom_Cijk"))]
+        if vend:
+            out += ["Vendor BLAS kernels in the same run (`--stats`), by the macro-tile and MFMA tokens of their names:",
+                    "", "| macro tile, MFMA | calls | average µs |", "|---|---|---|"]
+            for r in vend:
+                tag = " ".join(t for t in r["Name"].split("_") if t.startswith(("MT", "MI")))
+                out.append(f"| {tag} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} |")
+            out.append("")
     return "\n".join(out)
 
 

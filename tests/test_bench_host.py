@@ -34,10 +34,11 @@ def test_rocprof_summary_keeps_grids_apart_and_drops_runtime_kernels(tmp_path):
     rows += [trace_row(BWD, 10 + i, 512, 96, 200_000) for i in range(3)]
     rows += [trace_row("void at::native::vectorized_elementwise_kernel<4>(int)", 20, 256, 64, 5_000)]
     rows += [trace_row("__amd_rocclr_copyBuffer", 21, 256, 256, 7_000)]
+    rows += [trace_row("Cijk_Ailk_Bljk_BBS_BH_MT256x256x64_MI16x16x1", 22, 256, 256, 100_000)]  # vendor GEMM
     write_csv(str(tmp_path / "run" / "x_kernel_trace.csv"), TRACE_COLS, rows)
     md = bench.rocprof_summary(str(tmp_path), [])
     table = [l for l in md.splitlines() if l.startswith("| `")]
-    assert len(table) == 2  # runtime and torch kernels left out
+    assert len(table) == 2  # runtime, torch and vendor BLAS kernels left out
     sq = [l for l in table if "| 256x1x1 |" in l]
     bw = [l for l in table if "| 96x1x1 |" in l]
     assert len(sq) == 1 and len(bw) == 1
