@@ -154,6 +154,13 @@ extern "C" int gemm_run(tlg_plan_t p, const void* X, const void* W, const void* 
             set_error("gemm_run: workspace overlaps Y");
             return TLG_ERR_INVALID_ARG;
         }
+        // partials written there while the inputs are still being read
+        if (overlaps(workspace, p->ws_bytes, X, (size_t)p->M * p->K * isz) ||
+            overlaps(workspace, p->ws_bytes, W, (size_t)p->N * p->K * isz) ||
+            (bias && overlaps(workspace, p->ws_bytes, bias, (size_t)p->N * isz))) {
+            set_error("gemm_run: workspace overlaps an input");
+            return TLG_ERR_INVALID_ARG;
+        }
     }
     const hipStream_t s = static_cast<hipStream_t>(stream);
     switch (p->variant) {

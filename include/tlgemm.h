@@ -137,7 +137,8 @@ int gemm_plan_info(tlg_plan_t p, tlg_plan_info* info);
  * X, W, Y (and bias if TLG_EPI_BIAS) must be non-NULL device pointers, 16-byte aligned; bias must
  * be NULL when TLG_EPI_BIAS is not set.  Y must not overlap X, W or bias.
  * workspace: device memory of at least gemm_workspace_size(p) bytes when
- * that is non-zero; it may be NULL when the size is 0.  Its first 64 KiB
+ * that is non-zero, overlapping none of X, W, bias and Y (TLG_ERR_INVALID_ARG
+ * otherwise); it may be NULL when the size is 0.  Its first 64 KiB
  * hold arrival counters and the rest fp32 split partials.  It must be
  * zero-filled before its first use; after that every completed run of any
  * plan leaves the counters zero (split stream plans reset the counter of

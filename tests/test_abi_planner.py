@@ -230,6 +230,10 @@ def test_run_argument_errors_without_launch():
     assert lib.gemm_run(q.handle, big, 2 * big, None, 3 * big, None, 0, None) == t.ERR_WORKSPACE
     assert lib.gemm_run(q.handle, big, 2 * big, None, 3 * big, 8 * big, 16, None) == t.ERR_WORKSPACE
     assert "workspace" in t.gemm_last_error()
+    ws = q.workspace_size
+    for clash in (big, 2 * big):  # the workspace over X, then over W: the partials would overwrite inputs
+        assert lib.gemm_run(q.handle, big, 2 * big, None, 3 * big, clash, ws, None) == t.ERR_INVALID_ARG
+        assert "overlaps an input" in t.gemm_last_error()
 
 
 # --- transposed first operand and the residual -------------------------------------
