@@ -36,7 +36,7 @@ The oracle (plain C, double accumulation) is timed on this host's cores on
 a bounded row sample of the square workload and reported as
 ``cpu_baseline``; it is a reference point, not a target.
 
-Prints one JSON line.  ``--gpus`` above 1 exits with a message: this build
+Prints one JSON line.  ``--gpus`` above 1 exits with a message: the library
 runs on one GPU.
 """
 
