@@ -275,3 +275,26 @@ def random_case(seed: int, M: int, N: int, K: int, in_dtype: str = "f32", out_dt
     R = normal(seed * 16 + TENSOR_R, (M, N), 1.0, out_dtype) if residual else None
     return LinearCase(f"rand_{M}x{N}x{K}_{in_dtype}_{layout}{'_res' if residual else ''}", M, N, K, in_dtype,
                       out_dtype, layout, bias, gelu, X, W, b, R)
+
+
+def periodic_normal(seed: int, shape, std: float, dtype: str, block=(1021, 1031)) -> np.ndarray:
+    """``N(0, std)`` values of one ``block`` (prime sides) repeated over ``shape``: element (i, j) is
+    block[i % 1021][j % 1031].  Operands of several GiB are drawn in seconds this way, and an address off
+    by a multiple of 2^30 or 2^31 bytes still lands on a different value (the strides share no factor with
+    the primes)."""
+    rows, cols = shape
+    b = normal(seed, (min(rows, block[0]), min(cols, block[1])), std, dtype)
+    reps = (-(-rows // b.shape[0]), -(-cols // b.shape[1]))
+    return np.ascontiguousarray(np.tile(b, reps)[:rows, :cols])
+
+
+def large_case(seed: int, M: int, N: int, K: int, in_dtype: str, out_dtype: str | None = None,
+               layout: str = "NK") -> LinearCase:
+    """``random_case`` for operands of several GiB: X ~ N(0, 1) and W ~ N(0, 0.05) as periodic blocks."""
+    out_dtype = out_dtype or in_dtype
+    xshape = (K, M) if layout.startswith("AT_") else (M, K)
+    wshape = (K, N) if layout.endswith("KN") else (N, K)
+    X = periodic_normal(seed * 16 + TENSOR_X, xshape, 1.0, in_dtype)
+    W = periodic_normal(seed * 16 + TENSOR_W, wshape, 0.05, in_dtype)
+    return LinearCase(f"large_{M}x{N}x{K}_{in_dtype}_{layout}", M, N, K, in_dtype, out_dtype, layout, False, False,
+                      X, W, None, None)

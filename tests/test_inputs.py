@@ -45,3 +45,16 @@ def test_workload_shapes():
     assert sq.layout == "KN" and sq.out_dtype == "f32" and sq.W.dtype == np.uint16
     w = inputs.workload_fp32_linear_128x768().W.astype(np.float64)
     assert 0.015 < w.std() < 0.025
+
+
+def test_periodic_normal_repeats_one_prime_block():
+    """The multi-GiB generator repeats one seeded block with prime sides, seeded like ``normal``."""
+    a = inputs.periodic_normal(9, (2500, 3000), 0.05, "bf16")
+    b = inputs.normal(9, (1021, 1031), 0.05, "bf16")
+    assert a.shape == (2500, 3000) and a.dtype == b.dtype and a.flags.c_contiguous
+    for i, j in [(0, 0), (1020, 1030), (1021, 1031), (2499, 2999), (2042 + 5, 7)]:
+        assert a[i, j] == b[i % 1021, j % 1031]
+    small = inputs.periodic_normal(9, (10, 20), 1.0, "f32")  # smaller than a block: one draw of that shape
+    assert np.array_equal(small, inputs.normal(9, (10, 20), 1.0, "f32"))
+    c = inputs.large_case(3, 64, 96, 128, "f16", "f32", "KN")
+    assert c.X.shape == (64, 128) and c.W.shape == (128, 96) and c.b is None and c.out_dtype == "f32"
