@@ -68,3 +68,14 @@ def test_output_past_2g_elements(out_dtype):
     del Y
     torch.cuda.empty_cache()
     assert err <= TOL[case.in_dtype], f"{desc}: err {err:.3e}"
+
+
+def test_stream_weight_rows_past_2gib():
+    """16 rows against a 4 GiB fp16 weight (256 rows of 2^23): the stream kernel's row addresses pass 2^31
+    bytes and its split-K runs over 16 workgroups; sampled outputs against the oracle."""
+    case = inputs.large_case(42, 16, 256, 2 ** 23, "f16", "f16", "NK")
+    assert case.W.nbytes == 2 ** 32
+    Y, desc = _run(case)
+    assert "variant=stream" in desc, desc
+    err = _sample_check(case, Y, npts=120)
+    assert err <= TOL["f16"], f"{desc}: err {err:.3e}"
