@@ -58,7 +58,7 @@ METRIC = "TFLOP/s (% MFMA peak) @4096³ fp32; µs + HBM GB/s @16×4096×4096 fp1
 
 # Bytes each kernel moved between L2 and memory per launch, from rocprofv3
 # FETCH_SIZE and WRITE_SIZE passes over `bench.py --steps 3 --warmup 1
-# --narrow-launches 32 --no-cpu-baseline --no-parity --no-extra --ramp-ms 0`, summarised
+# --narrow-launches 32 --no-cpu-baseline --no-parity --no-extra --no-vendor --ramp-ms 0`, summarised
 # by `bench.py --pmc-summary` (the HBM-traffic profile under profiles/).
 # FETCH_SIZE is scaled by 1.998 and WRITE_SIZE by 1.0: the factors that make
 # the same counters read 32 MiB for the run's 32 MiB device-to-device copies.
@@ -66,7 +66,7 @@ METRIC = "TFLOP/s (% MFMA peak) @4096³ fp32; µs + HBM GB/s @16×4096×4096 fp1
 # after a change to either the figure no longer applies and the bench reports null.
 FETCH_SCALE, WRITE_SCALE = 1.998, 1.0
 TRAFFIC = {
-    "tiled_f32": {"sources": ("common.h", "tiled.h"), "sha": "bc1d84a98f036bd5",
+    "tiled_f32": {"sources": ("common.h", "tiled.h"), "sha": "1db6ebcf9a05bc22",
                   "tile": "256x256x16", "fetch_kib": 196685.0, "write_kib": 65536.0},
     "stream_f16": {"sources": ("common.h", "stream.h"), "sha": "24a261f043cb0dae",
                    "tile": "16x16x4096", "fetch_kib": 16916.5, "write_kib": 128.0},
