@@ -1048,6 +1048,16 @@ def main(argv=None) -> int:
         run_sqb(i)
     msb = time_launches(run_sqb, args.steps, stream)
     log(f"square bf16: {msb * 1e3:.1f} us, {sqb.flops / (msb * 1e-3) / 1e12:.1f} TFLOP/s, parity {sqb_err}")
+    # the same product with bf16 output (the planner's choice for a shape the table does not list)
+    Cb = torch.empty((sqb.M, sqb.N), dtype=torch.bfloat16, device=dev)
+    planbb = tlgemm.Plan.create(sqb.M, sqb.N, sqb.K, "bf16", "bf16", "KN")
+    run_sqbb = lambda i: planbb.run_ptrs(Ab.data_ptr(), Bb.data_ptr(), 0, Cb.data_ptr(), 0, 0, stream.cuda_stream)
+    run_sqbb(0)
+    torch.cuda.synchronize()
+    sqbb_err = None if args.no_parity else sampled_parity(sqb, to_f64(Cb))
+    ramp(run_sqbb, stream, args.ramp_ms)
+    msbb = time_launches(run_sqbb, args.steps, stream)
+    log(f"square bf16 -> bf16: {msbb * 1e3:.1f} us, parity {sqbb_err}")
     # The vendor library (torch.mm: hipBLASLt or rocBLAS) on the same inputs, for context: the same ramp, the
     # same event timing, fp32 arithmetic (TF32 off) and fp32 output for both squares.
     vendor = {}
@@ -1065,9 +1075,13 @@ def main(argv=None) -> int:
                                                       time_launches(vb, args.steps, stream), msb)
         except (TypeError, RuntimeError) as e:  # out_dtype is not in every torch build
             vendor["square_4096_bf16"] = {"error": str(e)[:160]}
+        vbb = lambda i: torch.mm(Ab, Bb, out=Cb)
+        ramp(vbb, stream, args.ramp_ms)
+        vendor["square_4096_bf16_out_bf16"] = vendor_entry("torch.mm(A, B, out=C), bf16 in and out",
+                                                           time_launches(vbb, args.steps, stream), msbb)
         torch.backends.cuda.matmul.allow_tf32 = tf32
         log(f"vendor squares: {vendor}")
-    del Ab, Bb
+    del Ab, Bb, Cb
 
     # ---- narrow fp16 linear 16×4096×4096, cold weights -----------------------------------
     log("narrow fp16 16x4096x4096: generating inputs")
@@ -1178,7 +1192,11 @@ def main(argv=None) -> int:
                         **clock_adjusted(extra.get("ceilings"), sqb.flops / (msb * 1e-3) / 1e12, PEAK_BF16_TFLOPS,
                                          "bf16"),
                         **l2_roofline(extra.get("ceilings"), planb, sqb, msb),
-                        "plan": planb.describe()},
+                        "plan": planb.describe(),
+                        "bf16_out": {"us": round(msbb * 1e3, 2),
+                                     "TFLOP/s": round(sqb.flops / (msbb * 1e-3) / 1e12, 2),
+                                     "frac_mfma_peak": round(sqb.flops / (msbb * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                                     "parity_err": sqbb_err, "plan": planbb.describe()}},
         "narrow_fp16": {"workload": "fp16 linear Y=X.W^T, M=16, K=4096, N=4096, W out x in, fp16 out, cold W "
                                     f"({COLD_COPIES} rotated copies)",
                         "us": round(n_ms * 1e3, 3), "warm_us": round(warm_ms * 1e3, 3),
