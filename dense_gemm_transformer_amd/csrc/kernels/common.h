@@ -65,11 +65,10 @@ template <int DT> __device__ inline u32x4 pack16(const float* v) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) o[u] = __float_as_uint(v[u]);
     } else if constexpr (DT == TLG_F16) {
+        typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const _Float16 lo = (_Float16)v[2 * u], hi = (_Float16)v[2 * u + 1];
-            o[u] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-        }
+        for (int u = 0; u < 4; ++u)  // v_cvt_pk_f16_f32: both halves rounded to nearest even
+            o[u] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){v[2 * u], v[2 * u + 1]}, f16x2_t));
     } else {
 #pragma unroll
         for (int u = 0; u < 4; ++u) o[u] = f32x2_to_bf16x2_rne(v[2 * u], v[2 * u + 1]);
