@@ -16,6 +16,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // ---- element formats ------------------------------------------------------------
 // Storage: fp32 as float, fp16 and bf16 as their 16-bit patterns.
@@ -78,6 +79,37 @@ template <int DT> __device__ inline u32x4 pack16(const float* v) {
 
 template <int DT> __device__ inline float load_elem(const void* p, int64_t idx) {
     return Elem<DT>::to_f32(static_cast<const typename Elem<DT>::storage*>(p)[idx]);
+}
+
+// EPC consecutive bias values from n on (n a multiple of EPC, the pointer
+// 16-byte aligned) as fp32, in one 8- or 16-byte load.
+template <int DT, int EPC> __device__ inline void load_bias_run(const void* bias, int n, float* b) {
+    using St = typename Elem<DT>::storage;
+    constexpr int BYTES = EPC * (int)sizeof(St);
+    const St* p = static_cast<const St*>(bias) + n;
+    if constexpr (BYTES == 16 && DT == TLG_F32) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) b[u] = __uint_as_float(w[u]);
+    } else if constexpr (DT != TLG_F32 && (BYTES == 16 || BYTES == 8)) {
+        constexpr int NW = BYTES / 4;
+        uint32_t w[NW];
+        if constexpr (NW == 4) {
+            const u32x4 x = *reinterpret_cast<const u32x4*>(p);
+            w[0] = x[0], w[1] = x[1], w[2] = x[2], w[3] = x[3];
+        } else {
+            const u32x2 x = *reinterpret_cast<const u32x2*>(p);
+            w[0] = x[0], w[1] = x[1];
+        }
+#pragma unroll
+        for (int u = 0; u < NW; ++u) {
+            b[2 * u] = Elem<DT>::to_f32((uint16_t)(w[u] & 0xffffu));
+            b[2 * u + 1] = Elem<DT>::to_f32((uint16_t)(w[u] >> 16));
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < EPC; ++u) b[u] = load_elem<DT>(bias, n + u);
+    }
 }
 
 // The inverse of pack16: 16 bytes of stored output as 16 / sizeof(element) fp32 values.
@@ -157,7 +189,6 @@ __device__ inline i32x4 buffer_rsrc(const void* p, int64_t bytes) {
 // row-major tile, four lanes per row and four elements apart, the group reads
 // a 4×16 block and each lane receives one column of it: four consecutive rows.
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 __device__ inline u32x2 lds_read_tr16(const void* p) {

@@ -553,12 +553,17 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_min_groups<IN, LAYOUT, BM, BN,
         int el = lane;
         asm volatile("" : "+v"(el));
         const int col = (el % CPR) * EPC;  // the same columns for every run of this lane
-        const int ncol = n0 + wn0 + col;
-        float bcol[EPC];
+        // Bias of each of this lane's runs, one vector load per run: a lane's
+        // runs sit at the same columns in every 16-row half-strip.
+        constexpr int NB = EVEN_RUNS ? 1 : NRUN;
+        float bq[NB][EPC];
 #pragma unroll
-        for (int q = 0; q < EPC; ++q) {
-            bcol[q] = 0.0f;
-            if constexpr (EVEN_RUNS && !SPLIT && (EPI & TLG_EPI_BIAS) != 0) bcol[q] = load_elem<IN>(bias, ncol + q);
+        for (int q = 0; q < NB; ++q) {
+            if constexpr (!SPLIT && (EPI & TLG_EPI_BIAS) != 0)
+                load_bias_run<IN, EPC>(bias, n0 + wn0 + (EVEN_RUNS ? col : ((el + 64 * q) % CPR) * EPC), bq[q]);
+            else
+#pragma unroll
+                for (int u = 0; u < EPC; ++u) bq[q][u] = 0.0f;
         }
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
@@ -578,13 +583,7 @@ __global__ __launch_bounds__(64 * WM * WN, (tiled_min_groups<IN, LAYOUT, BM, BN,
                     const int row = run / CPR;
                     const int rcol = EVEN_RUNS ? col : (run % CPR) * EPC;  // this run's first column in the strip
                     const int nrun = n0 + wn0 + rcol;
-                    float brun[EPC];
-#pragma unroll
-                    for (int u = 0; u < EPC; ++u) {
-                        brun[u] = bcol[u];
-                        if constexpr (!EVEN_RUNS && !SPLIT && (EPI & TLG_EPI_BIAS) != 0)
-                            brun[u] = load_elem<IN>(bias, nrun + u);
-                    }
+                    const float* brun = bq[EVEN_RUNS ? 0 : q];
                     const float* src = stg + row * SROW + rcol;
                     float v[EPC];
 #pragma unroll
