@@ -48,6 +48,17 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) { return __builtin_bit_cast(
 __device__ inline uint32_t f32x2_to_bf16x2_rne(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
+// fp32 pair -> fp16 pair, round to nearest even (v_cvt_pk_f16_f32).
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t f32x2_to_f16x2_rne(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, f16x2_t));
+}
+// Two fp32 values as the packed 16-bit pair of the output type.
+template <int DT> __device__ inline uint32_t pack2(float lo, float hi) {
+    static_assert(DT != TLG_F32, "16-bit types only");
+    if constexpr (DT == TLG_F16) return f32x2_to_f16x2_rne(lo, hi);
+    else return f32x2_to_bf16x2_rne(lo, hi);
+}
 
 template <int DT> __device__ inline void store_out(void* Y, int64_t idx, float v) {
     if constexpr (DT == TLG_F32) {
@@ -65,14 +76,9 @@ template <int DT> __device__ inline u32x4 pack16(const float* v) {
     if constexpr (DT == TLG_F32) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) o[u] = __float_as_uint(v[u]);
-    } else if constexpr (DT == TLG_F16) {
-        typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-#pragma unroll
-        for (int u = 0; u < 4; ++u)  // v_cvt_pk_f16_f32: both halves rounded to nearest even
-            o[u] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){v[2 * u], v[2 * u + 1]}, f16x2_t));
     } else {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) o[u] = f32x2_to_bf16x2_rne(v[2 * u], v[2 * u + 1]);
+        for (int u = 0; u < 4; ++u) o[u] = pack2<DT>(v[2 * u], v[2 * u + 1]);
     }
     return o;
 }

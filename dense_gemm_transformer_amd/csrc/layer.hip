@@ -43,11 +43,19 @@ template <int DT> __device__ inline typename Elem<DT>::storage to_storage(float 
 template <int DT, int VE> __device__ inline void store_vec(void* p, int64_t idx, const float* v) {
     using S = typename Elem<DT>::storage;
     using R = typename Raw<VE * (int)sizeof(S)>::T;
-    struct Pack { S e[VE]; };
-    Pack pk;
+    if constexpr (DT != TLG_F32 && VE % 2 == 0) {  // pairs through one packed conversion each
+        struct Words { uint32_t w[VE / 2]; };
+        Words wd;
 #pragma unroll
-    for (int u = 0; u < VE; ++u) pk.e[u] = to_storage<DT>(v[u]);
-    *reinterpret_cast<R*>(static_cast<S*>(p) + idx) = __builtin_bit_cast(R, pk);
+        for (int u = 0; u < VE / 2; ++u) wd.w[u] = pack2<DT>(v[2 * u], v[2 * u + 1]);
+        *reinterpret_cast<R*>(static_cast<S*>(p) + idx) = __builtin_bit_cast(R, wd);
+    } else {
+        struct Pack { S e[VE]; };
+        Pack pk;
+#pragma unroll
+        for (int u = 0; u < VE; ++u) pk.e[u] = to_storage<DT>(v[u]);
+        *reinterpret_cast<R*>(static_cast<S*>(p) + idx) = __builtin_bit_cast(R, pk);
+    }
 }
 
 __device__ inline float wave_sum(float x) {
