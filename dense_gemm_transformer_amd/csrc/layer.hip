@@ -521,14 +521,29 @@ __global__ __launch_bounds__(256, TMAX <= 128 ? 3 : 1) void attention16_kernel(c
         asm volatile("" ::: "memory");
         float inv[16];
         gather_rows(inv);
+        // The output leaves through the wave's score tile: each 32-dimension half
+        // of the block's 32 rows is written there in the accumulator layout and
+        // read back as 16 consecutive dimensions of one row per lane, for two
+        // 16-byte stores per half instead of sixteen 2-byte ones.
+        const int srow = lane >> 1, sd = 16 * (lane & 1);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int row = row0 + 8 * (e >> 2) + 4 * g + (e & 3);
-            if (row < T) {
-                const int64_t orow = ((int64_t)b * T + row) * C + (int64_t)h * HS;
-                const float y0 = o0[e] * inv[e], y1 = o1[e] * inv[e];
-                store_vec<DT, 1>(out, orow + r, &y0);
-                store_vec<DT, 1>(out, orow + 32 + r, &y1);
+        for (int half = 0; half < 2; ++half) {
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                P[p_at(8 * (e >> 2) + 4 * g + (e & 3), r)] = (half ? o1[e] : o0[e]) * inv[e];
+            asm volatile("" ::: "memory");
+            float y[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(P + p_at(srow, sd + 4 * q));
+                y[4 * q] = x[0], y[4 * q + 1] = x[1], y[4 * q + 2] = x[2], y[4 * q + 3] = x[3];
+            }
+            asm volatile("" ::: "memory");
+            if (row0 + srow < T) {
+                const int64_t o = ((int64_t)b * T + row0 + srow) * C + (int64_t)h * HS + 32 * half + sd;
+                store_vec<DT, 8>(out, o, y);
+                store_vec<DT, 8>(out, o + 8, y + 8);
             }
         }
     }
