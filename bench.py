@@ -393,6 +393,13 @@ def bench_ceilings(torch, dev, stream, cold_bufs):
                       "(s_memtime / s_memrealtime) across the MFMA loop, times the constant rate"}
 
 
+
+def linear_floor_us(c) -> float:
+    """Roofline floor of an fp32 linear with bias: max(flops / MFMA peak, bytes / HBM peak), bytes = X, W, bias
+    and Y once each."""
+    nbytes = 4 * (c.M * c.K + c.N * c.K + c.N + c.M * c.N)
+    return max(c.flops / (PEAK_F32_TFLOPS * 1e12), nbytes / (PEAK_HBM_GBS * 1e9)) * 1e6
+
 def bench_c1(torch, dev, stream, no_parity: bool):
     """fp32 linear 128x768x768 + bias: warm (one W) and cold (128 rotated copies of W, 302 MB)."""
     import oracle
@@ -425,7 +432,8 @@ def bench_c1(torch, dev, stream, no_parity: bool):
             "warm_us": round(warm * 1e3, 3), "cold_us": round(cold * 1e3, 3),
             "warm_graph_us": round(g_warm / 32 * 1e3, 3), "cold_graph_us": round(g_cold / len(copies) * 1e3, 3),
             "TFLOP/s_warm": round(c.flops / (warm * 1e-3) / 1e12, 2),
-            "floor_us": round(c.flops / (PEAK_F32_TFLOPS * 1e12) * 1e6, 3),
+            "floor_us": round(linear_floor_us(c), 3),
+            "frac_of_floor_warm_graph": round(linear_floor_us(c) / (g_warm / 32 * 1e3), 4),
             "parity_err": err, "parity_pass": None if err is None else err <= 1e-5, "plan": plan.describe(),
             "timing": "HIP events over back-to-back launches (includes launch gaps); *_graph_us: median replay "
                       "of a HIP graph of 32 (warm) or 128 (cold, one per weight copy) launches, per launch"}
@@ -466,7 +474,8 @@ def bench_c3(torch, dev, stream, no_parity: bool, copies: int = 12):
         warm = time_launches(lambda i: run(g, g["Ws"][0]), 512, stream)
         out["gemms"][c.name] = {"warm_us": round(warm * 1e3, 3),
                                 "TFLOP/s_warm": round(c.flops / (warm * 1e-3) / 1e12, 2),
-                                "floor_us": round(c.flops / (PEAK_F32_TFLOPS * 1e12) * 1e6, 3),
+                                "floor_us": round(linear_floor_us(c), 3),
+                                "frac_of_floor_warm": round(linear_floor_us(c) / (warm * 1e3), 4),
                                 "parity_err": err, "plan": g["plan"].describe()}
 
     def layer(l):
@@ -1201,6 +1210,9 @@ def main(argv=None) -> int:
                                     f"({COLD_COPIES} rotated copies)",
                         "us": round(n_ms * 1e3, 3), "warm_us": round(warm_ms * 1e3, 3),
                         "GB/s": round(n_gbs, 1),
+                        **({"frac_of_measured_cold_read": round(n_gbs / extra["ceilings"]["read_cold_GB/s"], 4),
+                            "measured_cold_read_GB/s": extra["ceilings"]["read_cold_GB/s"]}
+                           if (extra.get("ceilings") or {}).get("read_cold_GB/s") else {}),
                         "roofline": {"bound": "hbm", "achieved": round(n_gbs, 1), "peak": PEAK_HBM_GBS,
                                      "unit": "GB/s", "frac": round(n_gbs / PEAK_HBM_GBS, 4),
                                      "traffic": measured_traffic("stream_f16", tile_str(nplan)),

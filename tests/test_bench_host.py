@@ -129,3 +129,13 @@ def test_peaks_are_the_datasheet_figures():
     assert bench.PEAK_HBM_GBS == pytest.approx(8000.0)
     assert 2400 <= bench.PEAK_BF16_TFLOPS <= 2600
     assert np.isfinite(bench.PEAK_SCLK_MHZ) and bench.PEAK_SCLK_MHZ == 2400
+
+
+def test_linear_floor_takes_the_larger_of_the_two_bounds():
+    """128×768×768 fp32 is MFMA-bound (2·128·768² flops at 157.3 TF/s = 0.960 µs against 3.15 MB at 8 TB/s);
+    one row against a 4096² weight is HBM-bound (67.1 MB at 8 TB/s = 8.39 µs against 0.21 µs of MFMA work)."""
+    from types import SimpleNamespace as NS
+    c1 = NS(M=128, N=768, K=768, flops=2 * 128 * 768 * 768)
+    assert bench.linear_floor_us(c1) == pytest.approx(2 * 128 * 768 * 768 / 157.3e12 * 1e6)
+    row = NS(M=1, N=4096, K=4096, flops=2 * 4096 * 4096)
+    assert bench.linear_floor_us(row) == pytest.approx(4 * (4096 + 4096 * 4096 + 4096 + 4096) / 8000e9 * 1e6)
