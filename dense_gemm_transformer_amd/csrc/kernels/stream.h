@@ -41,7 +41,7 @@
 
 namespace tlg {
 
-template <int IN, int NB, int KW, int LOADS, int ROWB>
+template <int IN, int NB, int KW, int LOADS, int ROWB, bool PIPE = false>
 struct StreamGeom {
     static constexpr int EPV = Elem<IN>::per16;  // elements per 16-byte load
     static constexpr int KSTEP = 4 * EPV;        // k covered by one load across the 4 lane groups
@@ -49,13 +49,14 @@ struct StreamGeom {
     static constexpr int WCK = KW * CK;          // k per workgroup per chunk
     static constexpr int XROWS = 16 * ROWB;
     static constexpr int LDX = WCK + EPV;        // padded LDS row of the X chunk (elements)
-    static constexpr int X_BYTES = XROWS * LDX * (int)sizeof(typename Elem<IN>::storage);
+    static constexpr int X_BUF = XROWS * LDX;  // elements of one staged X chunk
+    static constexpr int X_BYTES = (PIPE ? 2 : 1) * X_BUF * (int)sizeof(typename Elem<IN>::storage);
     static constexpr int RED_BYTES = KW > 1 ? NB * KW * ROWB * 4 * 64 * 4 : 0;
     static constexpr int LDS_BYTES = X_BYTES + RED_BYTES;
     static constexpr bool FITS = LDS_BYTES <= 160 * 1024;
 };
 
-template <int IN, int OUT, uint32_t EPI, int NB, int KW, int LOADS, int ROWB, bool EVEN, bool SPLIT>
+template <int IN, int OUT, uint32_t EPI, int NB, int KW, int LOADS, int ROWB, bool EVEN, bool SPLIT, bool PIPE>
 __global__ __launch_bounds__(64 * NB * KW) void stream_kernel(const void* __restrict__ Xv,
                                                              const void* __restrict__ Wv,
                                                              const void* __restrict__ bias,
@@ -63,7 +64,7 @@ __global__ __launch_bounds__(64 * NB * KW) void stream_kernel(const void* __rest
                                                              unsigned* __restrict__ tickets, int M, int N,
                                                              int K, int kper, int resid) {
     using S = typename Elem<IN>::storage;
-    using G = StreamGeom<IN, NB, KW, LOADS, ROWB>;
+    using G = StreamGeom<IN, NB, KW, LOADS, ROWB, PIPE>;
     constexpr bool F32 = IN == TLG_F32;
     constexpr int THREADS = 64 * NB * KW;
     constexpr int EPV = G::EPV, KSTEP = G::KSTEP, CK = G::CK, WCK = G::WCK, LDX = G::LDX;
@@ -97,10 +98,8 @@ __global__ __launch_bounds__(64 * NB * KW) void stream_kernel(const void* __rest
 #pragma unroll
     for (int rb = 0; rb < ROWB; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int kc = kbeg; kc < kend; kc += WCK) {
-        // X chunk first (cache-resident, coalesced), then this wave's W
-        // stream; the scheduling barrier keeps every load ahead of the first use.
-        u32x4 xr[XPT];
+    // X chunk first (cache-resident, coalesced), then this wave's W stream.
+    auto load_chunk = [&](int kc, u32x4 (&xr)[XPT], u32x4 (&wv)[LOADS]) {
 #pragma unroll
         for (int i = 0; i < XPT; ++i) {
             const int v = t + THREADS * i;
@@ -111,7 +110,6 @@ __global__ __launch_bounds__(64 * NB * KW) void stream_kernel(const void* __rest
                 xr[i] = u32x4{0u, 0u, 0u, 0u};
         }
         const int kw0 = kc + kw * CK;
-        u32x4 wv[LOADS];
 #pragma unroll
         for (int j = 0; j < LOADS; ++j) {
             const int k = kw0 + j * KSTEP + g * EPV;
@@ -120,20 +118,22 @@ __global__ __launch_bounds__(64 * NB * KW) void stream_kernel(const void* __rest
             else
                 wv[j] = u32x4{0u, 0u, 0u, 0u};
         }
-        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto stage_x = [&](S* xb, const u32x4 (&xr)[XPT]) {
 #pragma unroll
         for (int i = 0; i < XPT; ++i) {
             const int v = t + THREADS * i;
             if (XVEC % THREADS == 0 || v < XVEC)
-                *reinterpret_cast<u32x4*>(xs + (v / XVPR) * LDX + (v % XVPR) * EPV) = xr[i];
+                *reinterpret_cast<u32x4*>(xb + (v / XVPR) * LDX + (v % XVPR) * EPV) = xr[i];
         }
-        __syncthreads();
+    };
+    auto multiply = [&](const S* xb, const u32x4 (&wv)[LOADS]) {
 #pragma unroll
         for (int rb = 0; rb < ROWB; ++rb) {
 #pragma unroll
             for (int j = 0; j < LOADS; ++j) {
                 const u32x4 xv =
-                    *reinterpret_cast<const u32x4*>(xs + (rb * 16 + r) * LDX + kw * CK + j * KSTEP + g * EPV);
+                    *reinterpret_cast<const u32x4*>(xb + (rb * 16 + r) * LDX + kw * CK + j * KSTEP + g * EPV);
                 if constexpr (F32) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
@@ -143,7 +143,55 @@ __global__ __launch_bounds__(64 * NB * KW) void stream_kernel(const void* __rest
                 }
             }
         }
-        if (kc + WCK < kend) __syncthreads();  // the next chunk overwrites xs
+    };
+    if constexpr (!PIPE) {
+        // Every load of a chunk ahead of its first product (the scheduling
+        // barrier), then one X buffer: a barrier before the next chunk's staging.
+        for (int kc = kbeg; kc < kend; kc += WCK) {
+            u32x4 xr[XPT], wv[LOADS];
+            load_chunk(kc, xr, wv);
+            __builtin_amdgcn_sched_barrier(0);
+            stage_x(xs, xr);
+            __syncthreads();
+            multiply(xs, wv);
+            if (kc + WCK < kend) __syncthreads();  // the next chunk overwrites xs
+        }
+    } else {
+        // Pipelined chunks: chunk c + 1's X and weight loads go out before
+        // chunk c's products, so they land while the MFMAs run.  Two register
+        // sets and two X buffers alternate (set and buffer A for even chunks, B
+        // for odd), so no prefetched register is copied: a copy would wait for
+        // the prefetch before the loop goes on.  The one barrier per chunk also
+        // orders the staging of chunk c + 2 into a buffer after every wave's
+        // products from it.  The last chunk leaves the loop before issuing a
+        // prefetch, so the wait before each chunk's products covers only that
+        // chunk's loads.
+        u32x4 xa[XPT], wa[LOADS], xb_[XPT], wb[LOADS];
+        S* const bufa = xs;
+        S* const bufb = xs + G::X_BUF;
+        load_chunk(kbeg, xa, wa);
+        for (int kc = kbeg; kc < kend;) {  // an empty range (none is planned) skips the loop
+            stage_x(bufa, xa);
+            __syncthreads();
+            if (kc + WCK >= kend) {
+                multiply(bufa, wa);
+                break;
+            }
+            load_chunk(kc + WCK, xb_, wb);
+            __builtin_amdgcn_sched_barrier(0);
+            multiply(bufa, wa);
+            kc += WCK;
+            stage_x(bufb, xb_);
+            __syncthreads();
+            if (kc + WCK >= kend) {
+                multiply(bufb, wb);
+                break;
+            }
+            load_chunk(kc + WCK, xa, wa);
+            __builtin_amdgcn_sched_barrier(0);
+            multiply(bufb, wb);
+            kc += WCK;
+        }
     }
 
     // In-workgroup K reduction: wave kw = 0 of each column block sums the KW
@@ -373,7 +421,7 @@ __global__ __launch_bounds__(512) void stream_dl_kernel(const void* __restrict__
     }
 }
 
-template <int I, int NB, int KW, int LOADS>
+template <int I, int NB, int KW, int LOADS, bool PIPE, int RBF>
 static int launch_stream_cfg(const tlg_plan& p, const void* X, const void* W, const void* bias, void* Y, void* ws,
                              hipStream_t stream) {
     const int S = p.split;
@@ -393,12 +441,12 @@ static int launch_stream_cfg(const tlg_plan& p, const void* X, const void* W, co
             constexpr uint32_t E = (uint32_t)decltype(epi)::value;
             auto go = [&](auto rowb, auto ev, auto sp) -> int {
                 constexpr int RB = decltype(rowb)::value;
-                if constexpr (!StreamGeom<I, NB, KW, LOADS, RB>::FITS) {
+                if constexpr (!StreamGeom<I, NB, KW, LOADS, RB, PIPE>::FITS) {
                     set_error("stream configuration does not fit in LDS for M=%lld", (long long)p.M);
                     return TLG_ERR_UNSUPPORTED;
                 } else {
                     hipLaunchKernelGGL((stream_kernel<I, O, E, NB, KW, LOADS, RB, decltype(ev)::value,
-                                                      decltype(sp)::value>),
+                                                      decltype(sp)::value, PIPE>),
                                        grid, block, 0, stream, X, W, bias, Y, part, tickets, (int)p.M, (int)p.N,
                                        (int)p.K, kper, (int)((p.epi & TLG_EPI_RESIDUAL) != 0));
                     return check_launch("stream_kernel");
@@ -410,9 +458,17 @@ static int launch_stream_cfg(const tlg_plan& p, const void* X, const void* W, co
             auto by_even = [&](auto rowb) {
                 return even ? by_split(rowb, std::true_type{}) : by_split(rowb, std::false_type{});
             };
-            if (p.rowb == 1) return by_even(ic<1>{});
-            if (p.rowb == 2) return by_even(ic<2>{});
-            return by_even(ic<4>{});
+            if constexpr (RBF != 0) {  // the option fixes the row blocks: one instantiation
+                if (p.rowb != RBF) {
+                    set_error("stream configuration takes %d-row blocks of X, the plan has %d", 16 * RBF, 16 * p.rowb);
+                    return (int)TLG_ERR_INVALID_ARG;
+                }
+                return by_even(ic<RBF>{});
+            } else {
+                if (p.rowb == 1) return by_even(ic<1>{});
+                if (p.rowb == 2) return by_even(ic<2>{});
+                return by_even(ic<4>{});
+            }
         });
     });
 }
@@ -464,9 +520,11 @@ static int launch_stream_dl(const tlg_plan& p, const void* X, const void* W, con
 template <int I>
 int launch_stream_in(const tlg_plan& p, const void* X, const void* W, const void* bias, void* Y, void* ws,
                      hipStream_t stream) {
-    static_assert(kNumStream == 10 && kStream[5].dl, "stream configurations changed");
-#define TLG_STREAM_CASE(i) \
-    case i: return launch_stream_cfg<I, kStream[i].nb, kStream[i].kw, kStream[i].loads>(p, X, W, bias, Y, ws, stream);
+    static_assert(kNumStream == 14 && kStream[5].dl, "stream configurations changed");
+#define TLG_STREAM_CASE(i)                                                                                     \
+    case i:                                                                                                     \
+        return launch_stream_cfg<I, kStream[i].nb, kStream[i].kw, kStream[i].loads, kStream[i].pipe != 0,      \
+                                 kStream[i].rb>(p, X, W, bias, Y, ws, stream);
     switch (p.tile) {
         TLG_STREAM_CASE(0)
         TLG_STREAM_CASE(1)
@@ -478,6 +536,10 @@ int launch_stream_in(const tlg_plan& p, const void* X, const void* W, const void
         TLG_STREAM_CASE(7)
         TLG_STREAM_CASE(8)
         TLG_STREAM_CASE(9)
+        TLG_STREAM_CASE(10)
+        TLG_STREAM_CASE(11)
+        TLG_STREAM_CASE(12)
+        TLG_STREAM_CASE(13)
     default: set_error("bad stream tile"); return (int)TLG_ERR_INVALID_ARG;
     }
 #undef TLG_STREAM_CASE

@@ -415,7 +415,7 @@ int gemm_plan_describe(tlg_plan_t p, char* buf, size_t n) {
     char tmp[320];
     int len = snprintf(tmp, sizeof tmp,
                        "variant=%s M=%lld N=%lld K=%lld in=%s out=%s layout=%s epi=%s%s%s tile=%dx%dx%d "
-                       "split=%d threads=%d grid=%lldx%lldx%lld launches=%d ws=%zu%s%s",
+                       "split=%d threads=%d grid=%lldx%lldx%lld launches=%d ws=%zu%s%s%s",
                        vname[p->variant], (long long)p->M, (long long)p->N, (long long)p->K,
                        dname[p->in_dt], dname[p->out_dt], lname[p->layout],
                        (p->epi & TLG_EPI_BIAS) ? "bias" : "none", (p->epi & TLG_EPI_GELU_TANH) ? "+gelu" : "",
@@ -425,7 +425,8 @@ int gemm_plan_describe(tlg_plan_t p, char* buf, size_t n) {
                        (p->variant == TLG_VARIANT_TILED && p->stages) || (p->variant == TLG_VARIANT_STREAM && kStream[p->tile].dl)
                            ? " load=direct"
                            : "",
-                       p->variant == TLG_VARIANT_TILED && p->persist ? " persistent" : "");
+                       p->variant == TLG_VARIANT_TILED && p->persist ? " persistent" : "",
+                       p->variant == TLG_VARIANT_STREAM && kStream[p->tile].pipe ? " pipelined" : "");
     if (buf && n) {
         size_t c = (size_t)len < n - 1 ? (size_t)len : n - 1;
         memcpy(buf, tmp, c);

@@ -110,6 +110,7 @@ struct StreamCfg {
     int loads;   // 16-byte loads per lane per chunk
     int dl = 0;  // the weight tile goes to LDS by direct loads, X to registers (16-bit, M <= 16, no split)
     int rb = 0;  // 16-row blocks of X per workgroup (0: all of M up to 64 rows, else 32-row blocks)
+    int pipe = 0;  // chunk c + 1's loads go out before chunk c's products; two X buffers in LDS
 };
 constexpr StreamCfg kStream[] = {
     {1, 8, 16},  // 0: 16-row tiles over all of K by 8 waves; no inter-workgroup traffic (M <= 16)
@@ -130,6 +131,14 @@ constexpr StreamCfg kStream[] = {
     // output of the tiles here (fc at 128 rows: 256 workgroups, 11.5 vs 13.4 µs
     // for the 32×32 three-chunk tile in a probe; qkv 11.0 vs 12.3 µs).
     {3, 4, 12, 0, 2},  // 9
+    // The one-chunk tiles load all of K before the first product: on qkv at
+    // 128 rows (stage timestamps, one box) the loads take 4.2 µs and the
+    // products 3-4 µs after them, never overlapping.  These split K = 768 into
+    // chunks whose loads are issued a chunk ahead of the products.
+    {3, 4, 6, 0, 2, 1},  // 10: 48 columns × 32 rows, two chunks of 384 (fp32)
+    {3, 4, 3, 0, 2, 1},  // 11: 48 columns × 32 rows, four chunks of 192
+    {2, 4, 6, 0, 1, 1},  // 12: 32 columns × 16 rows, two chunks
+    {1, 4, 6, 0, 1, 1},  // 13: 16 columns × 16 rows, two chunks
 };
 // Direct-load stream tile: 16 weight rows of K 16-bit elements resident in LDS.
 constexpr int kStreamDlMaxK = 4096, kStreamDlKStep = 512;
@@ -145,7 +154,7 @@ inline int64_t stream_lds_bytes(const StreamCfg& c, int in_dt, int rowb) {
     if (c.dl) return 16 * kStreamDlMaxK * 2 + 8 * 4 * 64 * 4;  // weight rows, wave partials
     const int64_t esize = in_dt == 0 ? 4 : 2, epv = 16 / esize;
     const int64_t wck = (int64_t)c.kw * c.loads * 4 * epv;
-    const int64_t x = 16 * rowb * (wck + epv) * esize;
+    const int64_t x = (c.pipe ? 2 : 1) * 16 * rowb * (wck + epv) * esize;
     const int64_t red = c.kw > 1 ? (int64_t)c.nb * c.kw * rowb * 4 * 64 * 4 : 0;
     return x + red;
 }

@@ -51,7 +51,7 @@ def test_generic(pair, layout, epi):
 
 @pytest.mark.parametrize("pair", PAIRS, ids=lambda p: f"{p[0]}->{p[1]}")
 @pytest.mark.parametrize("epi", EPIS, ids=["none", "bias", "gelu", "bias+gelu"])
-@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4, 5, 7, 8, 9, 10])
+@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4, 5, 7, 8, 9, 10, 11, 12, 13, 14])
 def test_stream(pair, epi, tile):
     ran = 0
     for M, N, K in [(1, 16, 8), (16, 48, 512), (5, 50, 520), (17, 36, 1032), (40, 100, 264), (64, 16, 4096),
@@ -77,6 +77,24 @@ def test_stream_weight_rows_in_lds(pair, epi):
         c = inputs.random_case(23, M, N, K, pair[0], pair[1], "NK", bias=epi[0], gelu=epi[1], residual=res)
         _, desc = _check(c, variant=tlgemm.VARIANT_STREAM, tile=6)
         assert "variant=stream" in desc and f"tile=16x16x{K} " in desc, desc
+
+
+@pytest.mark.parametrize("tile", [11, 12, 13, 14])
+def test_stream_pipelined(tile):
+    """Pipelined stream options (chunk c + 1's loads ahead of chunk c's products, two X buffers and two
+    register sets alternating): every linear of the 128-row GPT-2 layer and the 128×768×768 linear with
+    one split (2 to 16 chunks per workgroup), all outputs against the oracle; then ragged M, N and K,
+    16-bit inputs and a grid split on top (the automatic split gives one chunk per split)."""
+    for c in [inputs.workload_fp32_linear_128x768()] + inputs.workload_gpt2_layer(M=128, dtype="f32"):
+        _, desc = _check(c, variant=tlgemm.VARIANT_STREAM, tile=tile, split_k=1)
+        assert desc.endswith(" pipelined") and " split=1 " in desc, desc
+    for (M, N, K), pair, split, epi in [((37, 70, 1000), ("f32", "f32"), 1, (True, True)),
+                                        ((100, 130, 2056), ("f32", "f32"), 2, (True, False)),
+                                        ((16, 200, 3000), ("f16", "f16"), 1, (False, True)),
+                                        ((33, 96, 4104), ("bf16", "f32"), 2, (True, True))]:
+        c = _case(24, M, N, K, pair, "NK", epi)
+        _, desc = _check(c, variant=tlgemm.VARIANT_STREAM, tile=tile, split_k=split)
+        assert desc.endswith(" pipelined"), desc
 
 
 def test_stream_weight_rows_in_lds_limits():
