@@ -520,7 +520,7 @@ static int launch_stream_dl(const tlg_plan& p, const void* X, const void* W, con
 template <int I>
 int launch_stream_in(const tlg_plan& p, const void* X, const void* W, const void* bias, void* Y, void* ws,
                      hipStream_t stream) {
-    static_assert(kNumStream == 14 && kStream[5].dl, "stream configurations changed");
+    static_assert(kNumStream == 15 && kStream[5].dl, "stream configurations changed");
 #define TLG_STREAM_CASE(i)                                                                                     \
     case i:                                                                                                     \
         return launch_stream_cfg<I, kStream[i].nb, kStream[i].kw, kStream[i].loads, kStream[i].pipe != 0,      \
@@ -540,6 +540,7 @@ int launch_stream_in(const tlg_plan& p, const void* X, const void* W, const void
         TLG_STREAM_CASE(11)
         TLG_STREAM_CASE(12)
         TLG_STREAM_CASE(13)
+        TLG_STREAM_CASE(14)
     default: set_error("bad stream tile"); return (int)TLG_ERR_INVALID_ARG;
     }
 #undef TLG_STREAM_CASE

@@ -139,6 +139,7 @@ constexpr StreamCfg kStream[] = {
     {3, 4, 3, 0, 2, 1},  // 11: 48 columns × 32 rows, four chunks of 192
     {2, 4, 6, 0, 1, 1},  // 12: 32 columns × 16 rows, two chunks
     {1, 4, 6, 0, 1, 1},  // 13: 16 columns × 16 rows, two chunks
+    {2, 4, 3, 0, 1, 1},  // 14: 32 columns × 16 rows, four chunks
 };
 // Direct-load stream tile: 16 weight rows of K 16-bit elements resident in LDS.
 constexpr int kStreamDlMaxK = 4096, kStreamDlKStep = 512;

@@ -48,7 +48,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 TABLE = os.path.join(HERE, "csrc", "dispatch_table.inc")
 # Length of each variant's tile list (for 16-bit inputs, the longer tiled list):
 # the options a search walks.  A CPU test checks them against the planner.
-STREAM_OPTIONS = 14
+STREAM_OPTIONS = 15
 TILED_OPTIONS = 13
 
 

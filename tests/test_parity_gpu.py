@@ -51,7 +51,7 @@ def test_generic(pair, layout, epi):
 
 @pytest.mark.parametrize("pair", PAIRS, ids=lambda p: f"{p[0]}->{p[1]}")
 @pytest.mark.parametrize("epi", EPIS, ids=["none", "bias", "gelu", "bias+gelu"])
-@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4, 5, 7, 8, 9, 10, 11, 12, 13, 14])
+@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4, 5, 7, 8, 9, 10, 11, 12, 13, 14, 15])
 def test_stream(pair, epi, tile):
     ran = 0
     for M, N, K in [(1, 16, 8), (16, 48, 512), (5, 50, 520), (17, 36, 1032), (40, 100, 264), (64, 16, 4096),
@@ -79,7 +79,7 @@ def test_stream_weight_rows_in_lds(pair, epi):
         assert "variant=stream" in desc and f"tile=16x16x{K} " in desc, desc
 
 
-@pytest.mark.parametrize("tile", [11, 12, 13, 14])
+@pytest.mark.parametrize("tile", [11, 12, 13, 14, 15])
 def test_stream_pipelined(tile):
     """Pipelined stream options (chunk c + 1's loads ahead of chunk c's products, two X buffers and two
     register sets alternating): every linear of the 128-row GPT-2 layer and the 128×768×768 linear with
