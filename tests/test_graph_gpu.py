@@ -41,6 +41,7 @@ def _launch(g, stream):
 
 def test_captured_sequence_replays_bitwise():
     gemms = [
+        _setup(inputs.random_case(40, 128, 2304, 768, "f32", bias=True)),              # pipelined stream chunks
         _setup(inputs.random_case(41, 16, 520, 3000, "f16", bias=True, gelu=True),
                variant=tlgemm.VARIANT_STREAM, tile=3, split_k=4),                     # stream, ticketed split
         _setup(inputs.random_case(42, 128, 768, 768, "f32", bias=True),
@@ -56,6 +57,7 @@ def test_captured_sequence_replays_bitwise():
     ]
     assert all("load=direct" in g["plan"].describe() for g in gemms[-3:-1])
     assert "persistent" in gemms[-1]["plan"].describe()
+    assert gemms[0]["plan"].describe().endswith(" pipelined")
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())  # inputs, outputs and zeroed workspaces come from the default stream
     with torch.cuda.stream(s):
