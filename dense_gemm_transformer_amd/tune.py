@@ -92,7 +92,9 @@ def candidates(case, tlgemm):
     opts = []
     if case.layout == "NK" and case.M <= 256:
         for tile in range(1, STREAM_OPTIONS + 1):
-            opts += [(tlgemm.VARIANT_STREAM, tile, 0), (tlgemm.VARIANT_STREAM, tile, 1)]
+            # the automatic split, none, and 2 or 4 (the automatic split gives the
+            # pipelined options one chunk per split, which leaves nothing to overlap)
+            opts += [(tlgemm.VARIANT_STREAM, tile, split) for split in (0, 1, 2, 4)]
     for tile in range(1, TILED_OPTIONS + 1):  # past the dtype's tile list the planner refuses, and the option is skipped
         for split in (1, 2, 4, 8):
             opts.append((tlgemm.VARIANT_TILED, tile, split))
