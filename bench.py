@@ -68,7 +68,7 @@ FETCH_SCALE, WRITE_SCALE = 1.998, 1.0
 TRAFFIC = {
     "tiled_f32": {"sources": ("common.h", "tiled.h"), "sha": "6f4660e0ad36dce1",
                   "tile": "256x256x16", "fetch_kib": 196687.0, "write_kib": 65536.0},
-    "stream_f16": {"sources": ("common.h", "stream.h"), "sha": "9d46bcba36e040ac",
+    "stream_f16": {"sources": ("common.h", "stream.h"), "sha": "7278d7ba9ee58e13",
                    "tile": "16x16x4096", "fetch_kib": 16919.0, "write_kib": 128.0},
 }
 

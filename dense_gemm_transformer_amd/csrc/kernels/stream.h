@@ -12,7 +12,9 @@
 //    another workgroup (NB = 1, KW = 8: 256 workgroups for 4096 rows).
 //  * W never passes through LDS: each lane issues 16-byte loads straight into
 //    registers, all of a chunk's loads before the first product, so a wave
-//    keeps LOADS KiB of W in flight.
+//    keeps LOADS KiB of W in flight.  Pipelined options go one chunk further:
+//    chunk c + 1's loads are issued before chunk c's products, into a second
+//    register set and a second X buffer, so that the products hide the loads.
 //  * The X slice of the workgroup's K range is read with fully coalesced
 //    loads (consecutive threads, consecutive 16 bytes of one row) into LDS
 //    and every wave takes its MFMA operands from there.
