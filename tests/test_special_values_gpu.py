@@ -36,6 +36,8 @@ CASES = [
     ((40, 100, 264), ("f32", "f32"), "NK", dict(variant=tlgemm.VARIANT_STREAM), "variant=stream"),
     ((16, 260, 3000), ("f32", "f32"), "NK", dict(variant=tlgemm.VARIANT_STREAM, tile=3, split_k=3), "split=3"),
     ((33, 520, 2048), ("bf16", "f32"), "NK", dict(variant=tlgemm.VARIANT_STREAM, tile=3, split_k=2), "split=2"),
+    ((40, 100, 1000), ("f32", "f32"), "NK", dict(variant=tlgemm.VARIANT_STREAM, tile=12, split_k=1), "pipelined"),
+    ((33, 96, 2056), ("bf16", "bf16"), "NK", dict(variant=tlgemm.VARIANT_STREAM, tile=15, split_k=2), "pipelined"),
     ((13, 100, 3584), ("f16", "f16"), "NK", dict(variant=tlgemm.VARIANT_STREAM, tile=6), "load=direct"),
     ((16, 264, 2048), ("bf16", "bf16"), "NK", dict(variant=tlgemm.VARIANT_STREAM, tile=6), "load=direct"),
     ((128, 136, 72), ("f32", "f32"), "AT_NK", dict(variant=tlgemm.VARIANT_TILED, tile=1), "variant=tiled"),
