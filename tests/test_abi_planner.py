@@ -348,3 +348,25 @@ def test_wide_128x192_tiles_plan():
         p = t.Plan.create(M, N, K, "bf16", "bf16", "NK", variant=t.VARIANT_TILED, tile=12, split_k=split)
         assert "persistent" not in p.describe(), p.describe()
         p.close()
+
+
+def test_stream_pipelined_options_planning():
+    """Pipelined stream options (entries 10-14): the description says so, the row blocks are the option's own
+    whatever M is, the automatic split gives one chunk per split (nothing left to overlap), and a forced split
+    keeps several chunks per workgroup.  Their two X buffers fit LDS for fp32 and 16-bit inputs."""
+    for tile, (bn, bm, bk32) in {11: (48, 32, 384), 12: (48, 32, 192), 13: (32, 16, 384), 14: (16, 16, 384),
+                                 15: (32, 16, 192)}.items():
+        for M in (1, 16, 40, 128, 256):
+            p = _plan(M, 768, 768, "f32", variant=t.VARIANT_STREAM, tile=tile, split_k=1)
+            i = p.info
+            assert p.describe().endswith(" pipelined"), p.describe()
+            assert (i.tile_m, i.tile_n, i.tile_k, i.split_k) == (bm, bn, bk32, 1)
+            assert i.workgroups == -(-768 // bn) * -(-M // bm) and i.workspace_bytes == 0  # grid z walks row blocks
+        auto = _plan(128, 768, 3072, "f32", variant=t.VARIANT_STREAM, tile=tile).info
+        assert auto.split_k == min(3072 // bk32, 16)  # the fill rule: one chunk per split
+        forced = _plan(128, 768, 3072, "f32", variant=t.VARIANT_STREAM, tile=tile, split_k=4).info
+        assert forced.split_k == 4 and 3072 // 4 // forced.tile_k == 768 // bk32
+        h = _plan(16, 4096, 4096, "bf16", variant=t.VARIANT_STREAM, tile=tile, split_k=1)
+        assert h.info.tile_k == 2 * bk32 and h.describe().endswith(" pipelined")  # 16-byte loads: twice the k
+    assert not _plan(128, 768, 768, "f32", variant=t.VARIANT_STREAM, tile=10, split_k=1).describe().endswith(
+        " pipelined")
