@@ -352,8 +352,8 @@ def test_wide_128x192_tiles_plan():
 
 def test_stream_pipelined_options_planning():
     """Pipelined stream options (entries 10-14): the description says so, the row blocks are the option's own
-    whatever M is, the automatic split gives one chunk per split (nothing left to overlap), and a forced split
-    keeps several chunks per workgroup.  Their two X buffers fit LDS for fp32 and 16-bit inputs."""
+    whatever M is, the automatic split spreads the column tiles over the 256 CUs in whole chunks (here one or
+    two chunks per split, little left to overlap), and a forced split keeps several chunks per workgroup.  Their two X buffers fit LDS for fp32 and 16-bit inputs."""
     for tile, (bn, bm, bk32) in {11: (48, 32, 384), 12: (48, 32, 192), 13: (32, 16, 384), 14: (16, 16, 384),
                                  15: (32, 16, 192)}.items():
         for M in (1, 16, 40, 128, 256):
@@ -363,7 +363,9 @@ def test_stream_pipelined_options_planning():
             assert (i.tile_m, i.tile_n, i.tile_k, i.split_k) == (bm, bn, bk32, 1)
             assert i.workgroups == -(-768 // bn) * -(-M // bm) and i.workspace_bytes == 0  # grid z walks row blocks
         auto = _plan(128, 768, 3072, "f32", variant=t.VARIANT_STREAM, tile=tile).info
-        assert auto.split_k == min(3072 // bk32, 16)  # the fill rule: one chunk per split
+        s0 = min(-(-256 // (768 // bn)), 3072 // bk32, 16)  # the fill rule: 256 CUs over the column tiles
+        kper = -(-(-(-3072 // s0)) // bk32) * bk32            # whole chunks per split
+        assert auto.split_k == -(-3072 // kper)
         forced = _plan(128, 768, 3072, "f32", variant=t.VARIANT_STREAM, tile=tile, split_k=4).info
         assert forced.split_k == 4 and 3072 // 4 // forced.tile_k == 768 // bk32
         h = _plan(16, 4096, 4096, "bf16", variant=t.VARIANT_STREAM, tile=tile, split_k=1)
